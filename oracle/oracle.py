@@ -1,0 +1,201 @@
+"""ctypes binding of the plain C oracle (``rsfp4_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY.  Every function here marshals numpy arrays into the C
+oracle and back; the arithmetic lives in the C file, which follows the ResServe
+page (arXiv 2611.08713): Section 2 / Figure 1 for the formats, Appendix B.2
+Eqs. 8-10 for the NVFP4 scale computation, Section 4.2 Eq. 1 and Section 4.3
+Eq. 2 for the compensated product and its Fold.
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "rsfp4_oracle.c")
+_LIB = os.path.join(_HERE, "librsfp4_oracle.so")
+
+NVFP4, MXFP4 = 0, 1
+BLOCK = {NVFP4: 16, MXFP4: 32}
+
+__all__ = [
+    "NVFP4", "MXFP4", "BLOCK", "build", "lib",
+    "e2m1_value", "e2m1_encode_mag", "e4m3_value", "e4m3_encode",
+    "e8m0_for_amax", "e8m0_value", "nvfp4_global_scale", "absmax",
+    "quantize_act", "quantize_weight", "quantize_weight_rows", "dequant_rows",
+    "linear", "unpack_codes",
+]
+
+
+def build(force=False):
+    """Compile the oracle with gcc (-O2, no contraction, no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+                               "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = ctypes.CDLL(_LIB)
+        f32, u8, i64, i32, dbl = ctypes.c_float, ctypes.c_uint8, ctypes.c_int64, ctypes.c_int, ctypes.c_double
+        P = ctypes.c_void_p
+        L.oracle_e2m1_value.restype, L.oracle_e2m1_value.argtypes = f32, [u8]
+        L.oracle_e2m1_encode_mag.restype, L.oracle_e2m1_encode_mag.argtypes = u8, [f32]
+        L.oracle_e4m3_value.restype, L.oracle_e4m3_value.argtypes = f32, [u8]
+        L.oracle_e4m3_encode.restype, L.oracle_e4m3_encode.argtypes = u8, [f32]
+        L.oracle_e8m0_for_amax.restype, L.oracle_e8m0_for_amax.argtypes = u8, [f32]
+        L.oracle_e8m0_value.restype, L.oracle_e8m0_value.argtypes = f32, [u8]
+        L.oracle_nvfp4_global_scale.restype, L.oracle_nvfp4_global_scale.argtypes = f32, [f32]
+        L.oracle_absmax.restype, L.oracle_absmax.argtypes = f32, [P, i64]
+        L.oracle_nvfp4_quantize_row.restype = None
+        L.oracle_nvfp4_quantize_row.argtypes = [P, i64, f32, P, P, P]
+        L.oracle_mxfp4_quantize_row.restype = None
+        L.oracle_mxfp4_quantize_row.argtypes = [P, i64, P, P, P]
+        L.oracle_quantize_act.restype = None
+        L.oracle_quantize_act.argtypes = [i32, P, i64, i64, i32, P, P, P, P, P]
+        L.oracle_quantize_weight_rows.restype = None
+        L.oracle_quantize_weight_rows.argtypes = [i32, P, i64, i64, f32, P, P, P]
+        L.oracle_linear.restype = None
+        L.oracle_linear.argtypes = [P, P, i64, i64, i64, i32, P, P]
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _f32(a):
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def e2m1_value(code):
+    return lib().oracle_e2m1_value(int(code))
+
+
+def e2m1_encode_mag(u):
+    return lib().oracle_e2m1_encode_mag(float(u))
+
+
+def e4m3_value(code):
+    return lib().oracle_e4m3_value(int(code))
+
+
+def e4m3_encode(t):
+    return lib().oracle_e4m3_encode(float(t))
+
+
+def e8m0_for_amax(a):
+    return lib().oracle_e8m0_for_amax(float(a))
+
+
+def e8m0_value(b):
+    return lib().oracle_e8m0_value(int(b))
+
+
+def nvfp4_global_scale(amax):
+    return lib().oracle_nvfp4_global_scale(float(amax))
+
+
+def absmax(v):
+    v = _f32(v).ravel()
+    return lib().oracle_absmax(_p(v), v.size)
+
+
+def quantize_act(x, fmt, with_residue=True):
+    """Quantize activation rows x[M, K] (fp32 values; bf16 inputs already widened).
+
+    Returns a dict with stacked rows R = 2M (with residue) or M:
+      codes [R, K/2] u8, scales [R, K/blk] u8, globals [R] f32 (zeros for MXFP4),
+      deq [R, K] f32 (dequantized values), resid [M, K] f32 (fp32 residue) or None.
+    """
+    x = _f32(x)
+    M, K = x.shape
+    blk = BLOCK[fmt]
+    assert K % blk == 0
+    R = 2 * M if with_residue else M
+    codes = np.zeros((R, K // 2), np.uint8)
+    scales = np.zeros((R, K // blk), np.uint8)
+    globs = np.zeros((R,), np.float32)
+    deq = np.zeros((R, K), np.float32)
+    resid = np.zeros((M, K), np.float32) if with_residue else None
+    lib().oracle_quantize_act(fmt, _p(x), M, K, 1 if with_residue else 0, _p(codes), _p(scales),
+                              _p(globs), _p(deq), _p(resid) if with_residue else None)
+    return {"codes": codes, "scales": scales, "globals": globs, "deq": deq, "resid": resid}
+
+
+def quantize_weight_rows(W_rows, fmt, s_gw=0.0, want_deq=True):
+    """Quantize weight rows W_rows[n, K] with a given NVFP4 tensor scale s_gw."""
+    W_rows = _f32(W_rows)
+    n, K = W_rows.shape
+    blk = BLOCK[fmt]
+    codes = np.zeros((n, K // 2), np.uint8)
+    scales = np.zeros((n, K // blk), np.uint8)
+    deq = np.zeros((n, K), np.float32) if want_deq else None
+    lib().oracle_quantize_weight_rows(fmt, _p(W_rows), n, K, float(s_gw), _p(codes), _p(scales),
+                                      _p(deq) if want_deq else None)
+    return {"codes": codes, "scales": scales, "deq": deq}
+
+
+def quantize_weight(W, fmt, rows=None, want_deq=True):
+    """Quantize a weight tensor W[N, K] (NVFP4: one tensor scale from max|W|).
+
+    rows: optional index array; only those rows are quantized (the tensor scale
+    still comes from the whole tensor).  Returns codes, scales, deq, s_g.
+    """
+    W = _f32(W)
+    s_gw = nvfp4_global_scale(absmax(W)) if fmt == NVFP4 else 0.0
+    sub = W if rows is None else W[np.asarray(rows)]
+    out = quantize_weight_rows(sub, fmt, s_gw, want_deq)
+    out["s_g"] = np.float32(s_gw)
+    return out
+
+
+def unpack_codes(codes, K):
+    """[R, K/2] packed nibbles -> [R, K] u8 codes (low nibble = even index)."""
+    lo = codes & 15
+    hi = codes >> 4
+    out = np.empty((codes.shape[0], K), np.uint8)
+    out[:, 0::2] = lo
+    out[:, 1::2] = hi
+    return out
+
+
+def dequant_rows(codes, scales, globals_, fmt, K):
+    """Dequantize rows from codes/scales/globals with the oracle's codecs,
+    fl(fl(S_b * s_g) * e) for NVFP4 and fl(X * e) for MXFP4."""
+    L = lib()
+    c = unpack_codes(codes, K)
+    e = np.array([L.oracle_e2m1_value(i) for i in range(16)], np.float32)[c]
+    blk = BLOCK[fmt]
+    if fmt == NVFP4:
+        tab = np.array([L.oracle_e4m3_value(i) for i in range(256)], np.float32)
+        sb = tab[scales]
+        st = (sb * np.asarray(globals_, np.float32).reshape(-1, 1)).astype(np.float32)
+    else:
+        tab = np.array([L.oracle_e8m0_value(i) for i in range(256)], np.float32)
+        st = tab[scales]
+    return (np.repeat(st, blk, axis=1) * e).astype(np.float32)
+
+
+def linear(dx, dw, M, compensated, want_beta=True):
+    """fp64 linear over dequantized rows: dx [R, K] stacked (R = 2M when
+    compensated), dw [N, K].  Returns (y [M, N] f64, beta [M, N] f64)."""
+    dx = _f32(dx)
+    dw = _f32(dw)
+    N, K = dw.shape
+    y = np.zeros((M, N), np.float64)
+    beta = np.zeros((M, N), np.float64) if want_beta else None
+    lib().oracle_linear(_p(dx), _p(dw), M, N, K, 1 if compensated else 0, _p(y),
+                        _p(beta) if want_beta else None)
+    return y, beta

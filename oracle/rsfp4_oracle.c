@@ -1,0 +1,318 @@
+/*
+ * rsfp4_oracle.c -- plain, slow, scalar CPU oracle for the residue-compensated
+ * block-scaled FP4 linear layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or call
+ * this file: only the tests, the smoke check and the bench's CPU-baseline leg do.
+ * It shares no code, header, table or helper with the HIP library.
+ *
+ * Sources (all from the page "ResServe: Accurate and Efficient FP4 LLM Inference
+ * with Residue Compensation", arXiv 2611.08713):
+ *   - Section 2 (Background) and Figure 1: E2M1 elements; NVFP4 = 16-element blocks
+ *     with an E4M3 block scale and an FP32 tensor scale; MXFP4 = 32-element blocks
+ *     with a power-of-two E8M0 scale and no tensor scale.
+ *   - Appendix B.2, Eqs. 8-10: Max_i = max|x| over block i, s_i = Max_i / 6,
+ *     alpha = max_i s_i / 448, s_i,FP8 = round_E4M3(s_i / alpha),
+ *     s~_i = alpha * s_i,FP8, x_FP4 = round_E2M1(x / s~_i), x^ = s~_i * x_FP4.
+ *   - Section 2 (QDQ notation): the residue is r = x - QDQ(x).
+ *   - Section 4.2, Eq. 1 and Section 4.3, Eq. 2: Y = X^ W^ + R^ W^ (full residue),
+ *     formed as the stacked product [X^; R^] W^ and the Fold Y_j = Z_j + Z_{M+j}.
+ *
+ * Readings taken where the page leaves a step open (each one is listed with its
+ * reason in the design notes of the repository):
+ *   - the tensor scale is computed as amax / 2688 (2688 = 6 * 448), per row for
+ *     activations and for the residue, per tensor for weights;
+ *   - the block scale argument is t = blockmax / (6 * s_g) (product first);
+ *   - elements are q = v / s~ (IEEE division), dequantization is fl(s~ * e);
+ *   - E4M3 is the FN variant: saturates to 448, never emits the NaN code 0x7F;
+ *     a NaN or non-positive argument encodes to 0x00;
+ *   - an element whose effective scale s~ is zero gets magnitude code 0;
+ *   - the sign bit of every code is copied from the input (so -tiny -> 0x8);
+ *   - MXFP4 block scale is 2^(floor(log2(blockmax)) - 2), clamped to the E8M0
+ *     range [2^-127, 2^127]; an all-zero block gets byte 0x00;
+ *   - nibble order: the element with the even K index sits in the low nibble.
+ *
+ * Arithmetic: every quantization step is IEEE binary32 with round-to-nearest-even;
+ * this file is compiled with -ffp-contract=off so no multiply-add is fused.
+ * The linear accumulates exact fp32 x fp32 products in binary64.
+ *
+ * The encoders are written as exhaustive nearest-value searches over the code
+ * tables (not as bit manipulation), so they stay independent of any fast encoder.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stddef.h>
+#include <string.h>
+
+#define ORACLE_API __attribute__((visibility("default")))
+
+/* ---------------------------------------------------------------- E2M1 ---- */
+
+/* The eight non-negative E2M1 magnitudes, indexed by the 3-bit magnitude code
+ * (ResServe, Section 2 / Figure 1: 1 sign bit, 2 exponent bits, 1 mantissa bit,
+ * largest magnitude 6). */
+static const float E2M1_MAG[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+
+ORACLE_API float oracle_e2m1_value(uint8_t code) {
+    float m = E2M1_MAG[code & 7u];
+    return (code & 8u) ? -m : m;
+}
+
+/* Nearest E2M1 magnitude to u >= 0; on an exact tie the even code wins; anything
+ * above 6 saturates to 6; NaN encodes to 0. Exhaustive search over 8 values. */
+ORACLE_API uint8_t oracle_e2m1_encode_mag(float u) {
+    if (!(u == u)) return 0;
+    if (u > 6.0f) return 7;
+    uint8_t best = 0;
+    double best_d = fabs((double)u - (double)E2M1_MAG[0]);
+    for (uint8_t c = 1; c < 8; ++c) {
+        double d = fabs((double)u - (double)E2M1_MAG[c]);
+        if (d < best_d || (d == best_d && (c & 1u) == 0 && (best & 1u) == 1)) {
+            best = c;
+            best_d = d;
+        }
+    }
+    return best;
+}
+
+/* ---------------------------------------------------------------- E4M3 ---- */
+
+/* E4M3 (FN) decode: 4 exponent bits (bias 7), 3 mantissa bits, no infinities,
+ * S.1111.111 is NaN. Subnormals are m * 2^-9. Written from the format definition. */
+ORACLE_API float oracle_e4m3_value(uint8_t code) {
+    int s = (code >> 7) & 1;
+    int e = (code >> 3) & 15;
+    int m = code & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9);
+    else
+        v = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return (float)(s ? -v : v);
+}
+
+/* Nearest non-negative finite E4M3 value to t (codes 0x00..0x7E); ties go to the
+ * even code; t above 448 saturates to 448 (0x7E); NaN and t <= 0 give 0x00.
+ * Exhaustive search over the 127 candidate codes. */
+static float e4m3_table[0x7F];
+static int e4m3_table_ready = 0;
+
+ORACLE_API uint8_t oracle_e4m3_encode(float t) {
+    if (!(t > 0.0f)) return 0;
+    if (t >= 448.0f) return 0x7E;
+    if (!e4m3_table_ready) { /* decoded values of codes 0x00..0x7E, filled once */
+        for (int c = 0; c <= 0x7E; ++c) e4m3_table[c] = oracle_e4m3_value((uint8_t)c);
+        e4m3_table_ready = 1;
+    }
+    uint8_t best = 0;
+    double best_d = fabs((double)t);
+    for (int c = 1; c <= 0x7E; ++c) {
+        double d = fabs((double)t - (double)e4m3_table[c]);
+        if (d < best_d || (d == best_d && (c & 1) == 0 && (best & 1u) == 1)) {
+            best = (uint8_t)c;
+            best_d = d;
+        }
+    }
+    return best;
+}
+
+/* ---------------------------------------------------------------- E8M0 ---- */
+
+/* MXFP4 block scale byte for a block whose largest magnitude is a (a >= 0):
+ * the scale is 2^(floor(log2 a) - 2), stored as the biased exponent (bias 127),
+ * clamped to [-127, 127]; a == 0 gives 0x00. floor(log2 a) comes from frexp,
+ * which is exact for every finite binary32 value including subnormals. */
+ORACLE_API uint8_t oracle_e8m0_for_amax(float a) {
+    if (!(a > 0.0f)) return 0;
+    int ex;
+    (void)frexp((double)a, &ex); /* a = f * 2^ex, f in [0.5, 1) */
+    int e = (ex - 1) - 2;
+    if (e < -127) e = -127;
+    if (e > 127) e = 127;
+    return (uint8_t)(e + 127);
+}
+
+ORACLE_API float oracle_e8m0_value(uint8_t b) {
+    return (float)ldexp(1.0, (int)b - 127);
+}
+
+/* ------------------------------------------------------- NVFP4 rows ---- */
+
+/* Tensor (global) scale from an absolute maximum: amax / (6 * 448). */
+ORACLE_API float oracle_nvfp4_global_scale(float amax) {
+    return amax / 2688.0f;
+}
+
+ORACLE_API float oracle_absmax(const float* v, int64_t n) {
+    float a = 0.0f;
+    for (int64_t i = 0; i < n; ++i) {
+        float u = fabsf(v[i]);
+        if (u > a) a = u;
+    }
+    return a;
+}
+
+/* Quantize one row of K values (K a multiple of 16) with a given tensor scale s_g
+ * (Appendix B.2, Eqs. 8-10, in the reading above).
+ * codes: K/2 bytes (low nibble = even index); scales: K/16 E4M3 bytes;
+ * deq (optional): the K dequantized values fl(s~ * e). */
+ORACLE_API void oracle_nvfp4_quantize_row(const float* v, int64_t K, float s_g,
+                                          uint8_t* codes, uint8_t* scales, float* deq) {
+    for (int64_t b = 0; b < K / 16; ++b) {
+        const float* blk = v + 16 * b;
+        float amax_b = oracle_absmax(blk, 16);
+        float t = amax_b / (6.0f * s_g);
+        uint8_t sb = oracle_e4m3_encode(t);
+        float S_b = oracle_e4m3_value(sb);
+        float st = S_b * s_g; /* effective scale s~ */
+        scales[b] = sb;
+        for (int j = 0; j < 16; ++j) {
+            float x = blk[j];
+            uint8_t mag = 0;
+            if (st != 0.0f) {
+                float q = x / st;
+                mag = oracle_e2m1_encode_mag(fabsf(q));
+            }
+            uint8_t code = (uint8_t)((signbit(x) ? 8u : 0u) | mag);
+            int64_t k = 16 * b + j;
+            if ((k & 1) == 0)
+                codes[k / 2] = code;
+            else
+                codes[k / 2] = (uint8_t)(codes[k / 2] | (code << 4));
+            if (deq) deq[k] = st * oracle_e2m1_value(code);
+        }
+    }
+}
+
+/* ------------------------------------------------------- MXFP4 rows ---- */
+
+/* Quantize one row of K values (K a multiple of 32): per 32-block E8M0 scale X,
+ * elements q = v / X rounded to E2M1 (saturating at 6); deq = X * e. */
+ORACLE_API void oracle_mxfp4_quantize_row(const float* v, int64_t K,
+                                          uint8_t* codes, uint8_t* scales, float* deq) {
+    for (int64_t b = 0; b < K / 32; ++b) {
+        const float* blk = v + 32 * b;
+        float amax_b = oracle_absmax(blk, 32);
+        uint8_t e8 = oracle_e8m0_for_amax(amax_b);
+        float X = oracle_e8m0_value(e8);
+        scales[b] = e8;
+        for (int j = 0; j < 32; ++j) {
+            float x = blk[j];
+            float q = x / X;
+            uint8_t mag = oracle_e2m1_encode_mag(fabsf(q));
+            uint8_t code = (uint8_t)((signbit(x) ? 8u : 0u) | mag);
+            int64_t k = 32 * b + j;
+            if ((k & 1) == 0)
+                codes[k / 2] = code;
+            else
+                codes[k / 2] = (uint8_t)(codes[k / 2] | (code << 4));
+            if (deq) deq[k] = X * oracle_e2m1_value(code);
+        }
+    }
+}
+
+/* ------------------------------------------- activations with residue ---- */
+
+/* Quantize M activation rows; with_residue != 0 also forms r = x - deq(q(x)) in
+ * fp32 and quantizes it "the same way" (its own per-row tensor scale for NVFP4).
+ * Output rows are stacked [X^; R^]: rows 0..M-1 base, rows M..2M-1 residue.
+ * fmt: 0 = NVFP4, 1 = MXFP4.
+ * codes: R x K/2; scales: R x K/blk; globals: R floats (NVFP4; zeros for MXFP4);
+ * deq: R x K floats (optional); resid: M x K floats (optional; the fp32 residue). */
+ORACLE_API void oracle_quantize_act(int fmt, const float* x, int64_t M, int64_t K,
+                                    int with_residue, uint8_t* codes, uint8_t* scales,
+                                    float* globals, float* deq, float* resid) {
+    int64_t blk = fmt == 0 ? 16 : 32;
+    for (int64_t m = 0; m < M; ++m) {
+        const float* row = x + m * K;
+        float* drow = deq ? deq + m * K : (float*)0;
+        if (fmt == 0) {
+            float sg = oracle_nvfp4_global_scale(oracle_absmax(row, K));
+            globals[m] = sg;
+            oracle_nvfp4_quantize_row(row, K, sg, codes + m * (K / 2), scales + m * (K / blk), drow);
+        } else {
+            globals[m] = 0.0f;
+            oracle_mxfp4_quantize_row(row, K, codes + m * (K / 2), scales + m * (K / blk), drow);
+        }
+    }
+    if (!with_residue) return;
+    /* residue r = x - deq(q(x)): the dequantized base is rebuilt from the stored
+     * codes and scales with the same association, fl(fl(S_b * s_g) * e) */
+    for (int64_t m = 0; m < M; ++m) {
+        const float* row = x + m * K;
+        float* r = resid + m * K;
+        const uint8_t* c = codes + m * (K / 2);
+        const uint8_t* s = scales + m * (K / blk);
+        for (int64_t k = 0; k < K; ++k) {
+            uint8_t code = (uint8_t)((k & 1) ? (c[k / 2] >> 4) : (c[k / 2] & 15u));
+            float e = oracle_e2m1_value(code);
+            float dk;
+            if (fmt == 0)
+                dk = (oracle_e4m3_value(s[k / 16]) * globals[m]) * e;
+            else
+                dk = oracle_e8m0_value(s[k / 32]) * e;
+            r[k] = row[k] - dk;
+        }
+        int64_t rr = M + m;
+        float* drow = deq ? deq + rr * K : (float*)0;
+        if (fmt == 0) {
+            float sg = oracle_nvfp4_global_scale(oracle_absmax(r, K));
+            globals[rr] = sg;
+            oracle_nvfp4_quantize_row(r, K, sg, codes + rr * (K / 2), scales + rr * (K / blk), drow);
+        } else {
+            globals[rr] = 0.0f;
+            oracle_mxfp4_quantize_row(r, K, codes + rr * (K / 2), scales + rr * (K / blk), drow);
+        }
+    }
+}
+
+/* ----------------------------------------------------------- weights ---- */
+
+/* Quantize nrows weight rows of length K. NVFP4 uses the given per-tensor scale
+ * s_gw (from the absolute maximum over the whole tensor); MXFP4 ignores it. */
+ORACLE_API void oracle_quantize_weight_rows(int fmt, const float* W, int64_t nrows, int64_t K,
+                                            float s_gw, uint8_t* codes, uint8_t* scales,
+                                            float* deq) {
+    int64_t blk = fmt == 0 ? 16 : 32;
+    for (int64_t n = 0; n < nrows; ++n) {
+        float* drow = deq ? deq + n * K : (float*)0;
+        if (fmt == 0)
+            oracle_nvfp4_quantize_row(W + n * K, K, s_gw, codes + n * (K / 2), scales + n * (K / blk), drow);
+        else
+            oracle_mxfp4_quantize_row(W + n * K, K, codes + n * (K / 2), scales + n * (K / blk), drow);
+    }
+}
+
+/* ------------------------------------------------------------ linear ---- */
+
+/* y[m, n] = sum_k dx[m, k] * dw[n, k] (+ sum_k dr[m, k] * dw[n, k] when
+ * compensated), accumulated in binary64 over exact fp32 x fp32 products.
+ * dx holds the stacked dequantized activation rows: rows 0..M-1 base and, when
+ * compensated, rows M..2M-1 residue (Eq. 2's [X^; R^] with the Fold).
+ * beta[m, n] = sum_k |dx dw| (+ |dr dw|): the scale of the rounding bound. */
+ORACLE_API void oracle_linear(const float* dx, const float* dw, int64_t M, int64_t N, int64_t K,
+                              int compensated, double* y, double* beta) {
+    for (int64_t m = 0; m < M; ++m) {
+        const float* xb = dx + m * K;
+        const float* xr = compensated ? dx + (M + m) * K : (const float*)0;
+        for (int64_t n = 0; n < N; ++n) {
+            const float* w = dw + n * K;
+            double acc = 0.0, mag = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double p = (double)xb[k] * (double)w[k];
+                acc += p;
+                mag += fabs(p);
+            }
+            if (xr) {
+                for (int64_t k = 0; k < K; ++k) {
+                    double p = (double)xr[k] * (double)w[k];
+                    acc += p;
+                    mag += fabs(p);
+                }
+            }
+            y[m * N + n] = acc;
+            if (beta) beta[m * N + n] = mag;
+        }
+    }
+}
