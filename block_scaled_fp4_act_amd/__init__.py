@@ -1,1 +1,185 @@
-"""Residue-compensated block-scaled FP4 linear for AMD Instinct MI355X (gfx950)."""
+"""Residue-compensated block-scaled FP4 linear for AMD Instinct MI355X (gfx950).
+
+A thin binding over the C ABI in include/rsfp4.h (librsfp4.so): it only
+marshals torch tensors (device memory) and the current HIP stream into the C
+calls; every step of the path runs in the library's HIP kernels.  There is no
+CPU fallback: a missing library raises.
+
+Names follow the C ABI: ``nvfp4_prepack_weights``, ``nvfp4_quantize_act_with_residue``,
+``nvfp4_linear``, ``nvfp4_linear_compensated`` and the ``mxfp4_`` twins, plus the
+format-generic ``prepack_weights``, ``quantize_act_with_residue``, ``fp4_linear``
+and ``fp4_linear_compensated``.
+"""
+import ctypes
+
+from ._lib import lib
+
+NVFP4, MXFP4 = 0, 1
+F32, BF16 = 0, 1
+BLOCK = {NVFP4: 16, MXFP4: 32}
+_FMT_NAME = {NVFP4: "nvfp4", MXFP4: "mxfp4"}
+
+
+def _fmt(fmt):
+    if isinstance(fmt, str):
+        fmt = {"nvfp4": NVFP4, "mxfp4": MXFP4}[fmt.lower()]
+    return int(fmt)
+
+
+def _check(status):
+    if status != 0:
+        L = lib()
+        raise RuntimeError(f"rsfp4: {L.rsfp4_status_string(status).decode()}: "
+                           f"{L.rsfp4_last_error().decode()}")
+
+
+def _stream(t):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+# ------------------------------------------------------------------ sizes --
+
+def act_row_bytes(fmt, K):
+    return int(lib().rsfp4_act_row_bytes(_fmt(fmt), K))
+
+
+def packed_act_bytes(fmt, M, K, with_residue=True):
+    return int(lib().rsfp4_packed_act_bytes(_fmt(fmt), M, K, 1 if with_residue else 0))
+
+
+def packed_weight_bytes(fmt, N, K):
+    return int(lib().rsfp4_packed_weight_bytes(_fmt(fmt), N, K))
+
+
+def workspace_bytes(fmt, M, N, K, compensated=True):
+    return int(lib().rsfp4_workspace_bytes(_fmt(fmt), M, N, K, 1 if compensated else 0))
+
+
+# ---------------------------------------------------------------- prepack --
+
+def prepack_weights(W, fmt, out=None):
+    """Quantize W[N, K] (cuda, fp32/bf16) into a packed uint8 blob (offline step)."""
+    import torch
+    fmt = _fmt(fmt)
+    assert W.is_cuda and W.dim() == 2 and W.is_contiguous()
+    N, K = W.shape
+    nbytes = packed_weight_bytes(fmt, N, K)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=W.device)
+    fn = getattr(lib(), f"rsfp4_{_FMT_NAME[fmt]}_prepack_weights")
+    _check(fn(_ptr(W), _dtype_code(W), N, K, _ptr(out), out.numel(), _stream(W)))
+    return out
+
+
+def nvfp4_prepack_weights(W, out=None):
+    return prepack_weights(W, NVFP4, out)
+
+
+def mxfp4_prepack_weights(W, out=None):
+    return prepack_weights(W, MXFP4, out)
+
+
+# --------------------------------------------------------------- quantize --
+
+def quantize_act_with_residue(x, fmt, with_residue=True, out=None):
+    """Quantize x[M, K] (cuda, fp32/bf16) into the activation buffer (uint8)."""
+    import torch
+    fmt = _fmt(fmt)
+    assert x.is_cuda and x.dim() == 2 and x.is_contiguous()
+    M, K = x.shape
+    nbytes = packed_act_bytes(fmt, M, K, with_residue)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+    fn = getattr(lib(), f"rsfp4_{_FMT_NAME[fmt]}_quantize_act_with_residue")
+    _check(fn(_ptr(x), _dtype_code(x), M, K, 1 if with_residue else 0, _ptr(out), out.numel(), _stream(x)))
+    return out
+
+
+def nvfp4_quantize_act_with_residue(x, with_residue=True, out=None):
+    return quantize_act_with_residue(x, NVFP4, with_residue, out)
+
+
+def mxfp4_quantize_act_with_residue(x, with_residue=True, out=None):
+    return quantize_act_with_residue(x, MXFP4, with_residue, out)
+
+
+def act_views(act, fmt, M, K, with_residue=True):
+    """Canonical views into an activation buffer: codes [R, K/2], scales
+    [R, K/blk] (uint8) and the per-row fp32 tensor scales [R] (slicing only)."""
+    fmt = _fmt(fmt)
+    R = 2 * M if with_residue else M
+    rb = act_row_bytes(fmt, K)
+    rows = act[: R * rb].view(R, rb)
+    codes = rows[:, 16:16 + K // 2]
+    scales = rows[:, 16 + K // 2:16 + K // 2 + K // BLOCK[fmt]]
+    globs = rows[:, 0:4].contiguous().view(-1).view(__import__("torch").float32)
+    return codes, scales, globs
+
+
+# ----------------------------------------------------------------- linear --
+
+def _linear(act, w_packed, M, N, K, fmt, comp, out):
+    import torch
+    fmt = _fmt(fmt)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=act.device)
+    assert out.is_cuda and out.dtype == torch.float32 and out.is_contiguous() and out.numel() >= M * N
+    name = f"rsfp4_{_FMT_NAME[fmt]}_linear" + ("_compensated" if comp else "")
+    _check(getattr(lib(), name)(_ptr(act), act.numel(), _ptr(w_packed), w_packed.numel(), M, N, K,
+                                _ptr(out), None, 0, _stream(act)))
+    return out
+
+
+def fp4_linear(act, w_packed, M, N, K, fmt, out=None):
+    """y = deq(q(x)) W^T (plain W4A4), fp32 [M, N]."""
+    return _linear(act, w_packed, M, N, K, fmt, False, out)
+
+
+def fp4_linear_compensated(act, w_packed, M, N, K, fmt, out=None):
+    """y = deq(q(x)) W^T + deq(q(r)) W^T (residue-compensated), fp32 [M, N]."""
+    return _linear(act, w_packed, M, N, K, fmt, True, out)
+
+
+def nvfp4_linear(act, w_packed, M, N, K, out=None):
+    return _linear(act, w_packed, M, N, K, NVFP4, False, out)
+
+
+def nvfp4_linear_compensated(act, w_packed, M, N, K, out=None):
+    return _linear(act, w_packed, M, N, K, NVFP4, True, out)
+
+
+def mxfp4_linear(act, w_packed, M, N, K, out=None):
+    return _linear(act, w_packed, M, N, K, MXFP4, False, out)
+
+
+def mxfp4_linear_compensated(act, w_packed, M, N, K, out=None):
+    return _linear(act, w_packed, M, N, K, MXFP4, True, out)
+
+
+# ------------------------------------------------------------ test/debug --
+
+def unpack_weights_canonical(w_packed, fmt, N, K):
+    """Canonical codes [N, K/2], scales [N, K/blk] and the NVFP4 tensor scale."""
+    import torch
+    fmt = _fmt(fmt)
+    dev = w_packed.device
+    codes = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((N, K // BLOCK[fmt]), dtype=torch.uint8, device=dev)
+    s_g = torch.zeros(1, dtype=torch.float32, device=dev)
+    _check(lib().rsfp4_unpack_weights_canonical(_ptr(w_packed), w_packed.numel(), fmt, N, K, _ptr(codes),
+                                                _ptr(scales), _ptr(s_g), _stream(w_packed)))
+    return codes, scales, s_g

@@ -1,0 +1,88 @@
+// codec.h -- device-side E2M1 / E4M3 / E8M0 codecs for the gfx950 kernels.
+//
+// Formats as defined on the ResServe page (arXiv 2611.08713), Section 2 and
+// Figure 1: E2M1 elements (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), E4M3 block
+// scales (largest finite 448) for NVFP4, power-of-two E8M0 block scales for
+// MXFP4.  Every encoder rounds to nearest with ties to even and saturates; the
+// arithmetic is IEEE binary32 (these files build with -ffp-contract=off and
+// without fast-math, so division is correctly rounded and nothing fuses).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rsfp4 {
+
+// Magnitude code (0..7) of the E2M1 value nearest to u >= 0, ties to the even
+// code, saturating at 6. The midpoints between neighbouring magnitudes are
+// 0.25, 0.75, 1.25, 1.75, 2.5, 3.5 and 5; at a midpoint the even code wins, so
+// the comparison is "<=" towards an even lower neighbour and "<" towards an
+// odd one. A NaN argument compares false everywhere and gives code 0.
+__device__ __forceinline__ uint32_t e2m1_mag(float u) {
+    uint32_t c = 0;
+    c += (u > 0.25f);
+    c += (u >= 0.75f);
+    c += (u > 1.25f);
+    c += (u >= 1.75f);
+    c += (u > 2.5f);
+    c += (u >= 3.5f);
+    c += (u > 5.0f);
+    return c;
+}
+
+// Signed E2M1 value of a 4-bit code as float (bit 3 = sign).
+__device__ __forceinline__ float e2m1_val(uint32_t code) {
+    // magnitudes packed as halves of 2*value: 0,1,2,3,4,6,8,12
+    const uint32_t twice = (0xC8643210u >> (4 * (code & 7u))) & 15u;
+    float v = (float)twice * 0.5f;
+    return (code & 8u) ? -v : v;
+}
+
+// E4M3 (FN variant) byte -> value, for bytes 0x00..0x7e (non-negative scales).
+__device__ __forceinline__ float e4m3_val(uint32_t b) {
+    const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+    const float sub = (float)m * 0.001953125f;               // m * 2^-9
+    const float nrm = __uint_as_float(((e + 120u) << 23) | (m << 20));
+    return e ? nrm : sub;
+}
+
+// Non-negative t -> E4M3 byte: nearest finite value, ties to even code,
+// saturating at 448 (0x7e, never the NaN code 0x7f); t NaN or <= 0 -> 0.
+// The subnormal range [0, 2^-6) is a uniform grid of step 2^-9, so the code is
+// rint(t * 2^9); above it the 3-bit mantissa of t is rounded with rint.
+__device__ __forceinline__ uint32_t e4m3_encode(float t) {
+    if (!(t > 0.0f)) return 0u;
+    if (t >= 448.0f) return 0x7Eu;
+    if (t < 0.015625f) {                                      // below 2^-6
+        return (uint32_t)__builtin_rintf(t * 512.0f);         // 0..8; 8 = 2^-6
+    }
+    const uint32_t bits = __float_as_uint(t);
+    const int e = (int)((bits >> 23) & 255u) - 127;           // -6 .. 8
+    const float m = __uint_as_float((bits & 0x007FFFFFu) | 0x3F800000u); // [1,2)
+    uint32_t mm = (uint32_t)__builtin_rintf((m - 1.0f) * 8.0f);  // 0..8
+    uint32_t code = ((uint32_t)(e + 7) << 3) + mm;            // mm == 8 carries
+    return code > 0x7Eu ? 0x7Eu : code;
+}
+
+// MXFP4: E8M0 byte for a block whose largest magnitude is a >= 0:
+// floor(log2 a) - 2 biased by 127, clamped to [0, 254]; a == 0 -> 0.
+__device__ __forceinline__ uint32_t e8m0_for_amax(float a) {
+    if (!(a > 0.0f)) return 0u;
+    const uint32_t bits = __float_as_uint(a);
+    const int ef = (int)(bits >> 23);                         // a >= 0: no sign
+    int fl;                                                   // floor(log2 a)
+    if (ef > 0) {
+        fl = ef - 127;
+    } else {                                                  // subnormal
+        fl = (31 - __builtin_clz(bits)) - 149;
+    }
+    int e = fl - 2;
+    e = e < -127 ? -127 : (e > 127 ? 127 : e);
+    return (uint32_t)(e + 127);
+}
+
+// E8M0 byte -> 2^(b-127) as binary32 (b = 0 gives the subnormal 2^-127).
+__device__ __forceinline__ float e8m0_val(uint32_t b) {
+    return b ? __uint_as_float(b << 23) : __uint_as_float(0x00400000u);
+}
+
+}  // namespace rsfp4

@@ -1,0 +1,32 @@
+// kernels.h -- internal launchers of the gfx950 kernels (not part of the ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rsfp4 {
+
+hipError_t launch_quantize_act(int fmt, int xt_bf16, const void* x, int M, int64_t K, int with_res,
+                               void* act, hipStream_t s);
+
+hipError_t launch_prepack(int fmt, int wt_bf16, const void* W, int64_t N, int64_t K, void* blob,
+                          hipStream_t s);
+
+hipError_t launch_unpack(int fmt, const void* blob, int64_t N, int64_t K, uint8_t* codes,
+                         uint8_t* scales, float* s_g, hipStream_t s);
+
+// Launch shape of the narrow-M linear: rt row tiles of 16, maxs steps per wave,
+// kw waves per workgroup along K, grid workgroups (grid-stride over channel groups).
+struct GemmPlan {
+    int rt = 1;
+    int maxs = 1;
+    int kw = 1;
+    int64_t grid = 1;
+};
+
+GemmPlan plan_gemm_small(int64_t M, int64_t N, int64_t K, bool comp, int num_cus);
+
+hipError_t launch_gemm_small(int fmt, const GemmPlan& pl, bool comp, const void* act,
+                             int64_t row_bytes, const void* blob, int M, int64_t N, int64_t K,
+                             float* y, hipStream_t s);
+
+}  // namespace rsfp4

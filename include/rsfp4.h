@@ -1,0 +1,173 @@
+/*
+ * rsfp4.h -- C ABI of the residue-compensated block-scaled FP4 linear layer for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the full-residue decode linear of the page "ResServe: Accurate
+ * and Efficient FP4 LLM Inference with Residue Compensation" (arXiv 2611.08713):
+ *   - activations x[M,K] are quantized at run time to NVFP4 or MXFP4 (Section 2,
+ *     Figure 1; NVFP4 scale rules of Appendix B.2, Eqs. 8-10);
+ *   - the residue r = x - deq(q(x)) is formed in registers and quantized the same
+ *     way (Section 2; Section 4.4: residue generation fused into the quantizer);
+ *   - weights are quantized and laid out once, offline (Figure 1c; Section 5.4:
+ *     weight preparation happens once during export);
+ *   - the compensated product y = deq(q(x)) W^T + deq(q(r)) W^T is the stacked
+ *     GEMM [X^; R^] W^T whose paired rows are added on chip (Section 4.2, Eq. 1;
+ *     Section 4.3, Eq. 2, the Fold), reading each weight tile once.
+ *
+ * Numerics (both formats): E2M1 elements rounded to nearest, ties to even,
+ * saturated at +-6; the element with the even K index sits in the low nibble.
+ *   NVFP4: 16-element blocks, E4M3 (FN) block scale, fp32 tensor scale
+ *     s_g = amax / 2688 (per row for x and for r, per tensor for W);
+ *     block byte = E4M3_RNE(blockmax / (6 * s_g)) saturated at 448 (0x7e);
+ *     element = E2M1_RNE(v / (S_b * s_g)); value = (S_b * s_g) * e.
+ *   MXFP4: 32-element blocks, E8M0 scale 2^(floor(log2 blockmax) - 2) clamped to
+ *     [2^-127, 2^127] (byte 0 for an all-zero block), no tensor scale;
+ *     element = E2M1_RNE(v / X); value = X * e.
+ *   The output y is fp32, accumulated in fp32 on the matrix cores.
+ *   NaN or infinite inputs give unspecified codes and outputs.
+ *
+ * Conventions for every call:
+ *   - Pointers named W, x, act, w_packed, y, codes, scales, s_g are DEVICE
+ *     pointers owned by the caller; the library allocates no device memory and
+ *     keeps no device state besides its code objects.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Every
+ *     call only enqueues work on it and returns; nothing synchronizes except
+ *     where a call says so.
+ *   - Arguments are validated on the host before anything is enqueued. A failed
+ *     check returns a status other than RSFP4_OK, enqueues nothing, and leaves
+ *     a message for rsfp4_last_error() (per thread). A HIP launch failure returns
+ *     RSFP4_ERR_HIP with the HIP error string in the message.
+ *   - Shape limits: M >= 1, N >= 1, K >= 32 and K % 32 == 0 (both formats, so a
+ *     K-run of 32 is whole in either block size); quantize needs K <= 32768;
+ *     the linear needs K <= 16384 and B <= 32 activation rows, where B = M for
+ *     the plain call and B = 2M for the compensated call.  Calls outside these
+ *     limits return RSFP4_ERR_SHAPE or RSFP4_ERR_UNSUPPORTED.
+ *   - All calls are thread-safe; concurrent calls on different streams are
+ *     independent.
+ */
+#ifndef RSFP4_H
+#define RSFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RSFP4_ABI_VERSION 1
+
+typedef enum { RSFP4_NVFP4 = 0, RSFP4_MXFP4 = 1 } rsfp4_format;
+typedef enum { RSFP4_F32 = 0, RSFP4_BF16 = 1 } rsfp4_dtype;
+
+typedef enum {
+    RSFP4_OK = 0,
+    RSFP4_ERR_NULL = 1,             /* a required pointer is NULL */
+    RSFP4_ERR_SHAPE = 2,            /* M, N or K outside the documented limits */
+    RSFP4_ERR_ALIGN = 3,            /* a buffer is not 16-byte aligned */
+    RSFP4_ERR_FORMAT = 4,           /* unknown format or dtype */
+    RSFP4_ERR_BUFFER_TOO_SMALL = 5, /* a byte count is below the size query */
+    RSFP4_ERR_UNSUPPORTED = 6,      /* valid request this build does not run */
+    RSFP4_ERR_HIP = 7               /* the HIP runtime reported an error */
+} rsfp4_status;
+
+/* Version of this ABI (RSFP4_ABI_VERSION of the built library). */
+int rsfp4_abi_version(void);
+/* Static string naming a status code; never NULL. */
+const char* rsfp4_status_string(int status);
+/* Detail of the last failed call on this thread ("" if none); valid until the
+ * next call on the same thread. */
+const char* rsfp4_last_error(void);
+
+/* ------------------------------------------------------------------ sizes --
+ * Activation buffer ("act"): one record per quantized row, rows stacked as in
+ * Eq. 2 of the ResServe page: rows 0..M-1 hold q(x), rows M..2M-1 hold q(r)
+ * (present when quantized with_residue).  Record layout, stride
+ * rsfp4_act_row_bytes(fmt, K) (a multiple of 16):
+ *   [0, 4)              fp32 tensor scale s_g of the row (NVFP4; 0 for MXFP4)
+ *   [4, 16)             zero
+ *   [16, 16 + K/2)      E2M1 codes, element 2j in the low nibble of byte j
+ *   [16 + K/2, +K/blk)  block scale bytes (E4M3 for NVFP4, E8M0 for MXFP4)
+ *   then padding to the stride, left unwritten (unspecified).
+ * The first M records of a with_residue buffer form a valid plain buffer. */
+size_t rsfp4_act_row_bytes(int fmt, int64_t K);
+size_t rsfp4_packed_act_bytes(int fmt, int64_t M, int64_t K, int with_residue);
+
+/* Packed weight blob: a 256-byte header (magic "RSF4", ABI version, format, N,
+ * K, the NVFP4 per-tensor scale) followed by ceil(N/16) groups of 16 output
+ * channels; each group holds ceil(K/128) steps of 128 K-elements, and each step
+ * is 1024 bytes of codes laid out for one 64-lane wave load (lane l = 16*g + i
+ * holds channel i, K-elements 32*g .. 32*g+31 of the step) followed by that
+ * step's block scales (NVFP4: 2 bytes per lane, 128 bytes; MXFP4: 1 byte per
+ * lane, 64 bytes).  Channels beyond N and K-elements beyond K are zero codes
+ * with zero scales. Only rsfp4_unpack_weights_canonical reads it back. */
+size_t rsfp4_packed_weight_bytes(int fmt, int64_t N, int64_t K);
+
+/* Device workspace the linear calls need; this build needs none and returns 0
+ * (pass ws = NULL, ws_bytes = 0). */
+size_t rsfp4_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, int compensated);
+
+/* ------------------------------------------------------------- prepack ----
+ * Quantize W[N,K] (row-major, dtype wt: RSFP4_F32 or RSFP4_BF16) once, offline,
+ * into the packed blob at w_packed (w_packed_bytes >= rsfp4_packed_weight_bytes,
+ * 256-byte aligned).  NVFP4 takes one tensor scale from max|W| over the whole
+ * tensor (ResServe Appendix B.2, Eq. 8 with a per-tensor alpha); MXFP4 scales
+ * each 32-block (Section 2).  Enqueues three kernels; W may be freed once the
+ * stream has passed them. */
+rsfp4_status rsfp4_nvfp4_prepack_weights(const void* W, int wt, int64_t N, int64_t K,
+                                         void* w_packed, size_t w_packed_bytes, void* stream);
+rsfp4_status rsfp4_mxfp4_prepack_weights(const void* W, int wt, int64_t N, int64_t K,
+                                         void* w_packed, size_t w_packed_bytes, void* stream);
+
+/* ------------------------------------------------------------ quantize ----
+ * Quantize x[M,K] (row-major, dtype xt) to the activation buffer act
+ * (act_bytes >= rsfp4_packed_act_bytes(fmt, M, K, with_residue), 16-byte
+ * aligned).  One pass per row: row amax, tensor scale, block scales, codes;
+ * with_residue != 0 also forms r = x - deq(q(x)) in fp32 registers and quantizes
+ * it with its own row amax (ResServe Section 4.4 and Appendix B.2, Algorithm 1:
+ * residue and base produced in the same pass). */
+rsfp4_status rsfp4_nvfp4_quantize_act_with_residue(const void* x, int xt, int64_t M, int64_t K,
+                                                   int with_residue, void* act, size_t act_bytes,
+                                                   void* stream);
+rsfp4_status rsfp4_mxfp4_quantize_act_with_residue(const void* x, int xt, int64_t M, int64_t K,
+                                                   int with_residue, void* act, size_t act_bytes,
+                                                   void* stream);
+
+/* -------------------------------------------------------------- linear ----
+ * y[M,N] (fp32, row-major, fully overwritten) from a quantized activation
+ * buffer and a packed weight blob of the same format and the same N, K.
+ *   *_linear:              y = deq(q(x)) W^T                 (B = M rows; the
+ *                          buffer may or may not hold residue rows)
+ *   *_linear_compensated:  y = deq(q(x)) W^T + deq(q(r)) W^T (B = 2M rows; the
+ *                          buffer must have been quantized with_residue)
+ * Each packed weight step is loaded from HBM once and multiplied with all B
+ * activation rows; base and residue products of one token land in the same
+ * lane's accumulators and are added there before the single store (ResServe
+ * Section 4.3, Eq. 2 and Section 5.1, Eq. 4).  act_bytes and w_packed_bytes are
+ * checked against the size queries. */
+rsfp4_status rsfp4_nvfp4_linear(const void* act, size_t act_bytes, const void* w_packed,
+                                size_t w_packed_bytes, int64_t M, int64_t N, int64_t K,
+                                float* y, void* ws, size_t ws_bytes, void* stream);
+rsfp4_status rsfp4_nvfp4_linear_compensated(const void* act, size_t act_bytes, const void* w_packed,
+                                            size_t w_packed_bytes, int64_t M, int64_t N, int64_t K,
+                                            float* y, void* ws, size_t ws_bytes, void* stream);
+rsfp4_status rsfp4_mxfp4_linear(const void* act, size_t act_bytes, const void* w_packed,
+                                size_t w_packed_bytes, int64_t M, int64_t N, int64_t K,
+                                float* y, void* ws, size_t ws_bytes, void* stream);
+rsfp4_status rsfp4_mxfp4_linear_compensated(const void* act, size_t act_bytes, const void* w_packed,
+                                            size_t w_packed_bytes, int64_t M, int64_t N, int64_t K,
+                                            float* y, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------- test / debug ----
+ * Rewrite a packed blob in canonical row-major form: codes[N, K/2] (low nibble
+ * = even K index), scales[N, K/blk], and (NVFP4) the tensor scale to *s_g
+ * (a device pointer to one float; may be NULL for MXFP4).  Enqueued on stream. */
+rsfp4_status rsfp4_unpack_weights_canonical(const void* w_packed, size_t w_packed_bytes, int fmt,
+                                            int64_t N, int64_t K, uint8_t* codes, uint8_t* scales,
+                                            float* s_g, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RSFP4_H */

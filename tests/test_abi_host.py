@@ -1,0 +1,107 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/rsfp4.h declares, answers the size queries, and rejects
+bad arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_scaled_fp4_act_amd as rs
+from block_scaled_fp4_act_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "rsfp4.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(rsfp4_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = rs.lib()
+    names = _declared()
+    assert len(names) >= 16
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(_lib.SIGNATURES), "binding signatures out of sync with the header"
+
+
+def test_version_and_strings():
+    L = rs.lib()
+    assert L.rsfp4_abi_version() == 1
+    for s in range(8):
+        assert L.rsfp4_status_string(s)
+    assert L.rsfp4_status_string(99) == b"unknown status"
+
+
+def test_size_queries():
+    # act records: 16-byte head + K/2 codes + K/blk scales, padded to 16
+    assert rs.act_row_bytes(0, 4096) == 16 + 2048 + 256
+    assert rs.act_row_bytes(1, 4096) == 16 + 2048 + 128
+    assert rs.act_row_bytes(0, 32) == 48 and rs.act_row_bytes(1, 32) == 48
+    assert rs.packed_act_bytes(0, 4, 4096, True) == 8 * 2320
+    assert rs.packed_act_bytes(0, 4, 4096, False) == 4 * 2320
+    # weights: header + groups(16 ch) x steps(128 K) x (1 KB codes + scales)
+    assert rs.packed_weight_bytes(0, 4096, 4096) == 256 + 256 * 32 * 1152
+    assert rs.packed_weight_bytes(1, 25600, 5120) == 256 + 1600 * 40 * 1088
+    assert rs.packed_weight_bytes(0, 17, 160) == 256 + 2 * 2 * 1152
+    assert rs.workspace_bytes(0, 4, 4096, 4096, True) == 0
+    # invalid requests size to 0
+    assert rs.packed_weight_bytes(0, 16, 48) == 0
+    assert rs.packed_weight_bytes(2, 16, 64) == 0
+    assert rs.act_row_bytes(0, 0) == 0
+
+
+def _err():
+    return rs.lib().rsfp4_last_error().decode()
+
+
+FAKE = ctypes.c_void_p(0x100000)  # never dereferenced: validation fails first
+
+
+def test_validation_errors_without_device():
+    L = rs.lib()
+    # null pointers
+    assert L.rsfp4_nvfp4_linear(None, 0, None, 0, 1, 16, 128, None, None, 0, None) == 1
+    assert "non-NULL" in _err()
+    # bad K
+    assert L.rsfp4_nvfp4_linear(FAKE, 1 << 20, FAKE, 1 << 20, 1, 16, 100, FAKE, None, 0, None) == 2
+    assert L.rsfp4_mxfp4_quantize_act_with_residue(FAKE, 0, 1, 48, 1, FAKE, 1 << 20, None) == 2
+    # K above the linear's limit, B above 32
+    assert L.rsfp4_nvfp4_linear(FAKE, 1 << 30, FAKE, 1 << 30, 1, 16, 16416, FAKE, None, 0, None) == 6
+    assert L.rsfp4_mxfp4_linear_compensated(FAKE, 1 << 30, FAKE, 1 << 30, 17, 16, 512, FAKE, None, 0, None) == 6
+    # quantize K limit and M limit
+    assert L.rsfp4_nvfp4_quantize_act_with_residue(FAKE, 0, 1, 32800, 1, FAKE, 1 << 30, None) == 2
+    assert L.rsfp4_nvfp4_quantize_act_with_residue(FAKE, 0, 0, 512, 1, FAKE, 1 << 30, None) == 2
+    # unknown dtype / format
+    assert L.rsfp4_nvfp4_quantize_act_with_residue(FAKE, 5, 1, 512, 1, FAKE, 1 << 30, None) == 4
+    assert L.rsfp4_unpack_weights_canonical(FAKE, 1 << 30, 3, 16, 512, FAKE, FAKE, None, None) == 4
+    # alignment
+    odd = ctypes.c_void_p(0x100001)
+    assert L.rsfp4_nvfp4_quantize_act_with_residue(odd, 0, 1, 512, 1, FAKE, 1 << 30, None) == 3
+    assert L.rsfp4_nvfp4_prepack_weights(FAKE, 0, 16, 512, ctypes.c_void_p(0x100010), 1 << 30, None) == 3
+    # buffer sizes
+    assert L.rsfp4_nvfp4_quantize_act_with_residue(FAKE, 0, 4, 512, 1, FAKE, 100, None) == 5
+    assert "needs" in _err()
+    assert L.rsfp4_nvfp4_prepack_weights(FAKE, 0, 16, 512, FAKE, 100, None) == 5
+    assert L.rsfp4_nvfp4_linear_compensated(FAKE, 100, FAKE, 1 << 30, 2, 16, 512, FAKE, None, 0, None) == 5
+    assert L.rsfp4_nvfp4_linear(FAKE, 1 << 30, FAKE, 100, 2, 16, 512, FAKE, None, 0, None) == 5
+
+
+def test_binding_raises_on_error():
+    with pytest.raises(RuntimeError, match="bad shape"):
+        rs._check(2) if False else rs._check(rs.lib().rsfp4_nvfp4_linear(
+            FAKE, 1 << 20, FAKE, 1 << 20, 1, 16, 100, FAKE, None, 0, None))
+
+
+def test_product_path_does_not_import_oracle():
+    """The package never reaches the oracle: no module under it names it."""
+    pkg = os.path.dirname(rs.__file__)
+    for root, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                txt = open(os.path.join(root, f)).read()
+                assert "import oracle" not in txt and "from oracle" not in txt, f
+                assert "rsfp4_oracle" not in txt, f
