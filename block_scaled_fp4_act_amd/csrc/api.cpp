@@ -121,9 +121,9 @@ rsfp4_status linear(int fmt, bool comp, const void* act, size_t act_bytes, const
     if (st != RSFP4_OK) return st;
     const GemmPlan pl = plan_gemm_small(M, N, K, comp, cus);
     if (std::getenv("RSFP4_LOG"))
-        std::fprintf(stderr, "[rsfp4] linear fmt=%d comp=%d M=%lld N=%lld K=%lld rt=%d maxs=%d kw=%d grid=%lld\n",
+        std::fprintf(stderr, "[rsfp4] linear fmt=%d comp=%d M=%lld N=%lld K=%lld rt=%d maxs=%d kw=%d grid=%lld ngl=%d\n",
                      fmt, (int)comp, (long long)M, (long long)N, (long long)K, pl.rt, pl.maxs, pl.kw,
-                     (long long)pl.grid);
+                     (long long)pl.grid, pl.ngl);
     return hip_status(launch_gemm_small(fmt, pl, comp, act, rb,
                                         w_packed, (int)M, N, K, y, (hipStream_t)stream),
                       "linear launch");

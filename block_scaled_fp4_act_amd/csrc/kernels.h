@@ -21,6 +21,7 @@ struct GemmPlan {
     int maxs = 1;
     int kw = 1;
     int64_t grid = 1;
+    int ngl = 1;       // groups reduced together (partial sums held in LDS)
 };
 
 GemmPlan plan_gemm_small(int64_t M, int64_t N, int64_t K, bool comp, int num_cus);

@@ -1,18 +1,19 @@
 // quant.hip -- fused activation quantize + residue kernel (NVFP4 and MXFP4).
 //
-// One 256-thread workgroup per activation row.  Each thread owns 16-element
-// slices j = tid + 256*c of the row and keeps them in registers for the whole
-// kernel, so the row is read from HBM once:
-//   1. row amax -> tensor scale s_g = amax / 2688 (NVFP4; ResServe Appendix B.2,
-//      Eq. 8 with the maximum taken per row)
-//   2. block scale: NVFP4 E4M3_RNE(blockmax / (6 s_g)), MXFP4 E8M0 from the
-//      32-block maximum (Section 2, Figure 1)
-//   3. element codes E2M1_RNE(v / s~) (Eq. 10), packed two per byte
+// One workgroup per activation row, T = 64..1024 threads, four or eight
+// elements per thread per chunk (the ResServe page's quantizer, Appendix B.2,
+// Algorithm 1, gives each thread eight inputs; rows up to 4096 here use four so
+// that a row fills 1024 threads), and the row held in registers for the whole
+// kernel so it is read from HBM once:
+//   1. row amax -> tensor scale s_g = amax / 2688 (NVFP4; Appendix B.2, Eq. 8
+//      with the maximum taken per row)
+//   2. block amax over the adjacent lanes that share a block (DPP lane swaps),
+//      then the block scale:
+//      NVFP4 E4M3_RNE(blockmax / (6 s_g)), MXFP4 E8M0 (Section 2, Figure 1)
+//   3. element codes E2M1_RNE(v / s~) (Eq. 10), packed into one store per thread
 //   4. residue r = v - fl(s~ e) kept in the same registers (Section 4.4: the
 //      residue is formed in registers, no second read of x)
 //   5. steps 1-3 again on r with its own row amax; the row goes to record M+m.
-// A 16-element NVFP4 block is owned by one thread; a 32-element MXFP4 block
-// spans an adjacent lane pair, whose maxima meet through one lane swap.
 #include <hip/hip_runtime.h>
 #include <hip/hip_bf16.h>
 #include <stdint.h>
@@ -25,158 +26,193 @@ namespace rsfp4 {
 
 namespace {
 
-constexpr int kQThreads = 256;
+constexpr int kQMaxThreads = 1024;
+
+// Lane exchanges through DPP (no LDS round trip): quad permutations for the
+// lanes that share a block, row mirrors and lane reads for the wave maximum.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // reverse within 8 lanes
+constexpr int kDppMirror = 0x140;     // reverse within 16 lanes
 
 __device__ __forceinline__ float wave_max(float v) {
-    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-    return v;
+    v = fmaxf(v, dpp<kDppXor1>(v));
+    v = fmaxf(v, dpp<kDppXor2>(v));
+    v = fmaxf(v, dpp<kDppHalfMirror>(v));
+    v = fmaxf(v, dpp<kDppMirror>(v));   // every lane: max of its 16-lane row
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
 // Workgroup-wide maximum of non-negative values; every thread gets the result.
 __device__ __forceinline__ float block_max(float v, float* red) {
     v = wave_max(v);
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
     __syncthreads();                       // red may still be read from a prior call
     if (lane == 0) red[wid] = v;
     __syncthreads();
     float r = red[0];
-    for (int i = 1; i < kQThreads / 64; ++i) r = fmaxf(r, red[i]);
+    for (int i = 1; i < nw; ++i) r = fmaxf(r, red[i]);
     return r;
 }
 
-template <typename T>
-__device__ __forceinline__ void load16(const T* p, float* v);
+template <typename T, int EPT>
+__device__ __forceinline__ void load_chunk(const T* p, float* v);
 
 template <>
-__device__ __forceinline__ void load16<float>(const float* p, float* v) {
+__device__ __forceinline__ void load_chunk<float, 8>(const float* p, float* v) {
     const float4* q = reinterpret_cast<const float4*>(p);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        float4 t = q[i];
-        v[4 * i + 0] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
-    }
+    const float4 a = q[0], b = q[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
-
 template <>
-__device__ __forceinline__ void load16<__hip_bfloat16>(const __hip_bfloat16* p, float* v) {
-    const uint4* q = reinterpret_cast<const uint4*>(p);
+__device__ __forceinline__ void load_chunk<float, 4>(const float* p, float* v) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+}
+// bf16 -> fp32 is exact: the bf16 bits become the high half of the fp32 bits
+template <>
+__device__ __forceinline__ void load_chunk<__hip_bfloat16, 8>(const __hip_bfloat16* p, float* v) {
+    const uint4 t = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {t.x, t.y, t.z, t.w};
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        uint4 t = q[i];
-        uint32_t w[4] = {t.x, t.y, t.z, t.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {       // bf16 -> fp32 is exact: shift into the high half
-            v[8 * i + 2 * j + 0] = __uint_as_float(w[j] << 16);
-            v[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
-        }
+    for (int j = 0; j < 4; ++j) {
+        v[2 * j + 0] = __uint_as_float(w[j] << 16);
+        v[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
     }
 }
+template <>
+__device__ __forceinline__ void load_chunk<__hip_bfloat16, 4>(const __hip_bfloat16* p, float* v) {
+    const uint2 t = *reinterpret_cast<const uint2*>(p);
+    v[0] = __uint_as_float(t.x << 16);
+    v[1] = __uint_as_float(t.x & 0xFFFF0000u);
+    v[2] = __uint_as_float(t.y << 16);
+    v[3] = __uint_as_float(t.y & 0xFFFF0000u);
+}
 
-// Quantize the NCH slices held in v[] (in place: v becomes the residue) into the
-// record at rec.  amax is the row maximum.
-template <int FMT, int NCH>
-__device__ __forceinline__ void quantize_slices(float (&v)[NCH][16], int nslices, int64_t K,
+// Quantize the NC chunks of EPT elements held in v[] (in place: v becomes the
+// residue) into the record at rec.  amax is the row maximum; nchunks = K / EPT.
+template <int FMT, int NC, int EPT>
+__device__ __forceinline__ void quantize_chunks(float (&v)[NC][EPT], int nchunks, int64_t K,
                                                 float amax, uint8_t* rec) {
+    constexpr int LPB = (FMT == kNV ? 16 : 32) / EPT;   // lanes sharing one block
     const int tid = threadIdx.x;
     uint8_t* codes = rec + kActHead;
     uint8_t* scales = codes + K / 2;
     const float s_g = (FMT == kNV) ? amax / 2688.0f : 0.0f;
     if (tid == 0) *reinterpret_cast<uint4*>(rec) = make_uint4(__float_as_uint(s_g), 0u, 0u, 0u);
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-        const int j = tid + kQThreads * c;          // slice index (16 elements)
-        const bool valid = j < nslices;
+    for (int c = 0; c < NC; ++c) {
+        const int j = tid + (int)blockDim.x * c;     // chunk index
         float bm = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) bm = fmaxf(bm, fabsf(v[c][e]));
+        for (int e = 0; e < EPT; ++e) bm = fmaxf(bm, fabsf(v[c][e]));
+        // the block's chunks sit in adjacent lanes of one wave (blockDim % 64 == 0)
+        if (LPB >= 2) bm = fmaxf(bm, dpp<kDppXor1>(bm));
+        if (LPB >= 4) bm = fmaxf(bm, dpp<kDppXor2>(bm));
+        if (LPB >= 8) bm = fmaxf(bm, dpp<kDppHalfMirror>(bm));
         float st;                                    // effective element scale
         uint32_t sbyte;
         if (FMT == kNV) {
-            const float t = bm / (6.0f * s_g);
-            sbyte = e4m3_encode(t);
+            sbyte = e4m3_encode(bm / (6.0f * s_g));
             st = e4m3_val(sbyte) * s_g;
         } else {
-            // the 32-block spans slices 2i, 2i+1 = lanes tid, tid^1 (same wave)
-            const float other = __shfl_xor(bm, 1, 64);
-            sbyte = e8m0_for_amax(fmaxf(bm, other));
+            sbyte = e8m0_for_amax(bm);
             st = e8m0_val(sbyte);
         }
-        uint32_t packed[2] = {0u, 0u};
+        uint32_t packed = 0u;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
+        for (int e = 0; e < EPT; ++e) {
             const float x = v[c][e];
             uint32_t mag = 0u;
             if (st != 0.0f) mag = e2m1_mag(fabsf(x / st));
             const uint32_t code = (__float_as_uint(x) >> 28 & 8u) | mag;
-            packed[e >> 3] |= code << (4 * (e & 7));
+            packed |= code << (4 * e);
             const float d = st * e2m1_val(code);
             v[c][e] = x - d;                          // residue, exact (Sterbenz)
         }
-        if (valid) {
-            *reinterpret_cast<uint2*>(codes + 8 * (int64_t)j) = make_uint2(packed[0], packed[1]);
-            if (FMT == kNV) {
-                scales[j] = (uint8_t)sbyte;
-            } else if ((j & 1) == 0) {
-                scales[j >> 1] = (uint8_t)sbyte;
-            }
+        if (j < nchunks) {
+            if (EPT == 8)
+                *reinterpret_cast<uint32_t*>(codes + 4 * (int64_t)j) = packed;
+            else
+                *reinterpret_cast<uint16_t*>(codes + 2 * (int64_t)j) = (uint16_t)packed;
+            if ((j & (LPB - 1)) == 0) scales[j / LPB] = (uint8_t)sbyte;
         }
     }
 }
 
-template <int FMT, int NCH, typename TIn>
-__global__ __launch_bounds__(kQThreads) void quant_act_kernel(const TIn* __restrict__ x, int M,
-                                                              int64_t K, int with_res,
-                                                              uint8_t* __restrict__ act,
-                                                              int64_t row_bytes) {
-    __shared__ float red[kQThreads / 64];
+template <int FMT, int NC, int EPT, typename TIn>
+__global__ __launch_bounds__(kQMaxThreads) void quant_act_kernel(const TIn* __restrict__ x, int M,
+                                                                 int64_t K, int with_res,
+                                                                 uint8_t* __restrict__ act,
+                                                                 int64_t row_bytes) {
+    __shared__ float red[kQMaxThreads / 64];
     const int m = blockIdx.x;
     const int tid = threadIdx.x;
-    const int nslices = (int)(K / 16);
+    const int nchunks = (int)(K / EPT);
     const TIn* xr = x + (int64_t)m * K;
 
-    float v[NCH][16];
+    float v[NC][EPT];
     float tmax = 0.0f;
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-        const int j = tid + kQThreads * c;
-        if (j < nslices) {
-            load16<TIn>(xr + 16 * (int64_t)j, v[c]);
+    for (int c = 0; c < NC; ++c) {
+        const int j = tid + (int)blockDim.x * c;
+        if (j < nchunks) {
+            load_chunk<TIn, EPT>(xr + EPT * (int64_t)j, v[c]);
         } else {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) v[c][e] = 0.0f;
+            for (int e = 0; e < EPT; ++e) v[c][e] = 0.0f;
         }
 #pragma unroll
-        for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, fabsf(v[c][e]));
+        for (int e = 0; e < EPT; ++e) tmax = fmaxf(tmax, fabsf(v[c][e]));
     }
     const float amax = block_max(tmax, red);
-    quantize_slices<FMT, NCH>(v, nslices, K, amax, act + (int64_t)m * row_bytes);
+    quantize_chunks<FMT, NC, EPT>(v, nchunks, K, amax, act + (int64_t)m * row_bytes);
     if (!with_res) return;
 
-    // v now holds the residue (zero in invalid slices): second row statistic.
+    // v now holds the residue (zero in chunks past K): second row statistic.
     float rmax = 0.0f;
 #pragma unroll
-    for (int c = 0; c < NCH; ++c)
+    for (int c = 0; c < NC; ++c)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) rmax = fmaxf(rmax, fabsf(v[c][e]));
+        for (int e = 0; e < EPT; ++e) rmax = fmaxf(rmax, fabsf(v[c][e]));
     const float ramax = block_max(rmax, red);
-    quantize_slices<FMT, NCH>(v, nslices, K, ramax, act + (int64_t)(M + m) * row_bytes);
+    quantize_chunks<FMT, NC, EPT>(v, nchunks, K, ramax, act + (int64_t)(M + m) * row_bytes);
 }
 
-template <int FMT, int NCH, typename TIn>
-hipError_t launch_quant_t(const void* x, int M, int64_t K, int with_res, void* act, hipStream_t s) {
+template <int FMT, int NC, int EPT, typename TIn>
+hipError_t launch_quant_t(const void* x, int M, int64_t K, int with_res, void* act, int threads,
+                          hipStream_t s) {
     const int64_t rb = act_row_bytes(FMT, K);
-    hipLaunchKernelGGL((quant_act_kernel<FMT, NCH, TIn>), dim3(M), dim3(kQThreads), 0, s,
+    hipLaunchKernelGGL((quant_act_kernel<FMT, NC, EPT, TIn>), dim3(M), dim3(threads), 0, s,
                        static_cast<const TIn*>(x), M, K, with_res, static_cast<uint8_t*>(act), rb);
     return hipGetLastError();
 }
 
+// Up to 1024 threads per row (whole waves): four elements per thread while
+// that covers the row (K <= 4096), else eight, with NC chunks per thread for
+// rows longer than 8192.
 template <int FMT, typename TIn>
 hipError_t launch_quant_f(const void* x, int M, int64_t K, int with_res, void* act, hipStream_t s) {
-    const int64_t nsl = K / 16;
-    if (nsl <= 1 * kQThreads) return launch_quant_t<FMT, 1, TIn>(x, M, K, with_res, act, s);
-    if (nsl <= 2 * kQThreads) return launch_quant_t<FMT, 2, TIn>(x, M, K, with_res, act, s);
-    if (nsl <= 4 * kQThreads) return launch_quant_t<FMT, 4, TIn>(x, M, K, with_res, act, s);
-    return launch_quant_t<FMT, 8, TIn>(x, M, K, with_res, act, s);
+    if (K <= 4 * kQMaxThreads) {
+        const int threads = (int)((K / 4 + 63) / 64 * 64);
+        return launch_quant_t<FMT, 1, 4, TIn>(x, M, K, with_res, act, threads, s);
+    }
+    const int64_t nch = K / 8;
+    if (nch <= kQMaxThreads) {
+        const int threads = (int)((nch + 63) / 64 * 64);
+        return launch_quant_t<FMT, 1, 8, TIn>(x, M, K, with_res, act, threads, s);
+    }
+    if (nch <= 2 * kQMaxThreads) return launch_quant_t<FMT, 2, 8, TIn>(x, M, K, with_res, act, kQMaxThreads, s);
+    return launch_quant_t<FMT, 4, 8, TIn>(x, M, K, with_res, act, kQMaxThreads, s);
 }
 
 }  // namespace
