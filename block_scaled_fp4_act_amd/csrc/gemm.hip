@@ -14,13 +14,15 @@
 //
 // Work decomposition (one design for all M <= 16, i.e. B <= 32):
 //   * a workgroup owns groups of 16 output channels (grid-stride over groups)
-//     and has KW waves that split K: wave w owns a contiguous run of <= MAXS
-//     128-element steps;
-//   * a wave loads its activation fragments for its steps ONCE (they stay in
-//     VGPRs across all groups), then streams the packed weights: per step one
-//     16-byte load per lane = 1 KB per wave, fully coalesced, plus the step's
-//     scales; the next group's weights are prefetched while the current group
-//     computes, so every weight byte is read from HBM once;
+//     and KW waves that split K: wave w owns steps [w*MAXS, w*MAXS + MAXS) of
+//     128 elements (MAXS a power of two, so a wave's steps sit inside one
+//     4-step quad of the weight layout, or fill whole quads);
+//   * a wave loads its activation fragments ONCE (they stay in VGPRs across
+//     all groups; NVFP4 dequantizes them to f16 once where registers allow),
+//     then streams the packed weights: per step one 16-byte load per lane =
+//     1 KB per wave, fully coalesced, and per group one load for the block
+//     scales of all its steps.  The loads of the next PD groups are in flight
+//     while a group is computed (register ring);
 //   * NVFP4: each 8-element run is dequantized in registers to f16 with its
 //     E4M3 block scale (e * S_b has <= 6 significant bits and lies in
 //     [2^-10, 2688], so f16 holds it exactly) and fed to
@@ -29,10 +31,15 @@
 //   * MXFP4: codes and E8M0 scales go straight into the native block-scaled
 //     v_mfma_scale_f32_16x16x128_f8f6f4 (FP4 x FP4, one scale per lane = per
 //     32-element block), no dequantization at all;
-//   * the KW partial accumulators of a group meet in LDS and are summed in a
-//     fixed order (deterministic), then folded and stored as fp32.
+//   * the KW partial accumulators of a group meet in LDS; the last wave to
+//     deposit its partial (an LDS counter per group) sums the KW partials in a
+//     fixed order (deterministic), folds and stores, so no barrier is needed
+//     while groups are streamed.  When a workgroup owns more groups than LDS
+//     slots, the slots are recycled after a workgroup barrier.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <cstdlib>
 
 #include "codec.h"
 #include "kernels.h"
@@ -46,23 +53,21 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef int intx8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kMaxWaves = 16;
 constexpr int kRedBytesMax = 128 * 1024;   // LDS for partial sums per workgroup
 constexpr int kLdsPerCu = 160 * 1024;      // gfx950
+constexpr int kRsrcWord3 = 0x00020000;     // raw buffer, 32-bit dwords, range checked
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit dwords, range checked
-
-// NVFP4 block-scale pair -> two f16 holding S_b * 2^-8 each.  E4M3 (bias 7) and
-// f16 (bias 15) line up field by field: the E4M3 exponent and mantissa bits
-// moved to f16's exponent and top mantissa bits give the same value times 2^-8,
+// NVFP4 block-scale byte -> f16 holding S_b * 2^-8.  E4M3 (bias 7) and f16
+// (bias 15) line up field by field: the E4M3 exponent and mantissa bits moved to
+// f16's exponent and top mantissa bits give the same value times 2^-8,
 // subnormals included.  The 2^8 comes back through the conversion's power-of-
 // two scale below, so e * S_b is formed exactly.
-__device__ __forceinline__ half2v scale_pair_h(uint32_t two_bytes) {
-    const uint32_t bits = ((two_bytes & 0x7Fu) << 7) | ((two_bytes & 0x7F00u) << 15);
-    return __builtin_bit_cast(half2v, bits);
+__device__ __forceinline__ _Float16 scale_h(uint32_t byte) {
+    return __builtin_bit_cast(_Float16, (unsigned short)((byte & 0x7Fu) << 7));
 }
 
 // Eight E2M1 codes (one dword, element 2j in the low nibble of byte j) times the
@@ -93,6 +98,43 @@ __device__ __forceinline__ uint4 ld128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// Scale bytes of a wave's MAXS steps, per lane: NVFP4 2 bytes per step, MXFP4
+// 1.  Up to four steps sit in one quad entry and come with one load; eight
+// steps span two quads and take two.
+template <int FMT, int MAXS>
+struct ScaleWord {
+    static constexpr int kBytesPerQuad = (MAXS < 4 ? MAXS : 4) * (FMT == kNV ? 2 : 1);
+    static constexpr int kQuads = MAXS > 4 ? 2 : 1;
+    static constexpr int kWordsPerQuad = kBytesPerQuad > 4 ? 2 : 1;
+    uint32_t w[kQuads * kWordsPerQuad];
+    // the scale byte of step t, block h (NVFP4 h = 0/1; MXFP4 h = 0)
+    __device__ __forceinline__ uint32_t byte(int t, int h) const {
+        const int q = t >> 2, tq = t & 3;
+        const int bit = FMT == kNV ? 16 * tq + 8 * h : 8 * tq;
+        return (w[q * kWordsPerQuad + (bit >> 5)] >> (bit & 31)) & 0xFFu;
+    }
+};
+
+template <int FMT, int MAXS>
+__device__ __forceinline__ void load_scales(__amdgpu_buffer_rsrc_t r, const uint32_t* off,
+                                            ScaleWord<FMT, MAXS>& s) {
+    using SW = ScaleWord<FMT, MAXS>;
+#pragma unroll
+    for (int q = 0; q < SW::kQuads; ++q) {
+        if (SW::kBytesPerQuad == 1) {
+            s.w[q] = __builtin_amdgcn_raw_buffer_load_b8(r, off[q], 0, 0);
+        } else if (SW::kBytesPerQuad == 2) {
+            s.w[q] = __builtin_amdgcn_raw_buffer_load_b16(r, off[q], 0, 0);
+        } else if (SW::kBytesPerQuad == 4) {
+            s.w[q] = __builtin_amdgcn_raw_buffer_load_b32(r, off[q], 0, 0);
+        } else {
+            const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off[q], 0, 0);
+            s.w[2 * q] = v[0];
+            s.w[2 * q + 1] = v[1];
+        }
+    }
+}
+
 struct GemmArgs {
     const uint8_t* act;
     int64_t row_bytes;
@@ -101,7 +143,7 @@ struct GemmArgs {
     int64_t N;
     int64_t K;
     float* y;
-    int ngl;          // groups whose partial sums are held in LDS between reductions
+    int ngl;          // LDS slots for partial sums (groups in flight per workgroup)
 };
 
 // APRE: the activation fragments are dequantized to f16 once, before the
@@ -110,57 +152,65 @@ struct GemmArgs {
 // are dequantized at each use.
 // PD: weight prefetch depth.  The loads of group j + PD are issued before group
 // j is computed, through a ring of PD + 1 register buffers (the loop is
-// unrolled by PD + 1 so every buffer index is static); PD = 0 loads each group
-// just before its use.
-template <int FMT, int MAXS, int RT, bool COMP, int PD, bool APRE>
+// unrolled by PD + 1 so every buffer index is static).
+// RM: how the KW partial sums of a group are combined.  RM = 0: the last wave
+// to deposit its partial (LDS counter) reduces the group at once.  RM = 1: the
+// partials of up to ngl groups wait in LDS and the waves reduce them together
+// after one barrier (one group per wave).
+template <int FMT, int MAXS, int RT, bool COMP, int PD, bool APRE, int RM>
 __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmArgs p) {
-    extern __shared__ float red[];           // [ngl][KW][RT][4][64] partial sums
+    // LDS: [ngl] counters (padded to 64), then [ngl][KW][RT][4][64] partial sums
+    extern __shared__ float lds[];
     constexpr bool kPre = APRE && FMT == kNV;
     constexpr int kAC = kPre ? 1 : MAXS;     // code registers kept per row tile
     constexpr int kAH = kPre ? MAXS : 1;     // f16 fragments kept per row tile
     constexpr int NB = PD + 1;               // weight buffers in the ring
+    using SW = ScaleWord<FMT, MAXS>;
+    constexpr int64_t SB1 = scale_bytes_per_step_lane(FMT);
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int KW = blockDim.x >> 6;
     const int g = lane >> 4, i = lane & 15;
     const int64_t S = num_steps(p.K);
-    const int s0 = (int)((wave * S) / KW);
-    const int s1 = (int)(((wave + 1) * S) / KW);
-    const int ns = s1 - s0;                       // <= MAXS by the host's choice
+    const int s0 = wave * MAXS;                   // this wave's first step
     const int64_t G = num_groups(p.N);
     const int64_t GB = group_bytes(FMT, p.K);
-    constexpr uint32_t SB = (uint32_t)step_bytes(FMT);
     const uint32_t scale_base = (uint32_t)(kActHead + p.K / 2);
     const int64_t grid = gridDim.x;
     const int64_t c0 = blockIdx.x;
+    const int ngl = p.ngl;
+    int* counters = reinterpret_cast<int*>(lds);
+    float* red = lds + ((ngl + 63) & ~63);
 
     float s_gw = 1.0f;
     if (FMT == kNV) s_gw = reinterpret_cast<const WHeader*>(p.blob)->s_g;
 
+    // Offsets of this wave's loads inside a group: steps past the padded end
+    // of the group land past its last byte, i.e. out of range (zeros).
+    const uint32_t code_base = (uint32_t)step_code_offset(FMT, s0) + 16u * lane;
+    uint32_t sc_off[SW::kQuads];
+#pragma unroll
+    for (int q = 0; q < SW::kQuads; ++q)
+        sc_off[q] = (uint32_t)(quad_scale_offset(FMT, s0 + 4 * q) + lane * 4 * SB1 + (s0 % 4) * SB1);
+
     uint4 wb[NB][MAXS];
-    uint32_t wsc[NB][MAXS];
+    SW wsc[NB];
 
     // One buffer resource per group (32-bit lane offsets, no 4 GB limit
-    // overall).  Every load is issued unconditionally: a step past this wave's
-    // range, or a group past the end (zero-sized resource), reads out of range
-    // and the buffer unit returns zeros.  Without branches around the loads the
+    // overall).  Every load is issued unconditionally: a step past the end, or a
+    // group past the end (zero-sized resource), reads out of range and the
+    // buffer unit returns zeros.  Without branches around the loads the
     // compiler's memory-counter waits stay exact, so prefetched groups are
     // really in flight while earlier ones are computed.
-    auto load_w = [&](int64_t c, uint4 (&codes)[MAXS], uint32_t (&sc)[MAXS]) {
+    auto load_w = [&](int64_t c, uint4 (&codes)[MAXS], SW& sc) {
         const bool live = c < G;
         const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(p.blob + kWHeader + (live ? c : 0) * GB), (short)0, live ? (int)GB : 0, kRsrcWord3);
 #pragma unroll
-        for (int t = 0; t < MAXS; ++t) {
-            const bool in = t < ns;
-            const uint32_t st = (uint32_t)(s0 + t) * SB;
-            codes[t] = ld128(r, in ? st + 16u * lane : (uint32_t)GB);
-            if (FMT == kNV)
-                sc[t] = __builtin_amdgcn_raw_buffer_load_b16(r, in ? st + (uint32_t)kStepCodes + 2u * lane : (uint32_t)GB, 0, 0);
-            else
-                sc[t] = __builtin_amdgcn_raw_buffer_load_b8(r, in ? st + (uint32_t)kStepCodes + lane : (uint32_t)GB, 0, 0);
-        }
+        for (int t = 0; t < MAXS; ++t)
+            codes[t] = ld128(r, code_base + (uint32_t)((t / 4) * quad_bytes(FMT) + (t % 4) * kStepCodes));
+        load_scales<FMT, MAXS>(r, sc_off, sc);
     };
 
     // ---- activation fragments: loaded once, kept in registers ----
@@ -189,7 +239,7 @@ __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmArgs p) {
 #pragma unroll
         for (int t = 0; t < MAXS; ++t) {
             const int64_t k0 = kStepK * (s0 + t) + 32 * g;
-            const bool in = t < ns && rvalid && k0 < p.K;   // else: out of range -> zeros
+            const bool in = rvalid && k0 < p.K;   // else: out of range -> zeros
             const uint32_t rec = in ? (uint32_t)(arow * p.row_bytes) : act_bytes;
             a_raw[rt][t] = ld128(ra, in ? rec + (uint32_t)(kActHead + k0 / 2) : act_bytes);
             if (FMT == kNV)
@@ -199,13 +249,10 @@ __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmArgs p) {
         }
     }
 
-    if (PD == 0) {
-        load_w(c0, wb[0], wsc[0]);
-    } else {
 #pragma unroll
-        for (int q = 0; q < PD; ++q) load_w(c0 + q * grid, wb[q], wsc[q]);
-    }
+    for (int q = 0; q < PD; ++q) load_w(c0 + q * grid, wb[q], wsc[q]);
 
+    for (int k = threadIdx.x; k < ngl; k += blockDim.x) counters[k] = 0;
 
     uint4 a_codes[RT][kAC];
     uint32_t a_sc[RT][kAC];
@@ -215,82 +262,30 @@ __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmArgs p) {
 #pragma unroll
         for (int t = 0; t < MAXS; ++t) {
             if (kPre) {
-                const half2v h = scale_pair_h(a_rsc[rt][t]);
 #pragma unroll
-                for (int u = 0; u < 4; ++u) a_h[rt][t][u] = dequant8(get(a_raw[rt][t], u), u < 2 ? h[0] : h[1]);
+                for (int u = 0; u < 4; ++u)
+                    a_h[rt][t][u] = dequant8(get(a_raw[rt][t], u), scale_h((a_rsc[rt][t] >> (u < 2 ? 0 : 8)) & 0xFFu));
             } else {
                 a_codes[rt][t] = a_raw[rt][t];
                 a_sc[rt][t] = a_rsc[rt][t];
             }
         }
     }
+    __syncthreads();                              // counters are zero
 
-    // ---- one group: MFMAs over this wave's steps; partial sums to LDS slot ----
-    auto compute = [&](int slot, const uint4 (&w_codes)[MAXS], const uint32_t (&w_sc)[MAXS]) {
-        floatx4 acc[RT];
+    // ---- fold and store the group reduced from LDS slot `slot` (one wave) ----
+    auto reduce_slot = [&](int64_t c, int slot) {
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) acc[rt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-
-#pragma unroll
-        for (int t = 0; t < MAXS; ++t) {
-            if (t < ns) {
-                if (FMT == kNV) {
-                    const half2v sw = scale_pair_h(w_sc[t]);
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const half8 b = dequant8(get(w_codes[t], u), u < 2 ? sw[0] : sw[1]);
-#pragma unroll
-                        for (int rt = 0; rt < RT; ++rt) {
-                            half8 a;
-                            if (kPre) {
-                                a = a_h[rt][t][u];
-                            } else {
-                                const half2v sa = scale_pair_h(a_sc[rt][t]);
-                                a = dequant8(get(a_codes[rt][t], u), u < 2 ? sa[0] : sa[1]);
-                            }
-                            acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[rt], 0, 0, 0);
-                        }
-                    }
-                } else {
-                    const uint4 wc = w_codes[t];
-                    const intx8 b = {(int)wc.x, (int)wc.y, (int)wc.z, (int)wc.w, 0, 0, 0, 0};
-#pragma unroll
-                    for (int rt = 0; rt < RT; ++rt) {
-                        const uint4 ac = a_codes[rt][t];
-                        const intx8 a = {(int)ac.x, (int)ac.y, (int)ac.z, (int)ac.w, 0, 0, 0, 0};
-                        acc[rt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                            a, b, acc[rt], 4, 4, 0, (int)a_sc[rt][t], 0, (int)w_sc[t]);
-                    }
-                }
-            }
-        }
-        float* dst = red + ((slot * KW + wave) * RT) * 256;
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) dst[(rt * 4 + r) * 64 + lane] = acc[rt][r];
-    };
-
-    // ---- reduce the slots [0, nslots) of groups c_first, c_first + grid, ...:
-    // sum the KW partials in a fixed order (deterministic), Fold, store ----
-    auto flush = [&](int64_t c_first, int nslots) {
-        __syncthreads();
-        const int items = nslots * RT * 128;
-        for (int idx = threadIdx.x; idx < items; idx += blockDim.x) {
-            const int slot = idx / (RT * 128);
-            const int rem = idx - slot * (RT * 128);
-            const int rt = rem >> 7;
-            const int pr = (rem >> 6) & 1;
-            const int ln = rem & 63;
-            const float* src = red + (slot * KW * RT + rt) * 256 + (2 * pr) * 64 + ln;
+        for (int item = 0; item < 2 * RT; ++item) {   // (row tile, pair) per lane
+            const int rt = item >> 1, pr = item & 1;
+            const float* src = red + (slot * KW * RT + rt) * 256 + (2 * pr) * 64 + lane;
             float v0 = 0.0f, v1 = 0.0f;
             for (int w = 0; w < KW; ++w) {
                 v0 += src[w * RT * 256];
                 v1 += src[w * RT * 256 + 64];
             }
-            const int og = ln >> 4, oi = ln & 15;
-            const int ti0 = 16 * rt + 4 * og + 2 * pr;   // tile rows ti0, ti0 + 1
-            const int64_t n = (c_first + slot * grid) * kGroupN + oi;
+            const int ti0 = 16 * rt + 4 * g + 2 * pr;    // tile rows ti0, ti0 + 1
+            const int64_t n = c * kGroupN + i;
             if (n < p.N) {
                 if (COMP) {
                     const int m = ti0 >> 1;
@@ -320,97 +315,192 @@ __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmArgs p) {
                 }
             }
         }
-        __syncthreads();
+    };
+
+    // ---- one group: MFMAs over this wave's steps, partial to LDS, and the
+    // last wave to arrive reduces the group ----
+    auto compute = [&](int64_t c, int slot, const uint4 (&w_codes)[MAXS], const SW& w_sc) {
+        floatx4 acc[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) acc[rt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+
+#pragma unroll
+        for (int t = 0; t < MAXS; ++t) {
+            if (FMT == kNV) {
+                const _Float16 sw0 = scale_h(w_sc.byte(t, 0)), sw1 = scale_h(w_sc.byte(t, 1));
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const half8 b = dequant8(get(w_codes[t], u), u < 2 ? sw0 : sw1);
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt) {
+                        half8 a;
+                        if (kPre) {
+                            a = a_h[rt][t][u];
+                        } else {
+                            // the empty asm keeps the compiler from hoisting this
+                            // loop-invariant dequantization out of the group loop,
+                            // which would hold every f16 fragment in registers
+                            uint32_t ac = get(a_codes[rt][t], u), as = a_sc[rt][t];
+                            asm volatile("" : "+v"(ac), "+v"(as));
+                            a = dequant8(ac, scale_h((as >> (u < 2 ? 0 : 8)) & 0xFFu));
+                        }
+                        acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[rt], 0, 0, 0);
+                    }
+                }
+            } else {
+                const uint4 wc = w_codes[t];
+                const intx8 b = {(int)wc.x, (int)wc.y, (int)wc.z, (int)wc.w, 0, 0, 0, 0};
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
+                    const uint4 ac = a_codes[rt][t];
+                    const intx8 a = {(int)ac.x, (int)ac.y, (int)ac.z, (int)ac.w, 0, 0, 0, 0};
+                    acc[rt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        a, b, acc[rt], 4, 4, 0, (int)a_sc[rt][t], 0, (int)w_sc.byte(t, 0));
+                }
+            }
+        }
+        float* dst = red + ((slot * KW + wave) * RT) * 256;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dst[(rt * 4 + r) * 64 + lane] = acc[rt][r];
+        if (RM == 0) {
+            // publish this wave's partial, then count it in
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+            int old = 0;
+            if (lane == 0) old = atomicAdd(&counters[slot], 1);
+            old = __builtin_amdgcn_readfirstlane(old);
+            if (old == KW - 1) {                  // the last partial of this group
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+                reduce_slot(c, slot);
+            }
+        }
     };
 
     // groups of this workgroup: c0, c0 + grid, ...; the loop runs a whole number
-    // of ring turns and skips the work (never the loads) past the end.  Partial
-    // sums of up to ngl groups wait in LDS and are reduced together, so the
-    // waves meet at a barrier once per ngl groups, not per group.
+    // of ring turns and skips the work (never the loads) past the end.  Group j
+    // uses LDS slot j % ngl; before the slots wrap (RM = 0), or when they are
+    // full or the groups end (RM = 1), a barrier separates the partial sums of
+    // the groups so far from the reuse of their slots.
     const int64_t nj = c0 < G ? (G - c0 + grid - 1) / grid : 0;
-    const int ngl = p.ngl;
     int slot = 0;
-    if (PD == 0) {
-        for (int64_t j = 0; j < nj; ++j) {
-            if (j > 0) load_w(c0 + j * grid, wb[0], wsc[0]);
-            compute(slot, wb[0], wsc[0]);
-            if (++slot == ngl || j == nj - 1) {
-                flush(c0 + (j - slot + 1) * grid, slot);
-                slot = 0;
-            }
-        }
-    } else {
-        for (int64_t j0 = 0; j0 < nj; j0 += NB) {
+    auto flush = [&](int64_t jlast, int nslots) {   // RM = 1
+        __syncthreads();
+        for (int sl = wave; sl < nslots; sl += KW) reduce_slot(c0 + (jlast - nslots + 1 + sl) * grid, sl);
+        __syncthreads();
+    };
+    for (int64_t j0 = 0; j0 < nj; j0 += NB) {
 #pragma unroll
-            for (int q = 0; q < NB; ++q) {
-                const int64_t j = j0 + q;
-                load_w(c0 + (j + PD) * grid, wb[(q + PD) % NB], wsc[(q + PD) % NB]);
-                if (j < nj) {
-                    compute(slot, wb[q], wsc[q]);
-                    if (++slot == ngl || j == nj - 1) {
-                        flush(c0 + (j - slot + 1) * grid, slot);
-                        slot = 0;
-                    }
+        for (int q = 0; q < NB; ++q) {
+            const int64_t j = j0 + q;
+            load_w(c0 + (j + PD) * grid, wb[(q + PD) % NB], wsc[(q + PD) % NB]);
+            if (j < nj) {
+                if (RM == 0 && slot == ngl) {     // wrap: every slot reduced -> reset
+                    __syncthreads();
+                    for (int k = threadIdx.x; k < ngl; k += blockDim.x) counters[k] = 0;
+                    __syncthreads();
+                    slot = 0;
+                }
+                compute(c0 + j * grid, slot, wb[q], wsc[q]);
+                ++slot;
+                if (RM == 1 && (slot == ngl || j == nj - 1)) {
+                    flush(j, slot);
+                    slot = 0;
                 }
             }
         }
     }
 }
 
-template <int FMT, int MAXS, int RT, bool COMP, int PD, bool APRE>
+template <int FMT, int MAXS, int RT, bool COMP, int PD, bool APRE, int RM>
 hipError_t launch_t(const GemmArgs& a, int KW, int64_t grid, hipStream_t s) {
-    // allow the full LDS of a CU for the partial-sum slots (set once per kernel)
+    // allow the LDS of a CU for the partial-sum slots (set once per kernel)
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&gemm_small_kernel<FMT, MAXS, RT, COMP, PD, APRE>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, kRedBytesMax);
+        reinterpret_cast<const void*>(&gemm_small_kernel<FMT, MAXS, RT, COMP, PD, APRE, RM>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, kRedBytesMax + 1024);
     if (attr != hipSuccess) return attr;
-    const size_t lds = (size_t)a.ngl * KW * RT * 1024;
-    hipLaunchKernelGGL((gemm_small_kernel<FMT, MAXS, RT, COMP, PD, APRE>), dim3((unsigned)grid),
+    const size_t lds = (size_t)((a.ngl + 63) & ~63) * 4 + (size_t)a.ngl * KW * RT * 1024;
+    hipLaunchKernelGGL((gemm_small_kernel<FMT, MAXS, RT, COMP, PD, APRE, RM>), dim3((unsigned)grid),
                        dim3(64 * KW), lds, s, a);
     return hipGetLastError();
 }
 
-// Register budget (128 VGPRs at 16 waves per CU) decides the variant: each
-// prefetch level costs one more set of weight registers (5 per step), the f16
-// activation fragments 16 per step and row tile (NVFP4), the code fragments 5.
-// The table below was chosen from the compiler's register counts so that no
-// variant with one row tile spills; with two row tiles (B > 16) and 6-8 steps
-// per wave a few registers spill.
-constexpr int pd_for(int fmt, int rt, int maxs) {
-    if (fmt == kNV && rt == 1) return maxs <= 2 ? 3 : (maxs <= 4 ? 2 : (maxs == 5 ? 1 : 0));
-    if (fmt == kNV) return maxs == 1 ? 3 : (maxs == 2 ? 2 : (maxs <= 4 ? 1 : 0));
-    if (rt == 1) return maxs <= 4 ? 3 : (maxs == 5 ? 2 : (maxs == 6 ? 1 : 0));
-    return maxs <= 3 ? (maxs == 2 ? 2 : 3) : (maxs == 4 ? 1 : 0);
+// Variant table, from a sweep of prefetch depth, pre-dequantized activations
+// and reduction mode on the decode workloads (and the compiler's register
+// counts: 128 VGPRs at 16 waves per CU).  Deep prefetch does not pay: one group
+// ahead is best when a workgroup streams several groups.  A workgroup with a
+// single group reduces it as soon as its last partial lands (RM = 0); with
+// several groups the deferred reduction (RM = 1) is faster.
+constexpr int pd_for(int fmt, int rt, int maxs, bool single) {
+    if (single) return 0;
+    if (fmt == kNV) return maxs <= 4 ? 1 : 0;
+    return rt == 1 ? (maxs <= 4 ? 1 : 0) : (maxs <= 2 ? 1 : 0);
 }
-constexpr bool apre_for(int fmt, int rt, int maxs) { return fmt == kNV && rt == 1 && maxs <= 3; }
+constexpr bool apre_for(int fmt, int rt, int maxs, bool single) {
+    return fmt == kNV && rt == 1 && maxs <= (single ? 4 : 2);
+}
+constexpr int rm_for(int fmt, int rt, int maxs, bool single) { return single ? 0 : 1; }
+
+#ifdef RSFP4_TUNE
+// Tuning builds only: RSFP4_TUNE_PD / _APRE / _RM override the table for one
+// row tile of compensated calls, to measure the alternatives.
+inline int tune_env(const char* n, int dflt) {
+    const char* e = std::getenv(n);
+    return e ? std::atoi(e) : dflt;
+}
+template <int FMT, bool COMP, int MAXS, int PD, bool APRE>
+hipError_t launch_rm(const GemmArgs& a, int KW, int64_t grid, hipStream_t s, int rm) {
+    return rm == 0 ? launch_t<FMT, MAXS, 1, COMP, PD, APRE, 0>(a, KW, grid, s)
+                   : launch_t<FMT, MAXS, 1, COMP, PD, APRE, 1>(a, KW, grid, s);
+}
+template <int FMT, bool COMP, int MAXS>
+hipError_t launch_tune(const GemmArgs& a, int KW, int64_t grid, hipStream_t s) {
+    const int pd = tune_env("RSFP4_TUNE_PD", pd_for(FMT, 1, MAXS, false));
+    const bool apre = tune_env("RSFP4_TUNE_APRE", apre_for(FMT, 1, MAXS, false)) != 0;
+    const int rm = tune_env("RSFP4_TUNE_RM", rm_for(FMT, 1, MAXS, false));
+    switch (pd * 2 + (apre ? 1 : 0)) {
+        case 0: return launch_rm<FMT, COMP, MAXS, 0, false>(a, KW, grid, s, rm);
+        case 1: return launch_rm<FMT, COMP, MAXS, 0, true>(a, KW, grid, s, rm);
+        case 2: return launch_rm<FMT, COMP, MAXS, 1, false>(a, KW, grid, s, rm);
+        case 3: return launch_rm<FMT, COMP, MAXS, 1, true>(a, KW, grid, s, rm);
+        case 4: return launch_rm<FMT, COMP, MAXS, 2, false>(a, KW, grid, s, rm);
+        case 5: return launch_rm<FMT, COMP, MAXS, 2, true>(a, KW, grid, s, rm);
+        case 6: return launch_rm<FMT, COMP, MAXS, 3, false>(a, KW, grid, s, rm);
+        default: return launch_rm<FMT, COMP, MAXS, 3, true>(a, KW, grid, s, rm);
+    }
+}
+#endif
 
 template <int FMT, int RT, bool COMP, int MAXS>
-hipError_t launch_v(const GemmArgs& a, int KW, int64_t grid, hipStream_t s) {
-    return launch_t<FMT, MAXS, RT, COMP, pd_for(FMT, RT, MAXS), apre_for(FMT, RT, MAXS)>(a, KW, grid, s);
+hipError_t launch_v(const GemmArgs& a, int KW, int64_t grid, hipStream_t s, bool single) {
+#ifdef RSFP4_TUNE
+    if (RT == 1 && COMP) return launch_tune<FMT, COMP, MAXS>(a, KW, grid, s);
+#endif
+    if (single)
+        return launch_t<FMT, MAXS, RT, COMP, pd_for(FMT, RT, MAXS, true), apre_for(FMT, RT, MAXS, true),
+                        rm_for(FMT, RT, MAXS, true)>(a, KW, grid, s);
+    return launch_t<FMT, MAXS, RT, COMP, pd_for(FMT, RT, MAXS, false), apre_for(FMT, RT, MAXS, false),
+                    rm_for(FMT, RT, MAXS, false)>(a, KW, grid, s);
 }
 
 template <int FMT, int RT, bool COMP>
-hipError_t launch_maxs(const GemmArgs& a, int maxs, int KW, int64_t grid, hipStream_t s) {
+hipError_t launch_maxs(const GemmArgs& a, int maxs, int KW, int64_t grid, hipStream_t s, bool single) {
     switch (maxs) {
-        case 1: return launch_v<FMT, RT, COMP, 1>(a, KW, grid, s);
-        case 2: return launch_v<FMT, RT, COMP, 2>(a, KW, grid, s);
-        case 3: return launch_v<FMT, RT, COMP, 3>(a, KW, grid, s);
-        case 4: return launch_v<FMT, RT, COMP, 4>(a, KW, grid, s);
-        case 5: return launch_v<FMT, RT, COMP, 5>(a, KW, grid, s);
-        case 6: return launch_v<FMT, RT, COMP, 6>(a, KW, grid, s);
-        case 7: return launch_v<FMT, RT, COMP, 7>(a, KW, grid, s);
-        default: return launch_v<FMT, RT, COMP, 8>(a, KW, grid, s);
+        case 1: return launch_v<FMT, RT, COMP, 1>(a, KW, grid, s, single);
+        case 2: return launch_v<FMT, RT, COMP, 2>(a, KW, grid, s, single);
+        case 4: return launch_v<FMT, RT, COMP, 4>(a, KW, grid, s, single);
+        default: return launch_v<FMT, RT, COMP, 8>(a, KW, grid, s, single);
     }
 }
 
 template <int FMT>
 hipError_t launch_fmt(const GemmArgs& a, int rt, bool comp, int maxs, int KW, int64_t grid,
-                      hipStream_t s) {
+                      hipStream_t s, bool single) {
     if (rt == 1)
-        return comp ? launch_maxs<FMT, 1, true>(a, maxs, KW, grid, s)
-                    : launch_maxs<FMT, 1, false>(a, maxs, KW, grid, s);
-    return comp ? launch_maxs<FMT, 2, true>(a, maxs, KW, grid, s)
-                : launch_maxs<FMT, 2, false>(a, maxs, KW, grid, s);
+        return comp ? launch_maxs<FMT, 1, true>(a, maxs, KW, grid, s, single)
+                    : launch_maxs<FMT, 1, false>(a, maxs, KW, grid, s, single);
+    return comp ? launch_maxs<FMT, 2, true>(a, maxs, KW, grid, s, single)
+                : launch_maxs<FMT, 2, false>(a, maxs, KW, grid, s, single);
 }
 
 }  // namespace
@@ -420,8 +510,8 @@ GemmPlan plan_gemm_small(int64_t M, int64_t N, int64_t K, bool comp, int num_cus
     const int64_t S = num_steps(K);
     const int64_t B = comp ? 2 * M : M;
     pl.rt = B <= 16 ? 1 : 2;
-    // as many waves along K as allowed (16), then the fewest steps per wave
-    pl.maxs = (int)((S + kMaxWaves - 1) / kMaxWaves);
+    // the fewest steps per wave (a power of two) that covers K with <= 16 waves
+    pl.maxs = S <= 16 ? 1 : (S <= 32 ? 2 : (S <= 64 ? 4 : 8));
     pl.kw = (int)((S + pl.maxs - 1) / pl.maxs);
     const int per_cu = kMaxWaves / pl.kw > 0 ? kMaxWaves / pl.kw : 1;
     const int64_t G = num_groups(N);
@@ -429,9 +519,10 @@ GemmPlan plan_gemm_small(int64_t M, int64_t N, int64_t K, bool comp, int num_cus
     pl.grid = G < cap ? G : cap;
     const int64_t per_wg = (G + pl.grid - 1) / pl.grid;         // groups per workgroup
     // LDS per workgroup: at most 128 KB, and small enough for per_cu of them
-    const int64_t lds_cap = kRedBytesMax < kLdsPerCu / per_cu ? kRedBytesMax : kLdsPerCu / per_cu;
+    const int64_t lds_cap = kRedBytesMax < kLdsPerCu / per_cu - 1024 ? kRedBytesMax : kLdsPerCu / per_cu - 1024;
     const int64_t fit = lds_cap / ((int64_t)pl.kw * pl.rt * 1024);
     pl.ngl = (int)(per_wg < fit ? per_wg : fit);
+    if (pl.ngl < 1) pl.ngl = 1;
     return pl;
 }
 
@@ -440,8 +531,9 @@ hipError_t launch_gemm_small(int fmt, const GemmPlan& pl, bool comp, const void*
                              float* y, hipStream_t s) {
     GemmArgs a{static_cast<const uint8_t*>(act), row_bytes, static_cast<const uint8_t*>(blob), M,
                N, K, y, pl.ngl};
-    if (fmt == kNV) return launch_fmt<kNV>(a, pl.rt, comp, pl.maxs, pl.kw, pl.grid, s);
-    return launch_fmt<kMX>(a, pl.rt, comp, pl.maxs, pl.kw, pl.grid, s);
+    const bool single = num_groups(N) <= pl.grid;             // one group per workgroup
+    if (fmt == kNV) return launch_fmt<kNV>(a, pl.rt, comp, pl.maxs, pl.kw, pl.grid, s, single);
+    return launch_fmt<kMX>(a, pl.rt, comp, pl.maxs, pl.kw, pl.grid, s, single);
 }
 
 }  // namespace rsfp4

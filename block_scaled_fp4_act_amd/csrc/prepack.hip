@@ -58,29 +58,35 @@ __global__ __launch_bounds__(256) void w_amax_kernel(const T* __restrict__ W, in
     }
 }
 
-// Byte offsets inside the blob of the 16 codes of channel n, K-elements
-// k0 .. k0+15 (k0 a multiple of 16), and of their scale byte.
+// Byte offsets inside the blob of the 8 code bytes of channel n, K-elements
+// k0 .. k0+15 (k0 a multiple of 16), and of their block-scale byte.
 __device__ __forceinline__ int64_t code_off(int fmt, int64_t K, int64_t n, int64_t k0) {
     const int64_t c = n / kGroupN, i = n % kGroupN;
     const int64_t s = k0 / kStepK, g = (k0 % kStepK) / 32, half = (k0 % 32) / 16;
-    return kWHeader + c * group_bytes(fmt, K) + s * step_bytes(fmt) + (g * 16 + i) * 16 + half * 8;
+    return kWHeader + c * group_bytes(fmt, K) + step_code_offset(fmt, s) + (g * 16 + i) * 16 + half * 8;
 }
 __device__ __forceinline__ int64_t scale_off(int fmt, int64_t K, int64_t n, int64_t k0) {
     const int64_t c = n / kGroupN, i = n % kGroupN;
     const int64_t s = k0 / kStepK, g = (k0 % kStepK) / 32, half = (k0 % 32) / 16;
-    const int64_t base = kWHeader + c * group_bytes(fmt, K) + s * step_bytes(fmt) + kStepCodes;
-    return fmt == kNV ? base + (g * 16 + i) * 2 + half : base + (g * 16 + i);
+    const int64_t lane = g * 16 + i;
+    const int64_t base = kWHeader + c * group_bytes(fmt, K) + quad_scale_offset(fmt, s);
+    if (fmt == kNV) return base + lane * 8 + (s % kQuadSteps) * 2 + half;
+    return base + lane * 4 + (s % kQuadSteps);
 }
 
 // One thread per (channel n, 16-slice j) over the padded extent
-// [16 * groups) x [128 * steps / 16); MXFP4 pairs adjacent slices of one block
-// through a lane swap (blockDim is a multiple of 64, slices are channel-major so
-// slices 2t and 2t+1 of a channel sit in lanes 2u, 2u+1).
+// [16 * groups) x [128 * steps rounded up to whole quads / 16); MXFP4 pairs
+// adjacent slices of one block through a lane swap (blockDim is a multiple of 64,
+// slices are channel-major so slices 2t and 2t+1 of a channel sit in lanes 2u,
+// 2u+1).  Slices of the padding steps of the last quad write zero codes and
+// zero scales, so every byte a wave may load is defined.
 template <int FMT, typename T>
 __global__ __launch_bounds__(256) void prepack_kernel(const T* __restrict__ W, int64_t N, int64_t K,
                                                       uint8_t* __restrict__ blob) {
     const WHeader* h = reinterpret_cast<const WHeader*>(blob);
-    const int64_t slices_per_row = num_steps(K) * (kStepK / 16);
+    const int64_t S = num_steps(K);
+    const int64_t S_pad = (S + kQuadSteps - 1) / kQuadSteps * kQuadSteps;
+    const int64_t slices_per_row = S_pad * (kStepK / 16);
     const int64_t total = num_groups(N) * kGroupN * slices_per_row;
     const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
     const bool live = t < total;
@@ -157,7 +163,8 @@ hipError_t prepack_t(const void* W, int64_t N, int64_t K, void* blob, hipStream_
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const int64_t total = num_groups(N) * kGroupN * num_steps(K) * (kStepK / 16);
+    const int64_t S_pad = (num_steps(K) + kQuadSteps - 1) / kQuadSteps * kQuadSteps;
+    const int64_t total = num_groups(N) * kGroupN * S_pad * (kStepK / 16);
     const int64_t blocks = (total + 255) / 256;
     hipLaunchKernelGGL((prepack_kernel<FMT, T>), dim3((unsigned)blocks), dim3(256), 0, s,
                        static_cast<const T*>(W), N, K, b);

@@ -95,12 +95,14 @@ size_t rsfp4_packed_act_bytes(int fmt, int64_t M, int64_t K, int with_residue);
 
 /* Packed weight blob: a 256-byte header (magic "RSF4", ABI version, format, N,
  * K, the NVFP4 per-tensor scale) followed by ceil(N/16) groups of 16 output
- * channels; each group holds ceil(K/128) steps of 128 K-elements, and each step
- * is 1024 bytes of codes laid out for one 64-lane wave load (lane l = 16*g + i
- * holds channel i, K-elements 32*g .. 32*g+31 of the step) followed by that
- * step's block scales (NVFP4: 2 bytes per lane, 128 bytes; MXFP4: 1 byte per
- * lane, 64 bytes).  Channels beyond N and K-elements beyond K are zero codes
- * with zero scales. Only rsfp4_unpack_weights_canonical reads it back. */
+ * channels; each group holds ceil(K/512) quads of four 128-element K steps.  A
+ * quad is 4 x 1024 bytes of codes, each 1 KB laid out for one 64-lane wave load
+ * (lane l = 16*g + i holds channel i, K-elements 32*g .. 32*g+31 of the step),
+ * followed by the quad's block scales with each lane's four steps adjacent
+ * (NVFP4: 8 bytes per lane, the E4M3 bytes of blocks 2g, 2g+1 per step; MXFP4:
+ * 4 bytes per lane, the E8M0 byte of block g per step).  Channels beyond N,
+ * K-elements beyond K and the padding steps of the last quad are zero codes
+ * with zero scales.  Only rsfp4_unpack_weights_canonical reads it back. */
 size_t rsfp4_packed_weight_bytes(int fmt, int64_t N, int64_t K);
 
 /* Device workspace the linear calls need; this build needs none and returns 0

@@ -43,10 +43,10 @@ def test_size_queries():
     assert rs.act_row_bytes(0, 32) == 48 and rs.act_row_bytes(1, 32) == 48
     assert rs.packed_act_bytes(0, 4, 4096, True) == 8 * 2320
     assert rs.packed_act_bytes(0, 4, 4096, False) == 4 * 2320
-    # weights: header + groups(16 ch) x steps(128 K) x (1 KB codes + scales)
-    assert rs.packed_weight_bytes(0, 4096, 4096) == 256 + 256 * 32 * 1152
-    assert rs.packed_weight_bytes(1, 25600, 5120) == 256 + 1600 * 40 * 1088
-    assert rs.packed_weight_bytes(0, 17, 160) == 256 + 2 * 2 * 1152
+    # weights: header + groups(16 ch) x quads(4 steps of 128 K) x (4 KB codes + scales)
+    assert rs.packed_weight_bytes(0, 4096, 4096) == 256 + 256 * 8 * (4096 + 512)
+    assert rs.packed_weight_bytes(1, 25600, 5120) == 256 + 1600 * 10 * (4096 + 256)
+    assert rs.packed_weight_bytes(0, 17, 160) == 256 + 2 * 1 * (4096 + 512)   # padded quad
     assert rs.workspace_bytes(0, 4, 4096, 4096, True) == 0
     # invalid requests size to 0
     assert rs.packed_weight_bytes(0, 16, 48) == 0
