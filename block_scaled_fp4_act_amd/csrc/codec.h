@@ -48,36 +48,31 @@ __device__ __forceinline__ float e4m3_val(uint32_t b) {
 // Non-negative t -> E4M3 byte: nearest finite value, ties to even code,
 // saturating at 448 (0x7e, never the NaN code 0x7f); t NaN or <= 0 -> 0.
 // The subnormal range [0, 2^-6) is a uniform grid of step 2^-9, so the code is
-// rint(t * 2^9); above it the 3-bit mantissa of t is rounded with rint.
+// rint(t * 2^9); above it the 3-bit mantissa of t is rounded with rint.  Both
+// candidates are computed and selected (no branches: this sits on the
+// quantizer's critical path).
 __device__ __forceinline__ uint32_t e4m3_encode(float t) {
-    if (!(t > 0.0f)) return 0u;
-    if (t >= 448.0f) return 0x7Eu;
-    if (t < 0.015625f) {                                      // below 2^-6
-        return (uint32_t)__builtin_rintf(t * 512.0f);         // 0..8; 8 = 2^-6
-    }
+    const uint32_t sub = (uint32_t)__builtin_rintf(fminf(t, 0.015625f) * 512.0f);  // t < 2^-6: 0..8
     const uint32_t bits = __float_as_uint(t);
-    const int e = (int)((bits >> 23) & 255u) - 127;           // -6 .. 8
-    const float m = __uint_as_float((bits & 0x007FFFFFu) | 0x3F800000u); // [1,2)
-    uint32_t mm = (uint32_t)__builtin_rintf((m - 1.0f) * 8.0f);  // 0..8
-    uint32_t code = ((uint32_t)(e + 7) << 3) + mm;            // mm == 8 carries
-    return code > 0x7Eu ? 0x7Eu : code;
+    const int e = (int)((bits >> 23) & 255u) - 127;
+    const float m = __uint_as_float((bits & 0x007FFFFFu) | 0x3F800000u);   // [1,2)
+    const uint32_t mm = (uint32_t)__builtin_rintf((m - 1.0f) * 8.0f);     // 0..8, 8 carries
+    const uint32_t nrm = (uint32_t)((e + 7) << 3) + mm;
+    uint32_t code = t < 0.015625f ? sub : nrm;
+    code = t >= 448.0f ? 0x7Eu : code;
+    return t > 0.0f ? code : 0u;                                          // NaN and <= 0 -> 0
 }
 
 // MXFP4: E8M0 byte for a block whose largest magnitude is a >= 0:
 // floor(log2 a) - 2 biased by 127, clamped to [0, 254]; a == 0 -> 0.
 __device__ __forceinline__ uint32_t e8m0_for_amax(float a) {
-    if (!(a > 0.0f)) return 0u;
     const uint32_t bits = __float_as_uint(a);
     const int ef = (int)(bits >> 23);                         // a >= 0: no sign
-    int fl;                                                   // floor(log2 a)
-    if (ef > 0) {
-        fl = ef - 127;
-    } else {                                                  // subnormal
-        fl = (31 - __builtin_clz(bits)) - 149;
-    }
+    const int fl_sub = (31 - __builtin_clz(bits | 1u)) - 149;  // subnormal: leading one
+    const int fl = ef > 0 ? ef - 127 : fl_sub;                 // floor(log2 a)
     int e = fl - 2;
     e = e < -127 ? -127 : (e > 127 ? 127 : e);
-    return (uint32_t)(e + 127);
+    return a > 0.0f ? (uint32_t)(e + 127) : 0u;
 }
 
 // E8M0 byte -> 2^(b-127) as binary32 (b = 0 gives the subnormal 2^-127).

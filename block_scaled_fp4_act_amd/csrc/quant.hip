@@ -52,10 +52,11 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 // Workgroup-wide maximum of non-negative values; every thread gets the result.
+// `red` holds one slot per wave; callers alternate between two such arrays so
+// one barrier per reduction suffices (the next write goes to the other array).
 __device__ __forceinline__ float block_max(float v, float* red) {
     v = wave_max(v);
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    __syncthreads();                       // red may still be read from a prior call
     if (lane == 0) red[wid] = v;
     __syncthreads();
     float r = red[0];
@@ -132,8 +133,9 @@ __device__ __forceinline__ void quantize_chunks(float (&v)[NC][EPT], int nchunks
 #pragma unroll
         for (int e = 0; e < EPT; ++e) {
             const float x = v[c][e];
-            uint32_t mag = 0u;
-            if (st != 0.0f) mag = e2m1_mag(fabsf(x / st));
+            // (st == 0 gives inf or NaN here; the select below discards it)
+            const uint32_t mq = e2m1_mag(fabsf(x / st));
+            const uint32_t mag = st != 0.0f ? mq : 0u;
             const uint32_t code = (__float_as_uint(x) >> 28 & 8u) | mag;
             packed |= code << (4 * e);
             const float d = st * e2m1_val(code);
@@ -154,7 +156,7 @@ __global__ __launch_bounds__(kQMaxThreads) void quant_act_kernel(const TIn* __re
                                                                  int64_t K, int with_res,
                                                                  uint8_t* __restrict__ act,
                                                                  int64_t row_bytes) {
-    __shared__ float red[kQMaxThreads / 64];
+    __shared__ float red[2][kQMaxThreads / 64];
     const int m = blockIdx.x;
     const int tid = threadIdx.x;
     const int nchunks = (int)(K / EPT);
@@ -174,7 +176,7 @@ __global__ __launch_bounds__(kQMaxThreads) void quant_act_kernel(const TIn* __re
 #pragma unroll
         for (int e = 0; e < EPT; ++e) tmax = fmaxf(tmax, fabsf(v[c][e]));
     }
-    const float amax = block_max(tmax, red);
+    const float amax = block_max(tmax, red[0]);
     quantize_chunks<FMT, NC, EPT>(v, nchunks, K, amax, act + (int64_t)m * row_bytes);
     if (!with_res) return;
 
@@ -184,7 +186,7 @@ __global__ __launch_bounds__(kQMaxThreads) void quant_act_kernel(const TIn* __re
     for (int c = 0; c < NC; ++c)
 #pragma unroll
         for (int e = 0; e < EPT; ++e) rmax = fmaxf(rmax, fabsf(v[c][e]));
-    const float ramax = block_max(rmax, red);
+    const float ramax = block_max(rmax, red[1]);
     quantize_chunks<FMT, NC, EPT>(v, nchunks, K, ramax, act + (int64_t)(M + m) * row_bytes);
 }
 
