@@ -141,6 +141,7 @@ def run_workload(rs, torch, wl, M, steps, warmup, want_plain=True, want_kernels=
         out["quant_us"] = t_q * 1e3
         out["gemm_GBps"] = gb / (t_g * 1e-3) / 1e9
         out["gemm_hbm_frac"] = out["gemm_GBps"] / HBM_PEAK_GBS
+        out["gemm_TFLOPs"] = 2.0 * 2 * M * wl.N * wl.K / (t_g * 1e-3) / 1e12
     if want_plain:
         t_plain = time_graph(torch, lambda i: S.step(i, False), steps, warmup)
         out["plain_us_per_call"] = t_plain * 1e3
@@ -152,7 +153,7 @@ def run_workload(rs, torch, wl, M, steps, warmup, want_plain=True, want_kernels=
     return out, S, x
 
 
-def cpu_baseline(wl, x, W, budget_s=12.0, max_calls=30):
+def cpu_baseline(wl, x, W, budget_s=12.0, max_calls=100000):
     """The oracle (plain single-threaded C, fp64 accumulation) timed on the
     host: quantize + compensated linear per call, weights quantized beforehand
     as on the GPU.  Bounded: calls until ~budget_s seconds."""
@@ -225,8 +226,8 @@ def main():
     sweep = []
     if not args.no_sweep and not args.only_headline:
         cases = [(inputs.MLP_UP, 8), (inputs.MLP_DOWN, 8)]
-        cases += [(inputs.LARGE_MLP, m) for m in (1, 2, 4, 8)]
-        cases += [(inputs.MX, m) for m in (1, 8)]
+        cases += [(inputs.LARGE_MLP, m) for m in inputs.LARGE_MLP_M]
+        cases += [(inputs.MX, m) for m in inputs.MX_M]
         for w, m in cases:
             r, S2, _ = run_workload(rs, torch, w, m, min(args.steps, 100), min(args.warmup, 10))
             del S2

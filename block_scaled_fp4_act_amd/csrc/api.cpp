@@ -35,6 +35,7 @@ rsfp4_status hip_status(hipError_t e, const char* what) {
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 constexpr int kMaxDevices = 64;
+constexpr int64_t kNarrowRows = 32;   // tile rows (base + residue) the narrow-M kernel handles
 std::once_flag g_cu_once[kMaxDevices];
 int g_cus[kMaxDevices];
 
@@ -103,12 +104,10 @@ rsfp4_status linear(int fmt, bool comp, const void* act, size_t act_bytes, const
     rsfp4_status st = check_common(fmt, K);
     if (st != RSFP4_OK) return st;
     if (!act || !w_packed || !y) return fail(RSFP4_ERR_NULL, "act, w_packed and y must be non-NULL");
-    if (M < 1) return fail(RSFP4_ERR_SHAPE, "M = %lld must be >= 1", (long long)M);
+    if (M < 1 || M > 65535) return fail(RSFP4_ERR_SHAPE, "M = %lld outside [1, 65535]", (long long)M);
     if (N < 1 || N > (int64_t)1 << 24) return fail(RSFP4_ERR_SHAPE, "N = %lld outside [1, 2^24]", (long long)N);
     if (K > 16384) return fail(RSFP4_ERR_UNSUPPORTED, "the linear supports K <= 16384 (K = %lld)", (long long)K);
     const int64_t B = comp ? 2 * M : M;
-    if (B > 32)
-        return fail(RSFP4_ERR_UNSUPPORTED, "the linear supports at most 32 activation rows (B = %lld)", (long long)B);
     if (!aligned(act, 16) || !aligned(w_packed, 256) || !aligned(y, 4))
         return fail(RSFP4_ERR_ALIGN, "act must be 16-, w_packed 256- and y 4-byte aligned");
     const int64_t rb = act_row_bytes(fmt, K);
@@ -116,6 +115,13 @@ rsfp4_status linear(int fmt, bool comp, const void* act, size_t act_bytes, const
     if (act_bytes < need_a) return fail(RSFP4_ERR_BUFFER_TOO_SMALL, "act holds %zu bytes, needs %zu", act_bytes, need_a);
     const size_t need_w = (size_t)packed_weight_bytes(fmt, N, K);
     if (w_bytes < need_w) return fail(RSFP4_ERR_BUFFER_TOO_SMALL, "w_packed holds %zu bytes, needs %zu", w_bytes, need_w);
+    if (B > kNarrowRows) {
+        if (std::getenv("RSFP4_LOG"))
+            std::fprintf(stderr, "[rsfp4] linear fmt=%d comp=%d M=%lld N=%lld K=%lld tiled\n", fmt, (int)comp,
+                         (long long)M, (long long)N, (long long)K);
+        return hip_status(launch_gemm_tile(fmt, comp, act, rb, w_packed, (int)M, N, K, y, (hipStream_t)stream),
+                          "linear launch");
+    }
     int cus = 0;
     st = num_cus(&cus);
     if (st != RSFP4_OK) return st;

@@ -30,4 +30,9 @@ hipError_t launch_gemm_small(int fmt, const GemmPlan& pl, bool comp, const void*
                              int64_t row_bytes, const void* blob, int M, int64_t N, int64_t K,
                              float* y, hipStream_t s);
 
+// Wide-operand linear (any number of activation rows): 2-D tiles of 128 rows x
+// 128 channels per workgroup, each wave walking all of K.
+hipError_t launch_gemm_tile(int fmt, bool comp, const void* act, int64_t row_bytes, const void* blob,
+                            int M, int64_t N, int64_t K, float* y, hipStream_t s);
+
 }  // namespace rsfp4

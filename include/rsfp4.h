@@ -38,10 +38,9 @@
  *     a message for rsfp4_last_error() (per thread). A HIP launch failure returns
  *     RSFP4_ERR_HIP with the HIP error string in the message.
  *   - Shape limits: M >= 1, N >= 1, K >= 32 and K % 32 == 0 (both formats, so a
- *     K-run of 32 is whole in either block size); quantize needs K <= 32768;
- *     the linear needs K <= 16384 and B <= 32 activation rows, where B = M for
- *     the plain call and B = 2M for the compensated call.  Calls outside these
- *     limits return RSFP4_ERR_SHAPE or RSFP4_ERR_UNSUPPORTED.
+ *     K-run of 32 is whole in either block size); M <= 65535; quantize needs
+ *     K <= 32768; the linear needs K <= 16384 and N <= 2^24.  Calls outside
+ *     these limits return RSFP4_ERR_SHAPE or RSFP4_ERR_UNSUPPORTED.
  *   - All calls are thread-safe; concurrent calls on different streams are
  *     independent.
  */
@@ -142,11 +141,14 @@ rsfp4_status rsfp4_mxfp4_quantize_act_with_residue(const void* x, int xt, int64_
  *                          buffer may or may not hold residue rows)
  *   *_linear_compensated:  y = deq(q(x)) W^T + deq(q(r)) W^T (B = 2M rows; the
  *                          buffer must have been quantized with_residue)
- * Each packed weight step is loaded from HBM once and multiplied with all B
- * activation rows; base and residue products of one token land in the same
- * lane's accumulators and are added there before the single store (ResServe
- * Section 4.3, Eq. 2 and Section 5.1, Eq. 4).  act_bytes and w_packed_bytes are
- * checked against the size queries. */
+ * B = M (plain) or 2M (compensated) activation rows enter the product.  Up to
+ * 32 rows, each packed weight step is loaded from HBM once and multiplied with
+ * all B rows (the narrow-M, memory-bound regime); above 32 rows a 2-D tiled
+ * kernel covers 128 rows x 128 channels per workgroup (each weight tile is then
+ * read once per 128 rows).  Either way base and residue products of one token
+ * land in the same lane's accumulators and are added there before the single
+ * store (ResServe Section 4.3, Eq. 2 and Section 5.1, Eq. 4).  act_bytes and
+ * w_packed_bytes are checked against the size queries. */
 rsfp4_status rsfp4_nvfp4_linear(const void* act, size_t act_bytes, const void* w_packed,
                                 size_t w_packed_bytes, int64_t M, int64_t N, int64_t K,
                                 float* y, void* ws, size_t ws_bytes, void* stream);

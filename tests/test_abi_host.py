@@ -69,9 +69,12 @@ def test_validation_errors_without_device():
     # bad K
     assert L.rsfp4_nvfp4_linear(FAKE, 1 << 20, FAKE, 1 << 20, 1, 16, 100, FAKE, None, 0, None) == 2
     assert L.rsfp4_mxfp4_quantize_act_with_residue(FAKE, 0, 1, 48, 1, FAKE, 1 << 20, None) == 2
-    # K above the linear's limit, B above 32
+    # K above the linear's limit, M outside [1, 65535]
     assert L.rsfp4_nvfp4_linear(FAKE, 1 << 30, FAKE, 1 << 30, 1, 16, 16416, FAKE, None, 0, None) == 6
-    assert L.rsfp4_mxfp4_linear_compensated(FAKE, 1 << 30, FAKE, 1 << 30, 17, 16, 512, FAKE, None, 0, None) == 6
+    assert L.rsfp4_mxfp4_linear_compensated(FAKE, 1 << 30, FAKE, 1 << 30, 65536, 16, 512, FAKE, None, 0, None) == 2
+    assert L.rsfp4_mxfp4_linear(FAKE, 1 << 30, FAKE, 1 << 30, 0, 16, 512, FAKE, None, 0, None) == 2
+    # a wide operand's buffer is checked like a narrow one's
+    assert L.rsfp4_mxfp4_linear_compensated(FAKE, 1000, FAKE, 1 << 30, 40, 16, 512, FAKE, None, 0, None) == 5
     # quantize K limit and M limit
     assert L.rsfp4_nvfp4_quantize_act_with_residue(FAKE, 0, 1, 32800, 1, FAKE, 1 << 30, None) == 2
     assert L.rsfp4_nvfp4_quantize_act_with_residue(FAKE, 0, 0, 512, 1, FAKE, 1 << 30, None) == 2

@@ -168,6 +168,10 @@ def _oracle_linear(x, W, fmt, bf16, comp, rows=None):
 SMALL_CASES = [  # (M, N, K): several tiles, ragged N and K tails, both row-tile counts
     (1, 512, 512), (2, 72, 160), (3, 1000, 384), (4, 256, 4096), (5, 48, 640),
     (8, 320, 1024), (8, 100, 2080), (11, 64, 256), (16, 64, 512), (6, 16, 32),
+    # wide operands (more than 32 tile rows): the 2-D tiled kernel, with ragged
+    # row tiles, channel tiles and K tails
+    (17, 264, 384), (33, 130, 160), (40, 512, 1056), (64, 128, 256), (100, 72, 2048),
+    (129, 300, 512),
 ]
 
 
@@ -176,8 +180,6 @@ SMALL_CASES = [  # (M, N, K): several tiles, ragged N and K tails, both row-tile
 @pytest.mark.parametrize("MNK", SMALL_CASES, ids=lambda t: "M%dN%dK%d" % t)
 def test_linear_small_full(fmt, comp, MNK):
     M, N, K = MNK
-    if comp and 2 * M > 32:
-        pytest.skip("B = 2M above 32 rows")
     rng = np.random.default_rng(M * 1000 + N + K)
     x = rng.standard_normal((M, K)).astype(np.float32)
     x[:, rng.choice(K, max(1, K // 100), replace=False)] *= 20
@@ -189,8 +191,8 @@ def test_linear_small_full(fmt, comp, MNK):
 
 def _workload_cases():
     wls = [inputs.SMALL, inputs.ATTN, inputs.MLP_UP, inputs.MLP_DOWN]
-    wls += [inputs.LARGE_MLP.with_m(m) for m in (1, 8, 16)]
-    wls += [inputs.MX.with_m(m) for m in (1, 8)]
+    wls += [inputs.LARGE_MLP.with_m(m) for m in inputs.LARGE_MLP_M]
+    wls += [inputs.MX.with_m(m) for m in inputs.MX_M]
     return [(wl, comp) for wl in wls for comp in (True, False)]
 
 
@@ -199,8 +201,6 @@ def _workload_cases():
 def test_linear_workload_sampled(wl, comp):
     """Full-size workloads, launched exactly as the bench launches them; the
     oracle computes a sample of output channels one by one."""
-    if comp and 2 * wl.M > 32:
-        pytest.skip("B = 2M above 32 rows")
     fmt = FMT[wl.fmt]
     x, W = wl.draw_x(), _weights(wl)
     y, _, _ = _run_linear(x, W, fmt, wl.bf16, comp)
@@ -258,6 +258,10 @@ def test_linear_limits_rejected():
     act = torch.zeros(rs.packed_act_bytes(0, 17, 512, True), dtype=torch.uint8, device="cuda")
     blob = torch.zeros(rs.packed_weight_bytes(0, 64, 512), dtype=torch.uint8, device="cuda")
     with pytest.raises(RuntimeError, match="unsupported"):
-        rs.fp4_linear_compensated(act, blob, 17, 64, 512, 0)
+        rs.fp4_linear_compensated(act, blob, 1, 64, 16416, 0)
+    with pytest.raises(RuntimeError, match="outside"):
+        rs.fp4_linear_compensated(act, blob, 65536, 64, 512, 0)
     with pytest.raises(RuntimeError, match="too small"):
         rs.fp4_linear_compensated(act[:100], blob, 1, 64, 512, 0)
+    with pytest.raises(RuntimeError, match="too small"):
+        rs.fp4_linear_compensated(act, blob, 18, 64, 512, 0)
