@@ -14,9 +14,11 @@ roofline of the dominant kernel, the oracle timed on the host cores, and a
 sweep over the other decode workloads.
 """
 import argparse
+import hashlib
 import json
 import math
 import os
+import platform
 import sys
 import time
 
@@ -29,6 +31,27 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 ROTATE_BYTES = 512 << 20       # distinct weight bytes per timed loop (2x the MALL)
 
 METRIC = "compensated FP4 linear µs/call + HBM GB/s (% of peak) at M=1–8, K,N≥4096"
+
+# HBM traffic of the dominant kernel (compensated NVFP4 linear at the headline
+# shape), from rocprofv3 FETCH_SIZE / WRITE_SIZE passes over `bench.py
+# --pmc-launches`, per launch, already multiplied by the copy-kernel
+# calibration factors (FETCH_SIZE x2.0, WRITE_SIZE x1.0).  Valid only for the
+# kernel sources whose hash is recorded; reported as null otherwise.
+TRAFFIC = {
+    "sources_sha256": "21c7bb75ea1142b37c7d5bffaf3044f14fd2f155c5bcf242da2651d5009f1fcf",
+    "fetch_bytes": 2.0 * 4718 * 1024,   # FETCH_SIZE 4718 KiB per launch
+    "write_bytes": 1.0 * 64 * 1024,     # WRITE_SIZE 64 KiB per launch
+}
+KERNEL_SOURCES = ["gemm.hip", "layout.h", "codec.h"]
+
+
+def kernel_sources_sha256():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "block_scaled_fp4_act_amd", "csrc")
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def blk(fmt):
@@ -153,6 +176,62 @@ def run_workload(rs, torch, wl, M, steps, warmup, want_plain=True, want_kernels=
     return out, S, x
 
 
+def host_info():
+    model = platform.processor() or ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu": model, "nproc": os.cpu_count()}
+
+
+def read_peak_gbps(torch, nbytes=1 << 30, reps=20):
+    """Streaming-read rate of the box measured with a plain device reduction
+    (torch sum over a 1 GiB fp32 tensor), for context beside the nominal peak."""
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        x.sum()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        x.sum()
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / reps
+    del x
+    torch.cuda.empty_cache()
+    return nbytes / t / 1e9
+
+
+def pmc_launches(rs, torch):
+    """Eager launches for hardware-counter passes (no graphs): a 256 MiB device
+    copy three times (calibration: known bytes read and written), then six
+    compensated NVFP4 linears at the headline shape over distinct weight copies."""
+    from block_scaled_fp4_act_amd import inputs
+    a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+    wl = inputs.ATTN
+    S = Setup(rs, torch, 0, wl.M, wl.N, wl.K, wl.draw_x(), torch.from_numpy(wl.draw_w()).cuda())
+    for i in range(6):
+        S.quant(i, True)
+    torch.cuda.synchronize()
+    for i in range(6):
+        S.gemm(i, True)
+    torch.cuda.synchronize()
+    print(json.dumps({"pmc_launches": "done", "copy_bytes": 256 << 20,
+                      "linear_algorithmic_bytes": gemm_bytes(0, wl.M, wl.N, wl.K, True)}), flush=True)
+
+
 def cpu_baseline(wl, x, W, budget_s=12.0, max_calls=100000):
     """The oracle (plain single-threaded C, fp64 accumulation) timed on the
     host: quantize + compensated linear per call, weights quantized beforehand
@@ -172,7 +251,7 @@ def cpu_baseline(wl, x, W, budget_s=12.0, max_calls=100000):
     per_call = el / n
     sb = step_bytes(fmt, x.shape[0], W.shape[0], W.shape[1], True, 2)
     return {"value": sb / per_call / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "us_per_call": per_call * 1e6,
+            "us_per_call": per_call * 1e6, "host": host_info(),
             "sample": f"{n} full calls of the {wl.name} compensated step (quantize + linear, "
                       f"weights pre-quantized), single thread, {el:.1f} s"}
 
@@ -185,6 +264,8 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-headline", action="store_true", help="skip plain/kernels/sweep (profiling runs)")
+    ap.add_argument("--pmc-launches", action="store_true",
+                    help="only eager launches for counter passes (copy calibration + headline linear)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -196,6 +277,9 @@ def main():
     from block_scaled_fp4_act_amd import inputs
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     rs.lib()
+    if args.pmc_launches:
+        pmc_launches(rs, torch)
+        return
 
     wl = inputs.ATTN
     W = wl.draw_w()
@@ -218,8 +302,11 @@ def main():
     roof = None
     if "gemm_us" in head:
         ach = gb / (head["gemm_us"] * 1e-6) / 1e9
+        traffic = None
+        if TRAFFIC["sources_sha256"] is not None and TRAFFIC["sources_sha256"] == kernel_sources_sha256():
+            traffic = TRAFFIC["fetch_bytes"] + TRAFFIC["write_bytes"]
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": "gemm_small_kernel (compensated NVFP4 linear)",
                 "algorithmic_bytes_per_launch": gb}
 
@@ -233,6 +320,11 @@ def main():
             del S2
             torch.cuda.empty_cache()
             sweep.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()})
+
+    if roof is not None and not args.only_headline:
+        rp = read_peak_gbps(torch)
+        roof["measured_read_peak"] = round(rp, 1)
+        roof["frac_of_measured_read_peak"] = round(roof["achieved"] / rp, 4)
 
     cpu = None
     if not args.no_cpu_baseline:
