@@ -274,6 +274,8 @@ def main():
     ap.add_argument("--only-headline", action="store_true", help="skip plain/kernels/sweep (profiling runs)")
     ap.add_argument("--pmc-launches", action="store_true",
                     help="only eager launches for counter passes (copy calibration + headline linear)")
+    ap.add_argument("--cases", default=None,
+                    help="only these sweep cases, e.g. 'large_mlp:128,mx:256' (no headline, no oracle timing)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -287,6 +289,16 @@ def main():
     rs.lib()
     if args.pmc_launches:
         pmc_launches(rs, torch)
+        return
+    if args.cases:
+        named = {"attn": inputs.ATTN, "mlp_up": inputs.MLP_UP, "mlp_down": inputs.MLP_DOWN,
+                 "large_mlp": inputs.LARGE_MLP, "mx": inputs.MX, "small": inputs.SMALL}
+        for item in args.cases.split(","):
+            name, m = item.split(":")
+            r, S2, _ = run_workload(rs, torch, named[name], int(m), min(args.steps, 100), min(args.warmup, 10))
+            del S2
+            torch.cuda.empty_cache()
+            print(json.dumps({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}), flush=True)
         return
 
     wl = inputs.ATTN
