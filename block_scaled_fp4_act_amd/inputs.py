@@ -90,3 +90,24 @@ MX = Workload("mxfp4_k5120_n25600", "mxfp4", 8, 5120, 25600, 0, 1, 2, 0.01, 20.0
 MX_M = (1, 8, 256)
 
 ALL = (SMALL, ATTN, MLP_UP, MLP_DOWN, LARGE_MLP, MX)
+
+
+# ---- selective compensation (K-Ext) inputs ----
+# Channel masks: k of every 8 channels drawn uniformly (bit j of byte g marks
+# channel 8g + j).  Calibration rows: fresh draws of a workload's distribution
+# (same outlier channels, another seed), standing in for a calibration set.
+KEXT_K = (1, 2, 4)           # k = 8 * rho for rho = 0.125, 0.25, 0.5
+CALIB_ROWS = 64
+
+
+def random_masks(K: int, k: int, seed: int) -> np.ndarray:
+    g = np.random.Generator(np.random.PCG64(seed))
+    masks = np.zeros((K // 8,), np.uint8)
+    for i in range(K // 8):
+        for j in g.choice(8, size=k, replace=False):
+            masks[i] |= np.uint8(1 << int(j))
+    return masks
+
+
+def calibration_rows(w: Workload, T: int = CALIB_ROWS, seed_offset: int = 1000) -> np.ndarray:
+    return activations(T, w.K, w.x_seed + seed_offset, w.outlier_frac, w.outlier_scale, w.o_seed, w.bf16)

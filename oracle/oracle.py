@@ -4,7 +4,8 @@ TEST INFRASTRUCTURE ONLY.  Every function here marshals numpy arrays into the C
 oracle and back; the arithmetic lives in the C file, which follows the ResServe
 page (arXiv 2611.08713): Section 2 / Figure 1 for the formats, Appendix B.2
 Eqs. 8-10 for the NVFP4 scale computation, Section 4.2 Eq. 1 and Section 4.3
-Eq. 2 for the compensated product and its Fold.
+Eq. 2 for the compensated product and its Fold; Section 5.3, Eq. 6 and
+Appendix B.1, Eq. 7 for selective compensation (K-Ext).
 """
 import ctypes
 import os
@@ -25,6 +26,7 @@ __all__ = [
     "e8m0_for_amax", "e8m0_value", "nvfp4_global_scale", "absmax",
     "quantize_act", "quantize_weight", "quantize_weight_rows", "dequant_rows",
     "linear", "unpack_codes",
+    "channel_abs_sum", "kext_select", "kext_dim", "kext_extend_weight", "kext_quantize_act",
 ]
 
 
@@ -67,6 +69,14 @@ def lib():
         L.oracle_quantize_weight_rows.argtypes = [i32, P, i64, i64, f32, P, P, P]
         L.oracle_linear.restype = None
         L.oracle_linear.argtypes = [P, P, i64, i64, i64, i32, P, P]
+        L.oracle_channel_abs_sum.restype = None
+        L.oracle_channel_abs_sum.argtypes = [P, i64, i64, P]
+        L.oracle_kext_select.restype = None
+        L.oracle_kext_select.argtypes = [P, i64, i32, P]
+        L.oracle_kext_extend_weight.restype = None
+        L.oracle_kext_extend_weight.argtypes = [P, i64, i64, P, i32, P]
+        L.oracle_kext_quantize_act.restype = None
+        L.oracle_kext_quantize_act.argtypes = [i32, P, i64, i64, P, i32, P, P, P, P, P]
         _lib = L
     return _lib
 
@@ -199,3 +209,68 @@ def linear(dx, dw, M, compensated, want_beta=True):
     lib().oracle_linear(_p(dx), _p(dw), M, N, K, 1 if compensated else 0, _p(y),
                         _p(beta) if want_beta else None)
     return y, beta
+
+
+# ---------------------------------------------------------------- K-Ext --
+
+def channel_abs_sum(x, prev=None):
+    """Calibration score: per-channel sum of |x| over the rows of x[T, K] in
+    binary64, rows in order, continuing from prev (a [K] f64 array) if given."""
+    x = _f32(x)
+    T, K = x.shape
+    out = np.zeros((K,), np.float64) if prev is None else np.array(prev, np.float64, copy=True)
+    lib().oracle_channel_abs_sum(_p(x), T, K, _p(out))
+    return out
+
+
+def kext_select(score, k):
+    """Top-k channels of every 8-channel group (ties to the lower index) as
+    K/8 mask bytes."""
+    score = np.ascontiguousarray(score, dtype=np.float64)
+    K = score.size
+    assert K % 8 == 0 and k in (1, 2, 4, 8)
+    masks = np.zeros((K // 8,), np.uint8)
+    lib().oracle_kext_select(_p(score), K, int(k), _p(masks))
+    return masks
+
+
+def kext_dim(K, k):
+    """Effective reduction length K_eff = K + (K/8) k."""
+    return K + (K // 8) * k
+
+
+def _check_masks(masks, K, k):
+    masks = np.ascontiguousarray(masks, dtype=np.uint8)
+    assert masks.size == K // 8
+    pop = np.unpackbits(masks.reshape(-1, 1), axis=1).sum(axis=1)
+    assert np.all(pop == k), "every mask byte must select exactly k channels"
+    return masks
+
+
+def kext_extend_weight(W, masks, k):
+    """[W | W[:, S]] with the selected columns in extension order (fp32)."""
+    W = _f32(W)
+    N, K = W.shape
+    masks = _check_masks(masks, K, k)
+    out = np.zeros((N, kext_dim(K, k)), np.float32)
+    lib().oracle_kext_extend_weight(_p(W), N, K, _p(masks), int(k), _p(out))
+    return out
+
+
+def kext_quantize_act(x, fmt, masks, k):
+    """K-Ext activation records: codes [M, K_eff/2], scales [M, K_eff/blk],
+    globals [M] (NVFP4 base tensor scale), deq [M, K_eff]."""
+    x = _f32(x)
+    M, K = x.shape
+    masks = _check_masks(masks, K, k)
+    KE = kext_dim(K, k)
+    blk = BLOCK[fmt]
+    assert (KE - K) % blk == 0, "the extension must hold whole blocks"
+    codes = np.zeros((M, KE // 2), np.uint8)
+    scales = np.zeros((M, KE // blk), np.uint8)
+    globs = np.zeros((M,), np.float32)
+    deq = np.zeros((M, KE), np.float32)
+    work = np.zeros((KE - K,), np.float32)
+    lib().oracle_kext_quantize_act(fmt, _p(x), M, K, _p(masks), int(k), _p(codes), _p(scales),
+                                   _p(globs), _p(deq), _p(work))
+    return {"codes": codes, "scales": scales, "globals": globs, "deq": deq}

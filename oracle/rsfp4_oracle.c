@@ -32,6 +32,21 @@
  *     range [2^-127, 2^127]; an all-zero block gets byte 0x00;
  *   - nibble order: the element with the even K index sits in the low nibble.
  *
+ * Selective compensation (K-Ext; ResServe Section 5.2 "Selective Prefill
+ * Execution", Eq. 6, Appendix B.1 Eq. 7, Figure 15), in the reading listed in
+ * the design notes:
+ *   - calibration statistic of channel i: the sum over calibration rows of |x|
+ *     in binary64, rows in order (comparing sums is comparing means);
+ *   - per 8-channel group, the k channels with the largest statistic; ties go
+ *     to the lower channel index; an 8-bit mask per group records them;
+ *   - the extension holds the selected residues group by group, each group's
+ *     channels in increasing order, K_eff = K + (K/8) k;
+ *   - the extension is quantized in its own 16 (NVFP4) / 32 (MXFP4) blocks;
+ *     NVFP4 uses the base row's tensor scale for them (an extended row carries
+ *     one tensor scale in the GEMM), MXFP4 its E8M0 rule;
+ *   - the weights gain the selected columns in the same order and are quantized
+ *     as one K_eff-wide matrix (same per-tensor scale, the columns repeat).
+ *
  * Arithmetic: every quantization step is IEEE binary32 with round-to-nearest-even;
  * this file is compiled with -ffp-contract=off so no multiply-add is fused.
  * The linear accumulates exact fp32 x fp32 products in binary64.
@@ -314,5 +329,103 @@ ORACLE_API void oracle_linear(const float* dx, const float* dw, int64_t M, int64
             y[m * N + n] = acc;
             if (beta) beta[m * N + n] = mag;
         }
+    }
+}
+
+/* ----------------------------------------- selective compensation (K-Ext) ---- */
+
+/* Calibration statistic (Appendix B.1): sum[i] += |x[t, i]| for t = 0 .. T-1 in
+ * binary64, one row after another.  The page scores a channel by its mean
+ * absolute activation; for a fixed number of rows the sum orders channels the
+ * same way.  Continuing from an earlier sum is the same as summing the
+ * concatenated rows in order. */
+ORACLE_API void oracle_channel_abs_sum(const float* x, int64_t T, int64_t K, double* sum) {
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t i = 0; i < K; ++i) sum[i] += fabs((double)x[t * K + i]);
+}
+
+/* Block-local selection (Appendix B.1, Eq. 7): in every group of 8 channels the
+ * k with the largest score, ties to the lower index.  masks: K/8 bytes, bit j
+ * set when channel 8g + j is selected. */
+ORACLE_API void oracle_kext_select(const double* score, int64_t K, int k, uint8_t* masks) {
+    for (int64_t g = 0; g < K / 8; ++g) {
+        const double* s = score + 8 * g;
+        uint8_t mask = 0;
+        for (int q = 0; q < k; ++q) {      /* take the best channel not yet taken, k times */
+            int best = -1;
+            for (int j = 0; j < 8; ++j) {
+                if (mask & (1u << j)) continue;
+                if (best < 0 || s[j] > s[best]) best = j;   /* strict: lower index wins ties */
+            }
+            mask = (uint8_t)(mask | (1u << best));
+        }
+        masks[g] = mask;
+    }
+}
+
+/* Extension order (Section 5.3, Eq. 6 and Appendix B.1): extension element p
+ * belongs to group p / k and is the (p % k)-th selected channel of that group in
+ * increasing channel order.  Returns the channel index; masks must hold exactly
+ * k bits per byte. */
+static int64_t kext_channel(const uint8_t* masks, int k, int64_t p) {
+    const int64_t g = p / k;
+    int want = (int)(p % k);
+    for (int j = 0; j < 8; ++j) {
+        if (!(masks[g] & (1u << j))) continue;
+        if (want == 0) return 8 * g + j;
+        --want;
+    }
+    return -1;
+}
+
+/* Extended weight (Eq. 6): Wext[n] = [W[n, 0..K) | W[n, S]] with the selected
+ * columns in extension order; K_eff = K + (K/8) k.  Quantizing Wext as one
+ * K_eff-wide tensor gives the page's W^_S in the extended block layout. */
+ORACLE_API void oracle_kext_extend_weight(const float* W, int64_t N, int64_t K, const uint8_t* masks,
+                                          int k, float* Wext) {
+    const int64_t ext = (K / 8) * k, KE = K + ext;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t i = 0; i < K; ++i) Wext[n * KE + i] = W[n * K + i];
+        for (int64_t p = 0; p < ext; ++p) Wext[n * KE + K + p] = W[n * K + kext_channel(masks, k, p)];
+    }
+}
+
+/* Quantize M rows into K-Ext records of K_eff = K + (K/8) k elements (Eq. 6;
+ * Appendix B.2, Algorithm 1): elements [0, K) are the base q(x) exactly as in
+ * oracle_quantize_act; elements [K, K_eff) are the residues r = x - deq(q(x))
+ * of the selected channels in extension order, quantized in their own blocks
+ * (NVFP4: with the base row's tensor scale, which the algorithm passes to both
+ * block-scale steps; MXFP4: the E8M0 rule).  codes: M x K_eff/2; scales:
+ * M x K_eff/blk; globals: M (NVFP4 base tensor scale, 0 for MXFP4); deq:
+ * M x K_eff or NULL; work: (K/8) k floats of scratch. */
+ORACLE_API void oracle_kext_quantize_act(int fmt, const float* x, int64_t M, int64_t K,
+                                         const uint8_t* masks, int k, uint8_t* codes, uint8_t* scales,
+                                         float* globals, float* deq, float* work) {
+    const int64_t blk = fmt == 0 ? 16 : 32;
+    const int64_t ext = (K / 8) * k, KE = K + ext;
+    for (int64_t m = 0; m < M; ++m) {
+        const float* row = x + m * K;
+        uint8_t* c = codes + m * (KE / 2);
+        uint8_t* s = scales + m * (KE / blk);
+        float* d = deq ? deq + m * KE : (float*)0;
+        float sg = 0.0f;
+        if (fmt == 0) {
+            sg = oracle_nvfp4_global_scale(oracle_absmax(row, K));
+            oracle_nvfp4_quantize_row(row, K, sg, c, s, d);
+        } else {
+            oracle_mxfp4_quantize_row(row, K, c, s, d);
+        }
+        globals[m] = sg;
+        for (int64_t p = 0; p < ext; ++p) {
+            const int64_t i = kext_channel(masks, k, p);
+            const uint8_t code = (uint8_t)((i & 1) ? (c[i / 2] >> 4) : (c[i / 2] & 15u));
+            const float e = oracle_e2m1_value(code);
+            const float st = fmt == 0 ? oracle_e4m3_value(s[i / 16]) * sg : oracle_e8m0_value(s[i / 32]);
+            work[p] = row[i] - st * e;
+        }
+        if (fmt == 0)
+            oracle_nvfp4_quantize_row(work, ext, sg, c + K / 2, s + K / blk, d ? d + K : (float*)0);
+        else
+            oracle_mxfp4_quantize_row(work, ext, c + K / 2, s + K / blk, d ? d + K : (float*)0);
     }
 }
