@@ -10,8 +10,10 @@ graph so host launch cost does not enter the timing.
 
 Prints ONE JSON line.  Extra keys: the uncompensated (plain W4A4) pair and the
 compensation overhead, per-kernel averages, NMSE against the fp32 product, the
-roofline of the dominant kernel, the oracle timed on the host cores, and a
-sweep over the other decode workloads.
+roofline of the dominant kernel, the oracle timed on the host cores, a sweep
+over the other decode workloads, and selective compensation (K-Ext) at
+rho = 0.125 / 0.25 / 0.5 on the prefill-sized operands beside their plain and
+full-residue steps.
 """
 import argparse
 import hashlib
@@ -106,6 +108,69 @@ class Setup:
     def step(self, i, comp):
         self.quant(i, comp)
         self.gemm(i, comp)
+
+
+class KextSetup:
+    """Selective compensation (K-Ext) buffers: masks from an on-device
+    calibration pass, R rotated [W | W_S] blobs of width K_eff, inputs."""
+
+    def __init__(self, rs, torch, fmt, M, N, K, k, x_np, W_dev, x_cal_np):
+        self.rs, self.torch = rs, torch
+        self.fmt, self.M, self.N, self.K, self.k = fmt, M, N, K, k
+        self.KE = rs.kext_dim(K, k)
+        xc = torch.from_numpy(x_cal_np).cuda().to(torch.bfloat16)
+        self.masks = rs.kext_select(rs.channel_abs_sum(xc), k)
+        blob = rs.prepack_weights_kext(W_dev, fmt, self.masks, k)
+        self.R = max(2, int(math.ceil(ROTATE_BYTES / blob.numel())))
+        self.blobs = [blob] + [blob.clone() for _ in range(self.R - 1)]
+        x = torch.from_numpy(x_np).cuda().to(torch.bfloat16)
+        self.xs = [x.clone() for _ in range(self.R)]
+        nb = rs.packed_act_bytes(fmt, M, self.KE, False)
+        self.acts = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(self.R)]
+        self.ys = [torch.empty((M, N), dtype=torch.float32, device="cuda") for _ in range(self.R)]
+
+    def quant(self, i):
+        r = i % self.R
+        self.rs.quantize_act_kext(self.xs[r], self.fmt, self.masks, self.k, out=self.acts[r])
+
+    def gemm(self, i):
+        r = i % self.R
+        self.rs.fp4_linear(self.acts[r], self.blobs[r], self.M, self.N, self.KE, self.fmt, out=self.ys[r])
+
+    def step(self, i):
+        self.quant(i)
+        self.gemm(i)
+
+
+def run_kext(rs, torch, wl, M, ks, steps, warmup):
+    """K-Ext steps (quantize + one plain product over K_eff) at each k in ks,
+    beside the plain and full-residue steps of the same workload."""
+    from block_scaled_fp4_act_amd import inputs
+    fmt = 0 if wl.fmt == "nvfp4" else 1
+    base, S, x = run_workload(rs, torch, wl, M, steps, warmup, want_plain=True, want_kernels=False)
+    del S
+    torch.cuda.empty_cache()
+    gen = torch.Generator(device="cuda").manual_seed(wl.w_seed)
+    W_dev = torch.randn((wl.N, wl.K), generator=gen, device="cuda", dtype=torch.float32) * 0.02
+    xcal = inputs.calibration_rows(wl)
+    out = {"workload": wl.name, "format": wl.fmt, "M": M, "K": wl.K, "N": wl.N,
+           "plain_us_per_call": round(base["plain_us_per_call"], 3),
+           "full_us_per_call": round(base["us_per_call"], 3), "kext": []}
+    for k in ks:
+        S = KextSetup(rs, torch, fmt, M, wl.N, wl.K, k, x, W_dev, xcal)
+        t = time_graph(torch, lambda i: S.step(i), steps, warmup)
+        tg = time_graph(torch, lambda i: S.gemm(i), steps, warmup)
+        tq = time_graph(torch, lambda i: S.quant(i), steps, warmup)
+        out["kext"].append({
+            "rho": k / 8.0, "K_eff": S.KE, "us_per_call": round(t * 1e3, 3), "gemm_us": round(tg * 1e3, 3),
+            "quant_us": round(tq * 1e3, 3), "vs_plain": round(t * 1e3 / base["plain_us_per_call"], 4),
+            "vs_full": round(t * 1e3 / base["us_per_call"], 4),
+            "gemm_TFLOPs": round(2.0 * M * wl.N * S.KE / (tg * 1e-3) / 1e12, 2)})
+        del S
+        torch.cuda.empty_cache()
+    del W_dev
+    torch.cuda.empty_cache()
+    return out
 
 
 def time_graph(torch, fn, steps, warmup):
@@ -294,8 +359,14 @@ def main():
         named = {"attn": inputs.ATTN, "mlp_up": inputs.MLP_UP, "mlp_down": inputs.MLP_DOWN,
                  "large_mlp": inputs.LARGE_MLP, "mx": inputs.MX, "small": inputs.SMALL}
         for item in args.cases.split(","):
-            name, m = item.split(":")
-            r, S2, _ = run_workload(rs, torch, named[name], int(m), min(args.steps, 100), min(args.warmup, 10))
+            parts = item.split(":")
+            name, m = parts[0], int(parts[1])
+            if len(parts) > 2:      # name:M:k1/k2/..  -> selective compensation at those k
+                ks = [int(v) for v in parts[2].split("/")]
+                r = run_kext(rs, torch, named[name], m, ks, min(args.steps, 100), min(args.warmup, 10))
+                print(json.dumps(r), flush=True)
+                continue
+            r, S2, _ = run_workload(rs, torch, named[name], m, min(args.steps, 100), min(args.warmup, 10))
             del S2
             torch.cuda.empty_cache()
             print(json.dumps({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}), flush=True)
@@ -341,6 +412,10 @@ def main():
             del S2
             torch.cuda.empty_cache()
             sweep.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()})
+        # selective compensation (prefill-sized operands): rho = 0.125, 0.25, 0.5
+        kext = []
+        for w, m in ((inputs.LARGE_MLP, 128), (inputs.MX, 256)):
+            kext.append(run_kext(rs, torch, w, m, inputs.KEXT_K, min(args.steps, 100), min(args.warmup, 10)))
 
     if roof is not None and not args.only_headline:
         rp, which = read_peak_gbps(torch)
@@ -380,6 +455,7 @@ def main():
     line["step_hbm_frac"] = round(head["GBps"] / HBM_PEAK_GBS, 4)
     if sweep:
         line["sweep"] = sweep
+        line["kext"] = kext
     print(json.dumps(line), flush=True)
 
 

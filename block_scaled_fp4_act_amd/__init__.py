@@ -8,7 +8,10 @@ CPU fallback: a missing library raises.
 Names follow the C ABI: ``nvfp4_prepack_weights``, ``nvfp4_quantize_act_with_residue``,
 ``nvfp4_linear``, ``nvfp4_linear_compensated`` and the ``mxfp4_`` twins, plus the
 format-generic ``prepack_weights``, ``quantize_act_with_residue``, ``fp4_linear``
-and ``fp4_linear_compensated``.
+and ``fp4_linear_compensated``.  Selective compensation (K-Ext):
+``channel_abs_sum``, ``kext_select``, ``kext_dim``, ``prepack_weights_kext``,
+``quantize_act_kext`` (and the ``nvfp4_`` / ``mxfp4_`` forms); the product is
+then the plain ``fp4_linear`` over K_eff = kext_dim(K, k).
 """
 import ctypes
 
@@ -168,6 +171,84 @@ def mxfp4_linear(act, w_packed, M, N, K, out=None):
 
 def mxfp4_linear_compensated(act, w_packed, M, N, K, out=None):
     return _linear(act, w_packed, M, N, K, MXFP4, True, out)
+
+
+# ---------------------------------------------------------------- K-Ext --
+
+def kext_dim(K, k):
+    """K_eff = K + (K/8) k (raises for an unsupported K, k)."""
+    ke = int(lib().rsfp4_kext_dim(K, k))
+    if ke < 0:
+        raise ValueError(f"K = {K}, k = {k}: no whole-block extension (see rsfp4_kext_dim)")
+    return ke
+
+
+def channel_abs_sum(x, out=None, accumulate=False):
+    """Per-channel sum of |x| over the rows of x[T, K] in float64 (calibration)."""
+    import torch
+    assert x.is_cuda and x.dim() == 2 and x.is_contiguous()
+    T, K = x.shape
+    if out is None:
+        out = torch.zeros(K, dtype=torch.float64, device=x.device)
+    assert out.dtype == torch.float64 and out.is_contiguous() and out.numel() >= K
+    _check(lib().rsfp4_channel_abs_sum(_ptr(x), _dtype_code(x), T, K, _ptr(out), 1 if accumulate else 0,
+                                       _stream(x)))
+    return out
+
+
+def kext_select(score, k, out=None):
+    """K/8 mask bytes: the k best channels of every group of 8."""
+    import torch
+    assert score.is_cuda and score.dtype == torch.float64 and score.is_contiguous()
+    K = score.numel()
+    if out is None:
+        out = torch.empty(K // 8, dtype=torch.uint8, device=score.device)
+    _check(lib().rsfp4_kext_select(_ptr(score), K, int(k), _ptr(out), _stream(score)))
+    return out
+
+
+def prepack_weights_kext(W, fmt, masks, k, out=None):
+    """Pack [W | W_S] (width K_eff) into a blob for the plain linear."""
+    import torch
+    fmt = _fmt(fmt)
+    assert W.is_cuda and W.dim() == 2 and W.is_contiguous() and masks.is_cuda and masks.dtype == torch.uint8
+    N, K = W.shape
+    nbytes = packed_weight_bytes(fmt, N, kext_dim(K, k))
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=W.device)
+    fn = getattr(lib(), f"rsfp4_{_FMT_NAME[fmt]}_prepack_weights_kext")
+    _check(fn(_ptr(W), _dtype_code(W), N, K, _ptr(masks), int(k), _ptr(out), out.numel(), _stream(W)))
+    return out
+
+
+def quantize_act_kext(x, fmt, masks, k, out=None):
+    """Quantize x[M, K] into M records of width K_eff (base + selected residues)."""
+    import torch
+    fmt = _fmt(fmt)
+    assert x.is_cuda and x.dim() == 2 and x.is_contiguous() and masks.is_cuda and masks.dtype == torch.uint8
+    M, K = x.shape
+    nbytes = packed_act_bytes(fmt, M, kext_dim(K, k), False)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+    fn = getattr(lib(), f"rsfp4_{_FMT_NAME[fmt]}_quantize_act_kext")
+    _check(fn(_ptr(x), _dtype_code(x), M, K, _ptr(masks), int(k), _ptr(out), out.numel(), _stream(x)))
+    return out
+
+
+def nvfp4_prepack_weights_kext(W, masks, k, out=None):
+    return prepack_weights_kext(W, NVFP4, masks, k, out)
+
+
+def mxfp4_prepack_weights_kext(W, masks, k, out=None):
+    return prepack_weights_kext(W, MXFP4, masks, k, out)
+
+
+def nvfp4_quantize_act_kext(x, masks, k, out=None):
+    return quantize_act_kext(x, NVFP4, masks, k, out)
+
+
+def mxfp4_quantize_act_kext(x, masks, k, out=None):
+    return quantize_act_kext(x, MXFP4, masks, k, out)
 
 
 # ------------------------------------------------------------ test/debug --

@@ -1,6 +1,6 @@
 // api.cpp -- the C ABI: host-side validation, size queries and dispatch.
 // Nothing here computes on the host; every step of the path runs in the
-// kernels of quant.hip, prepack.hip and gemm.hip.
+// kernels of quant.hip, prepack.hip, calib.hip, gemm.hip and gemm_tile.hip.
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -36,6 +36,9 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 constexpr int kMaxDevices = 64;
 constexpr int64_t kNarrowRows = 32;   // tile rows (base + residue) the narrow-M kernel handles
+constexpr int64_t kMaxNarrowK = 16384; // K of one narrow-M launch (16 waves x 8 steps)
+constexpr int64_t kMaxLinearK = 32768;
+constexpr int64_t kMaxQuantK = 32768;
 std::once_flag g_cu_once[kMaxDevices];
 int g_cus[kMaxDevices];
 
@@ -86,7 +89,7 @@ rsfp4_status quantize(int fmt, const void* x, int xt, int64_t M, int64_t K, int 
     if (!x || !act) return fail(RSFP4_ERR_NULL, "x and act must be non-NULL");
     if (xt != RSFP4_F32 && xt != RSFP4_BF16) return fail(RSFP4_ERR_FORMAT, "unknown activation dtype %d", xt);
     if (M < 1 || M > 65535) return fail(RSFP4_ERR_SHAPE, "M = %lld outside [1, 65535]", (long long)M);
-    if (K > 32768) return fail(RSFP4_ERR_SHAPE, "quantize needs K <= 32768 (K = %lld)", (long long)K);
+    if (K > kMaxQuantK) return fail(RSFP4_ERR_SHAPE, "quantize needs K <= 32768 (K = %lld)", (long long)K);
     if (!aligned(x, 16) || !aligned(act, 16)) return fail(RSFP4_ERR_ALIGN, "x and act must be 16-byte aligned");
     const size_t need = (size_t)act_row_bytes(fmt, K) * (size_t)(with_res ? 2 * M : M);
     if (bytes < need) return fail(RSFP4_ERR_BUFFER_TOO_SMALL, "act holds %zu bytes, needs %zu", bytes, need);
@@ -106,7 +109,8 @@ rsfp4_status linear(int fmt, bool comp, const void* act, size_t act_bytes, const
     if (!act || !w_packed || !y) return fail(RSFP4_ERR_NULL, "act, w_packed and y must be non-NULL");
     if (M < 1 || M > 65535) return fail(RSFP4_ERR_SHAPE, "M = %lld outside [1, 65535]", (long long)M);
     if (N < 1 || N > (int64_t)1 << 24) return fail(RSFP4_ERR_SHAPE, "N = %lld outside [1, 2^24]", (long long)N);
-    if (K > 16384) return fail(RSFP4_ERR_UNSUPPORTED, "the linear supports K <= 16384 (K = %lld)", (long long)K);
+    if (K > kMaxLinearK) return fail(RSFP4_ERR_UNSUPPORTED, "the linear supports K <= %lld (K = %lld)",
+                                     (long long)kMaxLinearK, (long long)K);
     const int64_t B = comp ? 2 * M : M;
     if (!aligned(act, 16) || !aligned(w_packed, 256) || !aligned(y, 4))
         return fail(RSFP4_ERR_ALIGN, "act must be 16-, w_packed 256- and y 4-byte aligned");
@@ -115,7 +119,12 @@ rsfp4_status linear(int fmt, bool comp, const void* act, size_t act_bytes, const
     if (act_bytes < need_a) return fail(RSFP4_ERR_BUFFER_TOO_SMALL, "act holds %zu bytes, needs %zu", act_bytes, need_a);
     const size_t need_w = (size_t)packed_weight_bytes(fmt, N, K);
     if (w_bytes < need_w) return fail(RSFP4_ERR_BUFFER_TOO_SMALL, "w_packed holds %zu bytes, needs %zu", w_bytes, need_w);
+    // The tiled kernel addresses the activation operand with 32-bit offsets
+    // below its out-of-range marker 2^31.
     if (B > kNarrowRows) {
+        if ((int64_t)rb * B >= ((int64_t)1 << 31))
+            return fail(RSFP4_ERR_UNSUPPORTED, "activation operand of %lld bytes: the linear needs < 2^31",
+                        (long long)((int64_t)rb * B));
         if (std::getenv("RSFP4_LOG"))
             std::fprintf(stderr, "[rsfp4] linear fmt=%d comp=%d M=%lld N=%lld K=%lld tiled\n", fmt, (int)comp,
                          (long long)M, (long long)N, (long long)K);
@@ -125,14 +134,82 @@ rsfp4_status linear(int fmt, bool comp, const void* act, size_t act_bytes, const
     int cus = 0;
     st = num_cus(&cus);
     if (st != RSFP4_OK) return st;
-    const GemmPlan pl = plan_gemm_small(M, N, K, comp, cus);
-    if (std::getenv("RSFP4_LOG"))
-        std::fprintf(stderr, "[rsfp4] linear fmt=%d comp=%d M=%lld N=%lld K=%lld rt=%d maxs=%d kw=%d grid=%lld ngl=%d\n",
-                     fmt, (int)comp, (long long)M, (long long)N, (long long)K, pl.rt, pl.maxs, pl.kw,
-                     (long long)pl.grid, pl.ngl);
-    return hip_status(launch_gemm_small(fmt, pl, comp, act, rb,
-                                        w_packed, (int)M, N, K, y, (hipStream_t)stream),
-                      "linear launch");
+    // one launch covers up to kMaxNarrowK; a longer K takes two launches over
+    // consecutive step ranges (the first a multiple of 8 steps), the second
+    // adding its part to y
+    const int S = (int)num_steps(K);
+    const int split = K > kMaxNarrowK ? 8 * ((S + 15) / 16) : S;
+    for (int pass = 0; pass < (split < S ? 2 : 1); ++pass) {
+        const int s_lo = pass ? split : 0, s_hi = pass ? S : split;
+        const GemmPlan pl = plan_gemm_small(M, N, s_hi - s_lo, comp, cus);
+        if (std::getenv("RSFP4_LOG"))
+            std::fprintf(stderr, "[rsfp4] linear fmt=%d comp=%d M=%lld N=%lld K=%lld steps=[%d,%d) rt=%d maxs=%d "
+                         "kw=%d grid=%lld ngl=%d\n", fmt, (int)comp, (long long)M, (long long)N, (long long)K,
+                         s_lo, s_hi, pl.rt, pl.maxs, pl.kw, (long long)pl.grid, pl.ngl);
+        st = hip_status(launch_gemm_small(fmt, pl, comp, act, rb, w_packed, (int)M, N, K, y, s_lo, s_hi,
+                                          pass == 1, (hipStream_t)stream),
+                        "linear launch");
+        if (st != RSFP4_OK) return st;
+    }
+    return RSFP4_OK;
+}
+
+// ---- selective compensation (K-Ext) ----
+// Extended width K + (K/8) k, or -1: k in {1, 2, 4, 8}, K a multiple of 32, and
+// an extension of whole 32-element runs (so its blocks are whole in both formats).
+int64_t kext_dim(int64_t K, int k) {
+    if (k != 1 && k != 2 && k != 4 && k != 8) return -1;
+    if (K < 32 || K % 32 != 0) return -1;
+    const int64_t ext = (K / 8) * k;
+    if (ext % 32 != 0) return -1;
+    return K + ext;
+}
+
+rsfp4_status check_kext(int fmt, int64_t K, int k, int64_t* KE) {
+    if (fmt != RSFP4_NVFP4 && fmt != RSFP4_MXFP4) return fail(RSFP4_ERR_FORMAT, "unknown format %d", fmt);
+    if (k != 1 && k != 2 && k != 4 && k != 8)
+        return fail(RSFP4_ERR_SHAPE, "k = %d: channels per 8-group must be 1, 2, 4 or 8", k);
+    *KE = kext_dim(K, k);
+    if (*KE < 0)
+        return fail(RSFP4_ERR_SHAPE, "K = %lld with k = %d: K must be a multiple of 32 and K*k/8 of 32",
+                    (long long)K, k);
+    return RSFP4_OK;
+}
+
+rsfp4_status prepack_kext(int fmt, const void* W, int wt, int64_t N, int64_t K, const uint8_t* masks, int k,
+                          void* w_packed, size_t bytes, void* stream) {
+    g_err[0] = 0;
+    int64_t KE = 0;
+    rsfp4_status st = check_kext(fmt, K, k, &KE);
+    if (st != RSFP4_OK) return st;
+    if (!W || !w_packed || !masks) return fail(RSFP4_ERR_NULL, "W, masks and w_packed must be non-NULL");
+    if (wt != RSFP4_F32 && wt != RSFP4_BF16) return fail(RSFP4_ERR_FORMAT, "unknown weight dtype %d", wt);
+    if (N < 1 || N > (int64_t)1 << 24) return fail(RSFP4_ERR_SHAPE, "N = %lld outside [1, 2^24]", (long long)N);
+    if (KE > (int64_t)1 << 20) return fail(RSFP4_ERR_SHAPE, "K_eff = %lld above 2^20", (long long)KE);
+    if (!aligned(w_packed, 256)) return fail(RSFP4_ERR_ALIGN, "w_packed must be 256-byte aligned");
+    if (!aligned(W, 16)) return fail(RSFP4_ERR_ALIGN, "W must be 16-byte aligned");
+    const size_t need = (size_t)packed_weight_bytes(fmt, N, KE);
+    if (bytes < need) return fail(RSFP4_ERR_BUFFER_TOO_SMALL, "w_packed holds %zu bytes, needs %zu", bytes, need);
+    return hip_status(launch_prepack_kext(fmt, wt == RSFP4_BF16, W, N, K, masks, k, w_packed, (hipStream_t)stream),
+                      "prepack launch");
+}
+
+rsfp4_status quantize_kext(int fmt, const void* x, int xt, int64_t M, int64_t K, const uint8_t* masks, int k,
+                           void* act, size_t bytes, void* stream) {
+    g_err[0] = 0;
+    int64_t KE = 0;
+    rsfp4_status st = check_kext(fmt, K, k, &KE);
+    if (st != RSFP4_OK) return st;
+    if (!x || !act || !masks) return fail(RSFP4_ERR_NULL, "x, masks and act must be non-NULL");
+    if (xt != RSFP4_F32 && xt != RSFP4_BF16) return fail(RSFP4_ERR_FORMAT, "unknown activation dtype %d", xt);
+    if (M < 1 || M > 65535) return fail(RSFP4_ERR_SHAPE, "M = %lld outside [1, 65535]", (long long)M);
+    if (KE > kMaxQuantK) return fail(RSFP4_ERR_SHAPE, "K_eff = %lld above 32768", (long long)KE);
+    if (!aligned(x, 16) || !aligned(act, 16)) return fail(RSFP4_ERR_ALIGN, "x and act must be 16-byte aligned");
+    const size_t need = (size_t)act_row_bytes(fmt, KE) * (size_t)M;
+    if (bytes < need) return fail(RSFP4_ERR_BUFFER_TOO_SMALL, "act holds %zu bytes, needs %zu", bytes, need);
+    return hip_status(launch_quantize_act_kext(fmt, xt == RSFP4_BF16, x, (int)M, K, masks, k, act,
+                                               (hipStream_t)stream),
+                      "quantize launch");
 }
 
 }  // namespace
@@ -230,6 +307,52 @@ rsfp4_status rsfp4_unpack_weights_canonical(const void* w_packed, size_t w_packe
     const size_t need = (size_t)packed_weight_bytes(fmt, N, K);
     if (w_packed_bytes < need) return fail(RSFP4_ERR_BUFFER_TOO_SMALL, "w_packed holds %zu bytes, needs %zu", w_packed_bytes, need);
     return hip_status(launch_unpack(fmt, w_packed, N, K, codes, scales, s_g, (hipStream_t)stream), "unpack launch");
+}
+
+int64_t rsfp4_kext_dim(int64_t K, int k) { return kext_dim(K, k); }
+
+rsfp4_status rsfp4_channel_abs_sum(const void* x, int xt, int64_t T, int64_t K, double* sum, int accumulate,
+                                   void* stream) {
+    g_err[0] = 0;
+    if (!x || !sum) return fail(RSFP4_ERR_NULL, "x and sum must be non-NULL");
+    if (xt != RSFP4_F32 && xt != RSFP4_BF16) return fail(RSFP4_ERR_FORMAT, "unknown activation dtype %d", xt);
+    if (T < 1 || K < 1 || K > (int64_t)1 << 24 || T > ((int64_t)1 << 40) / K)
+        return fail(RSFP4_ERR_SHAPE, "T = %lld, K = %lld outside T >= 1, 1 <= K <= 2^24, T*K <= 2^40",
+                    (long long)T, (long long)K);
+    if (!aligned(sum, 8) || !aligned(x, xt == RSFP4_BF16 ? 2 : 4))
+        return fail(RSFP4_ERR_ALIGN, "sum must be 8-byte and x element aligned");
+    return hip_status(launch_channel_abs_sum(xt == RSFP4_BF16, x, T, K, sum, accumulate ? 1 : 0,
+                                             (hipStream_t)stream),
+                      "channel sum launch");
+}
+
+rsfp4_status rsfp4_kext_select(const double* score, int64_t K, int k, uint8_t* masks, void* stream) {
+    g_err[0] = 0;
+    if (!score || !masks) return fail(RSFP4_ERR_NULL, "score and masks must be non-NULL");
+    if (k != 1 && k != 2 && k != 4 && k != 8)
+        return fail(RSFP4_ERR_SHAPE, "k = %d: channels per 8-group must be 1, 2, 4 or 8", k);
+    if (K < 8 || K % 8 != 0 || K > (int64_t)1 << 24)
+        return fail(RSFP4_ERR_SHAPE, "K = %lld must be a multiple of 8 in [8, 2^24]", (long long)K);
+    if (!aligned(score, 8)) return fail(RSFP4_ERR_ALIGN, "score must be 8-byte aligned");
+    return hip_status(launch_kext_select(score, K, k, masks, (hipStream_t)stream), "select launch");
+}
+
+rsfp4_status rsfp4_nvfp4_prepack_weights_kext(const void* W, int wt, int64_t N, int64_t K, const uint8_t* masks,
+                                              int k, void* w_packed, size_t w_packed_bytes, void* stream) {
+    return prepack_kext(RSFP4_NVFP4, W, wt, N, K, masks, k, w_packed, w_packed_bytes, stream);
+}
+rsfp4_status rsfp4_mxfp4_prepack_weights_kext(const void* W, int wt, int64_t N, int64_t K, const uint8_t* masks,
+                                              int k, void* w_packed, size_t w_packed_bytes, void* stream) {
+    return prepack_kext(RSFP4_MXFP4, W, wt, N, K, masks, k, w_packed, w_packed_bytes, stream);
+}
+
+rsfp4_status rsfp4_nvfp4_quantize_act_kext(const void* x, int xt, int64_t M, int64_t K, const uint8_t* masks,
+                                           int k, void* act, size_t act_bytes, void* stream) {
+    return quantize_kext(RSFP4_NVFP4, x, xt, M, K, masks, k, act, act_bytes, stream);
+}
+rsfp4_status rsfp4_mxfp4_quantize_act_kext(const void* x, int xt, int64_t M, int64_t K, const uint8_t* masks,
+                                           int k, void* act, size_t act_bytes, void* stream) {
+    return quantize_kext(RSFP4_MXFP4, x, xt, M, K, masks, k, act, act_bytes, stream);
 }
 
 }  // extern "C"

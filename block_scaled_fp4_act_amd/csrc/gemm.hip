@@ -12,7 +12,9 @@
 // thread-local fp32 add before the only store (the idea of the row-pair packing
 // of Figure 5, realised with MFMA lane ownership instead of TMEM loads).
 //
-// Work decomposition (one design for all M <= 16, i.e. B <= 32):
+// Work decomposition (one design for all M <= 16, i.e. B <= 32; one launch
+// covers up to 16 waves x 8 steps = 16384 elements of K, and longer K runs as
+// two launches over consecutive step ranges, the second adding to y):
 //   * a workgroup owns groups of 16 output channels (grid-stride over groups)
 //     and KW waves that split K: wave w owns steps [w*MAXS, w*MAXS + MAXS) of
 //     128 elements (MAXS a power of two, so a wave's steps sit inside one
@@ -144,6 +146,9 @@ struct GemmArgs {
     int64_t K;
     float* y;
     int ngl;          // LDS slots for partial sums (groups in flight per workgroup)
+    int s_lo;         // first K step of this launch (wave w owns s_lo + w*MAXS ..)
+    int64_t k_hi;     // K elements at or past k_hi are left to another launch
+    int accum;        // add to y instead of overwriting it
 };
 
 // APRE: the activation fragments are dequantized to f16 once, before the
@@ -172,8 +177,7 @@ __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmArgs p) {
     const int wave = threadIdx.x >> 6;
     const int KW = blockDim.x >> 6;
     const int g = lane >> 4, i = lane & 15;
-    const int64_t S = num_steps(p.K);
-    const int s0 = wave * MAXS;                   // this wave's first step
+    const int s0 = p.s_lo + wave * MAXS;          // this wave's first step
     const int64_t G = num_groups(p.N);
     const int64_t GB = group_bytes(FMT, p.K);
     const uint32_t scale_base = (uint32_t)(kActHead + p.K / 2);
@@ -239,7 +243,7 @@ __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmArgs p) {
 #pragma unroll
         for (int t = 0; t < MAXS; ++t) {
             const int64_t k0 = kStepK * (s0 + t) + 32 * g;
-            const bool in = rvalid && k0 < p.K;   // else: out of range -> zeros
+            const bool in = rvalid && k0 < p.k_hi;   // else: out of range -> zeros
             const uint32_t rec = in ? (uint32_t)(arow * p.row_bytes) : act_bytes;
             a_raw[rt][t] = ld128(ra, in ? rec + (uint32_t)(kActHead + k0 / 2) : act_bytes);
             if (FMT == kNV)
@@ -298,6 +302,7 @@ __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmArgs p) {
                         } else {
                             out = v0 + v1;
                         }
+                        if (p.accum) out += p.y[(int64_t)m * p.N + n];
                         p.y[(int64_t)m * p.N + n] = out;
                     }
                 } else {
@@ -309,6 +314,7 @@ __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmArgs p) {
                             float out = v;
                             if (FMT == kNV)
                                 out = s_gw * (*reinterpret_cast<const float*>(p.act + (int64_t)m * p.row_bytes) * v);
+                            if (p.accum) out += p.y[(int64_t)m * p.N + n];
                             p.y[(int64_t)m * p.N + n] = out;
                         }
                     }
@@ -505,9 +511,8 @@ hipError_t launch_fmt(const GemmArgs& a, int rt, bool comp, int maxs, int KW, in
 
 }  // namespace
 
-GemmPlan plan_gemm_small(int64_t M, int64_t N, int64_t K, bool comp, int num_cus) {
+GemmPlan plan_gemm_small(int64_t M, int64_t N, int64_t S, bool comp, int num_cus) {
     GemmPlan pl;
-    const int64_t S = num_steps(K);
     const int64_t B = comp ? 2 * M : M;
     pl.rt = B <= 16 ? 1 : 2;
     // the fewest steps per wave (a power of two) that covers K with <= 16 waves
@@ -528,9 +533,10 @@ GemmPlan plan_gemm_small(int64_t M, int64_t N, int64_t K, bool comp, int num_cus
 
 hipError_t launch_gemm_small(int fmt, const GemmPlan& pl, bool comp, const void* act,
                              int64_t row_bytes, const void* blob, int M, int64_t N, int64_t K,
-                             float* y, hipStream_t s) {
+                             float* y, int s_lo, int s_hi, bool accum, hipStream_t s) {
+    const int64_t k_hi = (int64_t)s_hi * kStepK < K ? (int64_t)s_hi * kStepK : K;
     GemmArgs a{static_cast<const uint8_t*>(act), row_bytes, static_cast<const uint8_t*>(blob), M,
-               N, K, y, pl.ngl};
+               N, K, y, pl.ngl, s_lo, k_hi, accum ? 1 : 0};
     const bool single = num_groups(N) <= pl.grid;             // one group per workgroup
     if (fmt == kNV) return launch_fmt<kNV>(a, pl.rt, comp, pl.maxs, pl.kw, pl.grid, s, single);
     return launch_fmt<kMX>(a, pl.rt, comp, pl.maxs, pl.kw, pl.grid, s, single);

@@ -11,6 +11,16 @@ hipError_t launch_quantize_act(int fmt, int xt_bf16, const void* x, int M, int64
 hipError_t launch_prepack(int fmt, int wt_bf16, const void* W, int64_t N, int64_t K, void* blob,
                           hipStream_t s);
 
+// Selective compensation (K-Ext): extended quantizer, [W | W_S] prepack and the
+// calibration kernels.
+hipError_t launch_quantize_act_kext(int fmt, int xt_bf16, const void* x, int M, int64_t K,
+                                    const uint8_t* masks, int k, void* act, hipStream_t s);
+hipError_t launch_prepack_kext(int fmt, int wt_bf16, const void* W, int64_t N, int64_t Kb,
+                               const uint8_t* masks, int k, void* blob, hipStream_t s);
+hipError_t launch_channel_abs_sum(int xt_bf16, const void* x, int64_t T, int64_t K, double* sum,
+                                  int accumulate, hipStream_t s);
+hipError_t launch_kext_select(const double* score, int64_t K, int k, uint8_t* masks, hipStream_t s);
+
 hipError_t launch_unpack(int fmt, const void* blob, int64_t N, int64_t K, uint8_t* codes,
                          uint8_t* scales, float* s_g, hipStream_t s);
 
@@ -24,11 +34,14 @@ struct GemmPlan {
     int ngl = 1;       // groups reduced together (partial sums held in LDS)
 };
 
-GemmPlan plan_gemm_small(int64_t M, int64_t N, int64_t K, bool comp, int num_cus);
+// Plan for a launch over `steps` K steps of 128 (at most 128 steps).
+GemmPlan plan_gemm_small(int64_t M, int64_t N, int64_t steps, bool comp, int num_cus);
 
+// One launch over steps [s_lo, s_hi) of K (s_lo a multiple of 8); accum adds
+// the result to y (the second launch of a K longer than one launch covers).
 hipError_t launch_gemm_small(int fmt, const GemmPlan& pl, bool comp, const void* act,
                              int64_t row_bytes, const void* blob, int M, int64_t N, int64_t K,
-                             float* y, hipStream_t s);
+                             float* y, int s_lo, int s_hi, bool accum, hipStream_t s);
 
 // Wide-operand linear (any number of activation rows): 2-D tiles of 128 rows x
 // 128 channels per workgroup, each wave walking all of K.

@@ -9,7 +9,9 @@
 // atomicMax on the binary32 bits, which orders like the values for x >= 0, so
 // the result does not depend on the order of arrival), and the pack kernel in
 // which each thread quantizes one 16-element slice of one channel and writes its
-// 8 code bytes and its scale byte straight to their tiled positions.
+// 8 code bytes and its scale byte straight to their tiled positions.  The
+// selective-compensation variant packs [W | W_S] the same way, reading the
+// extension slices through the channel masks.
 #include <hip/hip_runtime.h>
 #include <hip/hip_bf16.h>
 #include <stdint.h>
@@ -80,9 +82,21 @@ __device__ __forceinline__ int64_t scale_off(int fmt, int64_t K, int64_t n, int6
 // slices are channel-major so slices 2t and 2t+1 of a channel sit in lanes 2u,
 // 2u+1).  Slices of the padding steps of the last quad write zero codes and
 // zero scales, so every byte a wave may load is defined.
+// Selective compensation (ResServe Section 5.3, Eq. 6): the packed operand is
+// [W | W_S], K = Kb + (Kb/8) k columns; column Kb + p is W's column of the
+// (p % k)-th selected channel of group p / k (lowest channel first).  A mask
+// byte with fewer than k bits falls back to the group's channel 7, in bounds.
+__device__ __forceinline__ int64_t ext_column(const uint8_t* masks, int ks, int64_t p) {
+    const int64_t g = p / ks;
+    uint32_t rest = masks[g];
+    for (int q = (int)(p % ks); q > 0; --q) rest &= rest - 1u;
+    return 8 * g + (rest ? __builtin_ctz(rest) : 7);
+}
+
 template <int FMT, typename T>
 __global__ __launch_bounds__(256) void prepack_kernel(const T* __restrict__ W, int64_t N, int64_t K,
-                                                      uint8_t* __restrict__ blob) {
+                                                      uint8_t* __restrict__ blob, int64_t Kb,
+                                                      const uint8_t* __restrict__ masks, int ks) {
     const WHeader* h = reinterpret_cast<const WHeader*>(blob);
     const int64_t S = num_steps(K);
     const int64_t S_pad = (S + kQuadSteps - 1) / kQuadSteps * kQuadSteps;
@@ -95,9 +109,16 @@ __global__ __launch_bounds__(256) void prepack_kernel(const T* __restrict__ W, i
     const int64_t k0 = 16 * j;
     const bool real = live && n < N && k0 < K;   // K % 32 == 0: a slice is all in or all out
 
+    // the slice's source columns: W's own for k0 < Kb, selected ones beyond
+    // (Kb % 32 == 0: a 16-slice lies wholly on one side)
     float v[16];
+    if (k0 < Kb || !real) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) v[e] = real ? ld<T>(W, n * K + k0 + e) : 0.0f;
+        for (int e = 0; e < 16; ++e) v[e] = real ? ld<T>(W, n * Kb + k0 + e) : 0.0f;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) v[e] = ld<T>(W, n * Kb + ext_column(masks, ks, k0 + e - Kb));
+    }
     float bm = 0.0f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) bm = fmaxf(bm, fabsf(v[e]));
@@ -148,14 +169,16 @@ __global__ __launch_bounds__(256) void unpack_kernel(const uint8_t* __restrict__
     }
 }
 
+// K: columns of the packed operand; Kb: columns of W (K = Kb unless masks).
 template <int FMT, typename T>
-hipError_t prepack_t(const void* W, int64_t N, int64_t K, void* blob, hipStream_t s) {
+hipError_t prepack_t(const void* W, int64_t N, int64_t K, int64_t Kb, const uint8_t* masks, int ks,
+                     void* blob, hipStream_t s) {
     uint8_t* b = static_cast<uint8_t*>(blob);
     hipLaunchKernelGGL(hdr_init_kernel, dim3(1), dim3(1), 0, s, b, FMT, N, K);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (FMT == kNV) {
-        const int64_t n = N * K;
+        const int64_t n = N * Kb;   // the selected columns repeat W's: same maximum
         int64_t blocks = (n + 255) / 256;
         if (blocks > 4096) blocks = 4096;
         hipLaunchKernelGGL((w_amax_kernel<T>), dim3((unsigned)blocks), dim3(256), 0, s,
@@ -167,7 +190,7 @@ hipError_t prepack_t(const void* W, int64_t N, int64_t K, void* blob, hipStream_
     const int64_t total = num_groups(N) * kGroupN * S_pad * (kStepK / 16);
     const int64_t blocks = (total + 255) / 256;
     hipLaunchKernelGGL((prepack_kernel<FMT, T>), dim3((unsigned)blocks), dim3(256), 0, s,
-                       static_cast<const T*>(W), N, K, b);
+                       static_cast<const T*>(W), N, K, b, Kb, masks, ks);
     return hipGetLastError();
 }
 
@@ -176,10 +199,20 @@ hipError_t prepack_t(const void* W, int64_t N, int64_t K, void* blob, hipStream_
 hipError_t launch_prepack(int fmt, int wt_bf16, const void* W, int64_t N, int64_t K, void* blob,
                           hipStream_t s) {
     if (fmt == kNV)
-        return wt_bf16 ? prepack_t<kNV, __hip_bfloat16>(W, N, K, blob, s)
-                       : prepack_t<kNV, float>(W, N, K, blob, s);
-    return wt_bf16 ? prepack_t<kMX, __hip_bfloat16>(W, N, K, blob, s)
-                   : prepack_t<kMX, float>(W, N, K, blob, s);
+        return wt_bf16 ? prepack_t<kNV, __hip_bfloat16>(W, N, K, K, nullptr, 0, blob, s)
+                       : prepack_t<kNV, float>(W, N, K, K, nullptr, 0, blob, s);
+    return wt_bf16 ? prepack_t<kMX, __hip_bfloat16>(W, N, K, K, nullptr, 0, blob, s)
+                   : prepack_t<kMX, float>(W, N, K, K, nullptr, 0, blob, s);
+}
+
+hipError_t launch_prepack_kext(int fmt, int wt_bf16, const void* W, int64_t N, int64_t Kb,
+                               const uint8_t* masks, int k, void* blob, hipStream_t s) {
+    const int64_t K = Kb + (Kb / 8) * k;
+    if (fmt == kNV)
+        return wt_bf16 ? prepack_t<kNV, __hip_bfloat16>(W, N, K, Kb, masks, k, blob, s)
+                       : prepack_t<kNV, float>(W, N, K, Kb, masks, k, blob, s);
+    return wt_bf16 ? prepack_t<kMX, __hip_bfloat16>(W, N, K, Kb, masks, k, blob, s)
+                   : prepack_t<kMX, float>(W, N, K, Kb, masks, k, blob, s);
 }
 
 hipError_t launch_unpack(int fmt, const void* blob, int64_t N, int64_t K, uint8_t* codes,

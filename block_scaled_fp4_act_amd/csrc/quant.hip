@@ -99,17 +99,41 @@ __device__ __forceinline__ void load_chunk<__hip_bfloat16, 4>(const __hip_bfloat
     v[3] = __uint_as_float(t.y & 0xFFFF0000u);
 }
 
+// Block scale of a block whose largest magnitude is bm: the scale byte and the
+// effective element scale s~ (NVFP4: E4M3_RNE(bm / (6 s_g)) and S_b * s_g;
+// MXFP4: the E8M0 rule and its power of two).
+template <int FMT>
+__device__ __forceinline__ float block_scale(float bm, float s_g, uint32_t& sbyte) {
+    if (FMT == kNV) {
+        sbyte = e4m3_encode(bm / (6.0f * s_g));
+        return e4m3_val(sbyte) * s_g;
+    }
+    sbyte = e8m0_for_amax(bm);
+    return e8m0_val(sbyte);
+}
+
+// Signed E2M1 code of x at element scale st (0 magnitude when st == 0).
+__device__ __forceinline__ uint32_t e2m1_code(float x, float st) {
+    // (st == 0 gives inf or NaN here; the select discards it)
+    const uint32_t mq = e2m1_mag(fabsf(x / st));
+    const uint32_t mag = st != 0.0f ? mq : 0u;
+    return (__float_as_uint(x) >> 28 & 8u) | mag;
+}
+
+// Record header: the row's fp32 tensor scale (0 for MXFP4) and zero padding.
+__device__ __forceinline__ void store_head(uint8_t* rec, float s_g) {
+    if (threadIdx.x == 0) *reinterpret_cast<uint4*>(rec) = make_uint4(__float_as_uint(s_g), 0u, 0u, 0u);
+}
+
 // Quantize the NC chunks of EPT elements held in v[] (in place: v becomes the
-// residue) into the record at rec.  amax is the row maximum; nchunks = K / EPT.
+// residue): chunk j's codes go to codes[j * EPT / 2 ..], its block scale byte
+// to scales[j / lanes-per-block].  s_g is the row's tensor scale (NVFP4);
+// nchunks = K / EPT.
 template <int FMT, int NC, int EPT>
-__device__ __forceinline__ void quantize_chunks(float (&v)[NC][EPT], int nchunks, int64_t K,
-                                                float amax, uint8_t* rec) {
+__device__ __forceinline__ void quantize_chunks(float (&v)[NC][EPT], int nchunks, float s_g,
+                                                uint8_t* codes, uint8_t* scales) {
     constexpr int LPB = (FMT == kNV ? 16 : 32) / EPT;   // lanes sharing one block
     const int tid = threadIdx.x;
-    uint8_t* codes = rec + kActHead;
-    uint8_t* scales = codes + K / 2;
-    const float s_g = (FMT == kNV) ? amax / 2688.0f : 0.0f;
-    if (tid == 0) *reinterpret_cast<uint4*>(rec) = make_uint4(__float_as_uint(s_g), 0u, 0u, 0u);
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
         const int j = tid + (int)blockDim.x * c;     // chunk index
@@ -120,23 +144,13 @@ __device__ __forceinline__ void quantize_chunks(float (&v)[NC][EPT], int nchunks
         if (LPB >= 2) bm = fmaxf(bm, dpp<kDppXor1>(bm));
         if (LPB >= 4) bm = fmaxf(bm, dpp<kDppXor2>(bm));
         if (LPB >= 8) bm = fmaxf(bm, dpp<kDppHalfMirror>(bm));
-        float st;                                    // effective element scale
         uint32_t sbyte;
-        if (FMT == kNV) {
-            sbyte = e4m3_encode(bm / (6.0f * s_g));
-            st = e4m3_val(sbyte) * s_g;
-        } else {
-            sbyte = e8m0_for_amax(bm);
-            st = e8m0_val(sbyte);
-        }
+        const float st = block_scale<FMT>(bm, s_g, sbyte);   // effective element scale
         uint32_t packed = 0u;
 #pragma unroll
         for (int e = 0; e < EPT; ++e) {
             const float x = v[c][e];
-            // (st == 0 gives inf or NaN here; the select below discards it)
-            const uint32_t mq = e2m1_mag(fabsf(x / st));
-            const uint32_t mag = st != 0.0f ? mq : 0u;
-            const uint32_t code = (__float_as_uint(x) >> 28 & 8u) | mag;
+            const uint32_t code = e2m1_code(x, st);
             packed |= code << (4 * e);
             const float d = st * e2m1_val(code);
             v[c][e] = x - d;                          // residue, exact (Sterbenz)
@@ -177,7 +191,10 @@ __global__ __launch_bounds__(kQMaxThreads) void quant_act_kernel(const TIn* __re
         for (int e = 0; e < EPT; ++e) tmax = fmaxf(tmax, fabsf(v[c][e]));
     }
     const float amax = block_max(tmax, red[0]);
-    quantize_chunks<FMT, NC, EPT>(v, nchunks, K, amax, act + (int64_t)m * row_bytes);
+    uint8_t* rec = act + (int64_t)m * row_bytes;
+    const float s_g = FMT == kNV ? amax / 2688.0f : 0.0f;
+    store_head(rec, s_g);
+    quantize_chunks<FMT, NC, EPT>(v, nchunks, s_g, rec + kActHead, rec + kActHead + K / 2);
     if (!with_res) return;
 
     // v now holds the residue (zero in chunks past K): second row statistic.
@@ -187,7 +204,10 @@ __global__ __launch_bounds__(kQMaxThreads) void quant_act_kernel(const TIn* __re
 #pragma unroll
         for (int e = 0; e < EPT; ++e) rmax = fmaxf(rmax, fabsf(v[c][e]));
     const float ramax = block_max(rmax, red[1]);
-    quantize_chunks<FMT, NC, EPT>(v, nchunks, K, ramax, act + (int64_t)(M + m) * row_bytes);
+    uint8_t* rrec = act + (int64_t)(M + m) * row_bytes;
+    const float r_g = FMT == kNV ? ramax / 2688.0f : 0.0f;
+    store_head(rrec, r_g);
+    quantize_chunks<FMT, NC, EPT>(v, nchunks, r_g, rrec + kActHead, rrec + kActHead + K / 2);
 }
 
 template <int FMT, int NC, int EPT, typename TIn>
@@ -217,6 +237,144 @@ hipError_t launch_quant_f(const void* x, int M, int64_t K, int with_res, void* a
     return launch_quant_t<FMT, 4, 8, TIn>(x, M, K, with_res, act, kQMaxThreads, s);
 }
 
+// ---------------------------------------------------------------- K-Ext --
+// Selective compensation (ResServe Section 5.3, Eq. 6; Appendix B.1 and
+// Algorithm 1): the record of row m holds K_eff = K + (K/8) k elements, the base
+// codes of all K channels followed by the extension, the residues of the k
+// channels that mask byte g selects in group g, in increasing channel order,
+// group after group.  One thread owns one 8-channel group (EPT = 8), so its k
+// extension elements are the contiguous run [g k, g k + k); an extension block
+// (16 or 32 elements) spans blk / k adjacent lanes.  Residue blocks take the
+// base row's tensor scale (the algorithm feeds one alpha to both block-scale
+// steps), MXFP4 the E8M0 rule.
+
+__device__ __forceinline__ uint32_t dpp_xor1_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppXor1, 0xF, 0xF, false);
+}
+
+// Maximum over aligned runs of L adjacent lanes (L a power of two <= 32).
+template <int L>
+__device__ __forceinline__ float run_max(float bm) {
+    if (L >= 2) bm = fmaxf(bm, dpp<kDppXor1>(bm));
+    if (L >= 4) bm = fmaxf(bm, dpp<kDppXor2>(bm));
+    if (L >= 8) bm = fmaxf(bm, dpp<kDppHalfMirror>(bm));
+    if (L >= 16) bm = fmaxf(bm, dpp<kDppMirror>(bm));
+    if (L >= 32) bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+    return bm;
+}
+
+template <int FMT, int NC, int KS, typename TIn>
+__global__ __launch_bounds__(kQMaxThreads) void quant_kext_kernel(const TIn* __restrict__ x, int64_t K,
+                                                                  const uint8_t* __restrict__ masks,
+                                                                  uint8_t* __restrict__ act,
+                                                                  int64_t row_bytes) {
+    constexpr int BLK = FMT == kNV ? 16 : 32;
+    constexpr int LPE = BLK / KS;                 // lanes per extension block
+    __shared__ float red[kQMaxThreads / 64];
+    const int m = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int nchunks = (int)(K / 8);
+    const TIn* xr = x + (int64_t)m * K;
+
+    float v[NC][8];
+    uint32_t mk[NC];
+    float tmax = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int j = tid + (int)blockDim.x * c;
+        if (j < nchunks) {
+            load_chunk<TIn, 8>(xr + 8 * (int64_t)j, v[c]);
+            mk[c] = masks[j];
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[c][e] = 0.0f;
+            mk[c] = 0u;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) tmax = fmaxf(tmax, fabsf(v[c][e]));
+    }
+    const float amax = block_max(tmax, red);
+    const int64_t KE = K + (K / 8) * KS;
+    uint8_t* rec = act + (int64_t)m * row_bytes;
+    uint8_t* codes = rec + kActHead;
+    uint8_t* scales = codes + KE / 2;
+    const float s_g = FMT == kNV ? amax / 2688.0f : 0.0f;
+    store_head(rec, s_g);
+    quantize_chunks<FMT, NC, 8>(v, nchunks, s_g, codes, scales);   // v: residue from here on
+
+    uint8_t* ecodes = codes + K / 2;
+    uint8_t* escales = scales + K / BLK;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int j = tid + (int)blockDim.x * c;
+        // the k selected residues of this group, lowest channel first
+        float rs[KS];
+        uint32_t rest = mk[c];
+#pragma unroll
+        for (int q = 0; q < KS; ++q) {
+            if (KS == 8) {
+                rs[q] = v[c][q];
+            } else {
+                // lowest set bit still pending (a byte with fewer than k bits
+                // falls back to channel 7: defined, in-register, no memory access)
+                const int idx = rest ? __builtin_ctz(rest) : 7;
+                float r = v[c][0];
+#pragma unroll
+                for (int e = 1; e < 8; ++e) r = idx == e ? v[c][e] : r;
+                rs[q] = r;
+                rest &= rest - 1u;
+            }
+        }
+        float bm = 0.0f;
+#pragma unroll
+        for (int q = 0; q < KS; ++q) bm = fmaxf(bm, fabsf(rs[q]));
+        bm = run_max<LPE>(bm);
+        uint32_t sbyte;
+        const float st = block_scale<FMT>(bm, s_g, sbyte);
+        uint32_t packed = 0u;
+#pragma unroll
+        for (int q = 0; q < KS; ++q) packed |= e2m1_code(rs[q], st) << (4 * q);
+        uint32_t pair = 0u;
+        if (KS == 1) pair = packed | (dpp_xor1_u32(packed) << 4);   // even lane: its nibble low
+        if (j < nchunks) {
+            if (KS == 8) *reinterpret_cast<uint32_t*>(ecodes + 4 * (int64_t)j) = packed;
+            if (KS == 4) *reinterpret_cast<uint16_t*>(ecodes + 2 * (int64_t)j) = (uint16_t)packed;
+            if (KS == 2) ecodes[j] = (uint8_t)packed;
+            if (KS == 1 && (j & 1) == 0) ecodes[j >> 1] = (uint8_t)pair;
+            if ((j & (LPE - 1)) == 0) escales[j / LPE] = (uint8_t)sbyte;
+        }
+    }
+}
+
+template <int FMT, int NC, int KS, typename TIn>
+hipError_t launch_kext_t(const void* x, int M, int64_t K, const uint8_t* masks, void* act, hipStream_t s) {
+    const int64_t rb = act_row_bytes(FMT, K + (K / 8) * KS);
+    const int64_t nch = K / 8;
+    const int threads = nch >= kQMaxThreads ? kQMaxThreads : (int)((nch + 63) / 64 * 64);
+    hipLaunchKernelGGL((quant_kext_kernel<FMT, NC, KS, TIn>), dim3(M), dim3(threads), 0, s,
+                       static_cast<const TIn*>(x), K, masks, static_cast<uint8_t*>(act), rb);
+    return hipGetLastError();
+}
+
+template <int FMT, int KS, typename TIn>
+hipError_t launch_kext_nc(const void* x, int M, int64_t K, const uint8_t* masks, void* act, hipStream_t s) {
+    const int64_t nch = K / 8;
+    if (nch <= kQMaxThreads) return launch_kext_t<FMT, 1, KS, TIn>(x, M, K, masks, act, s);
+    if (nch <= 2 * kQMaxThreads) return launch_kext_t<FMT, 2, KS, TIn>(x, M, K, masks, act, s);
+    return launch_kext_t<FMT, 4, KS, TIn>(x, M, K, masks, act, s);
+}
+
+template <int FMT, typename TIn>
+hipError_t launch_kext_f(const void* x, int M, int64_t K, const uint8_t* masks, int k, void* act,
+                         hipStream_t s) {
+    switch (k) {
+        case 1: return launch_kext_nc<FMT, 1, TIn>(x, M, K, masks, act, s);
+        case 2: return launch_kext_nc<FMT, 2, TIn>(x, M, K, masks, act, s);
+        case 4: return launch_kext_nc<FMT, 4, TIn>(x, M, K, masks, act, s);
+        default: return launch_kext_nc<FMT, 8, TIn>(x, M, K, masks, act, s);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_quantize_act(int fmt, int xt_bf16, const void* x, int M, int64_t K, int with_res,
@@ -227,6 +385,15 @@ hipError_t launch_quantize_act(int fmt, int xt_bf16, const void* x, int M, int64
     }
     return xt_bf16 ? launch_quant_f<kMX, __hip_bfloat16>(x, M, K, with_res, act, s)
                    : launch_quant_f<kMX, float>(x, M, K, with_res, act, s);
+}
+
+hipError_t launch_quantize_act_kext(int fmt, int xt_bf16, const void* x, int M, int64_t K,
+                                    const uint8_t* masks, int k, void* act, hipStream_t s) {
+    if (fmt == kNV)
+        return xt_bf16 ? launch_kext_f<kNV, __hip_bfloat16>(x, M, K, masks, k, act, s)
+                       : launch_kext_f<kNV, float>(x, M, K, masks, k, act, s);
+    return xt_bf16 ? launch_kext_f<kMX, __hip_bfloat16>(x, M, K, masks, k, act, s)
+                   : launch_kext_f<kMX, float>(x, M, K, masks, k, act, s);
 }
 
 }  // namespace rsfp4

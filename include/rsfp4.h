@@ -39,8 +39,10 @@
  *     RSFP4_ERR_HIP with the HIP error string in the message.
  *   - Shape limits: M >= 1, N >= 1, K >= 32 and K % 32 == 0 (both formats, so a
  *     K-run of 32 is whole in either block size); M <= 65535; quantize needs
- *     K <= 32768; the linear needs K <= 16384 and N <= 2^24.  Calls outside
- *     these limits return RSFP4_ERR_SHAPE or RSFP4_ERR_UNSUPPORTED.
+ *     K <= 32768; the linear needs K <= 32768 and N <= 2^24, and where it runs
+ *     the tiled kernel (more than 32 operand rows) an activation operand below
+ *     2^31 bytes.  Calls outside these limits return RSFP4_ERR_SHAPE or
+ *     RSFP4_ERR_UNSUPPORTED.
  *   - All calls are thread-safe; concurrent calls on different streams are
  *     independent.
  */
@@ -147,8 +149,11 @@ rsfp4_status rsfp4_mxfp4_quantize_act_with_residue(const void* x, int xt, int64_
  * kernel covers 128 rows x 128 channels per workgroup (each weight tile is then
  * read once per 128 rows).  Either way base and residue products of one token
  * land in the same lane's accumulators and are added there before the single
- * store (ResServe Section 4.3, Eq. 2 and Section 5.1, Eq. 4).  act_bytes and
- * w_packed_bytes are checked against the size queries. */
+ * store (ResServe Section 4.3, Eq. 2 and Section 5.1, Eq. 4).  With up to 32
+ * rows and K above 16384 the narrow kernel runs twice, over the two halves of
+ * the K steps, the second launch adding its part to y (so y is written, read
+ * back and written again).  act_bytes and w_packed_bytes are checked against
+ * the size queries. */
 rsfp4_status rsfp4_nvfp4_linear(const void* act, size_t act_bytes, const void* w_packed,
                                 size_t w_packed_bytes, int64_t M, int64_t N, int64_t K,
                                 float* y, void* ws, size_t ws_bytes, void* stream);
@@ -161,6 +166,74 @@ rsfp4_status rsfp4_mxfp4_linear(const void* act, size_t act_bytes, const void* w
 rsfp4_status rsfp4_mxfp4_linear_compensated(const void* act, size_t act_bytes, const void* w_packed,
                                             size_t w_packed_bytes, int64_t M, int64_t N, int64_t K,
                                             float* y, void* ws, size_t ws_bytes, void* stream);
+
+/* --------------------------------------- selective compensation (K-Ext) --
+ * ResServe Section 5.3 ("Selective Prefill Execution", Eq. 6) and Appendix B.1
+ * (Eq. 7, Algorithm 1): only k of every 8 input channels get a residue term,
+ * k = 8 rho with rho in {0.125, 0.25, 0.5, 1}.  The selected residues are
+ * appended to the quantized activation row and the matching weight columns to
+ * W, so one plain FP4 product over K_eff = K + (K/8) k = K (1 + rho) adds the
+ * base and the correction:  y = [X^ R^_S] [W^ W^_S]^T.
+ *
+ * Channel masks: K/8 bytes (device memory); bit j of byte g selects channel
+ * 8g + j.  Each byte must have exactly k bits set (the select call makes such
+ * masks); another popcount gives unspecified extension values, never an
+ * out-of-bounds access.  Extension order: group after group, each group's
+ * selected channels in increasing channel order.
+ *
+ * Flow: rsfp4_channel_abs_sum over calibration rows -> rsfp4_kext_select ->
+ * masks; offline rsfp4_*_prepack_weights_kext(W, masks) -> a packed blob of
+ * width K_eff; per call rsfp4_*_quantize_act_kext(x, masks) -> M records of
+ * width K_eff, then rsfp4_*_linear(act, blob, M, N, K_eff) (the plain linear:
+ * the sum over K_eff already holds both terms). */
+
+/* K_eff = K + (K/8) k, or -1 unless k is 1, 2, 4 or 8, K a multiple of 32 and
+ * (K/8) k a multiple of 32 (so the extension is whole blocks in both formats:
+ * K % 256 == 0 for k = 1, % 128 for k = 2, % 64 for k = 4). */
+int64_t rsfp4_kext_dim(int64_t K, int k);
+
+/* Calibration score (Appendix B.1: mean absolute activation; a sum over a fixed
+ * number of rows ranks channels the same way): sum[i] = (accumulate ? sum[i] :
+ * 0) + |x[0, i]| + |x[1, i]| + ... + |x[T-1, i]|, added in binary64 one row
+ * after another, so continuing over several batches equals one call over their
+ * concatenation.  x [T, K] row-major (xt: RSFP4_F32 or RSFP4_BF16, element
+ * aligned); sum: K doubles (device, 8-byte aligned).  T*K <= 2^40. */
+rsfp4_status rsfp4_channel_abs_sum(const void* x, int xt, int64_t T, int64_t K, double* sum,
+                                   int accumulate, void* stream);
+
+/* Block-local selection (Eq. 7): masks[g] gets the k channels of group g with
+ * the largest score; equal scores go to the lower channel index.  score: K
+ * doubles (device), K % 8 == 0; masks: K/8 bytes (device).  NaN scores give
+ * unspecified masks. */
+rsfp4_status rsfp4_kext_select(const double* score, int64_t K, int k, uint8_t* masks, void* stream);
+
+/* Pack [W | W_S] (W [N, K] row-major, dtype wt) into a blob of width K_eff
+ * (w_packed_bytes >= rsfp4_packed_weight_bytes(fmt, N, K_eff), 256-byte
+ * aligned).  Column K + p is W's column of the extension's p-th channel.  The
+ * blob is quantized as one K_eff-wide tensor (Section 5.3: the selected rows
+ * are appended offline and quantized in the extended block layout): NVFP4's
+ * tensor scale is max|W| / 2688 (the appended columns repeat W's values), and
+ * the blocks of the extension are new blocks over the gathered columns. */
+rsfp4_status rsfp4_nvfp4_prepack_weights_kext(const void* W, int wt, int64_t N, int64_t K,
+                                              const uint8_t* masks, int k, void* w_packed,
+                                              size_t w_packed_bytes, void* stream);
+rsfp4_status rsfp4_mxfp4_prepack_weights_kext(const void* W, int wt, int64_t N, int64_t K,
+                                              const uint8_t* masks, int k, void* w_packed,
+                                              size_t w_packed_bytes, void* stream);
+
+/* Quantize x [M, K] into M activation records of width K_eff (act_bytes >=
+ * rsfp4_packed_act_bytes(fmt, M, K_eff, 0); record layout as above with K_eff
+ * in place of K).  One pass per row, x read once (Algorithm 1): row amax and
+ * tensor scale s_g, base codes of all K channels, the residue r = x - deq(q(x))
+ * in registers, then the selected residues quantized in their own blocks of
+ * the extension -- NVFP4 with the base row's s_g (the one tensor scale of the
+ * extended row), MXFP4 with the E8M0 rule.  K_eff <= 32768. */
+rsfp4_status rsfp4_nvfp4_quantize_act_kext(const void* x, int xt, int64_t M, int64_t K,
+                                           const uint8_t* masks, int k, void* act, size_t act_bytes,
+                                           void* stream);
+rsfp4_status rsfp4_mxfp4_quantize_act_kext(const void* x, int xt, int64_t M, int64_t K,
+                                           const uint8_t* masks, int k, void* act, size_t act_bytes,
+                                           void* stream);
 
 /* ------------------------------------------------------- test / debug ----
  * Rewrite a packed blob in canonical row-major form: codes[N, K/2] (low nibble

@@ -70,7 +70,11 @@ def test_validation_errors_without_device():
     assert L.rsfp4_nvfp4_linear(FAKE, 1 << 20, FAKE, 1 << 20, 1, 16, 100, FAKE, None, 0, None) == 2
     assert L.rsfp4_mxfp4_quantize_act_with_residue(FAKE, 0, 1, 48, 1, FAKE, 1 << 20, None) == 2
     # K above the linear's limit, M outside [1, 65535]
-    assert L.rsfp4_nvfp4_linear(FAKE, 1 << 30, FAKE, 1 << 30, 1, 16, 16416, FAKE, None, 0, None) == 6
+    assert L.rsfp4_nvfp4_linear(FAKE, 1 << 30, FAKE, 1 << 30, 1, 16, 32800, FAKE, None, 0, None) == 6
+    # the tiled kernel's activation operand must stay below 2^31 bytes
+    big = 1 << 40
+    assert L.rsfp4_nvfp4_linear_compensated(FAKE, big, FAKE, big, 65535, 16, 32768, FAKE, None, 0, None) == 6
+    assert "2^31" in _err()
     assert L.rsfp4_mxfp4_linear_compensated(FAKE, 1 << 30, FAKE, 1 << 30, 65536, 16, 512, FAKE, None, 0, None) == 2
     assert L.rsfp4_mxfp4_linear(FAKE, 1 << 30, FAKE, 1 << 30, 0, 16, 512, FAKE, None, 0, None) == 2
     # a wide operand's buffer is checked like a narrow one's
@@ -108,3 +112,29 @@ def test_product_path_does_not_import_oracle():
                 txt = open(os.path.join(root, f)).read()
                 assert "import oracle" not in txt and "from oracle" not in txt, f
                 assert "rsfp4_oracle" not in txt, f
+
+
+def test_kext_dim_and_validation():
+    L = rs.lib()
+    assert rs.kext_dim(4096, 1) == 4096 + 512
+    assert rs.kext_dim(4096, 2) == 5120 and rs.kext_dim(4096, 4) == 6144 and rs.kext_dim(4096, 8) == 8192
+    assert rs.kext_dim(128, 2) == 160 and rs.kext_dim(64, 4) == 96 and rs.kext_dim(32, 8) == 64
+    for K, k in ((160, 1), (4096, 3), (96, 2), (48, 8), (0, 1)):
+        assert L.rsfp4_kext_dim(K, k) == -1
+        with pytest.raises(ValueError):
+            rs.kext_dim(K, k)
+    # the extended calls check like the plain ones, against K_eff
+    assert L.rsfp4_nvfp4_quantize_act_kext(FAKE, 0, 4, 512, FAKE, 3, FAKE, 1 << 30, None) == 2
+    assert "1, 2, 4 or 8" in _err()
+    assert L.rsfp4_mxfp4_quantize_act_kext(FAKE, 0, 4, 160, FAKE, 1, FAKE, 1 << 30, None) == 2
+    assert L.rsfp4_nvfp4_quantize_act_kext(FAKE, 0, 4, 512, None, 2, FAKE, 1 << 30, None) == 1
+    need = rs.packed_act_bytes(0, 4, 640, False)
+    assert L.rsfp4_nvfp4_quantize_act_kext(FAKE, 0, 4, 512, FAKE, 2, FAKE, need - 1, None) == 5
+    assert L.rsfp4_nvfp4_quantize_act_kext(FAKE, 0, 4, 32768, FAKE, 1, FAKE, 1 << 40, None) == 2
+    wneed = rs.packed_weight_bytes(1, 64, 768)
+    assert L.rsfp4_mxfp4_prepack_weights_kext(FAKE, 0, 64, 512, FAKE, 4, FAKE, wneed - 1, None) == 5
+    assert L.rsfp4_mxfp4_prepack_weights_kext(FAKE, 0, 64, 512, FAKE, 4, ctypes.c_void_p(0x100010), wneed, None) == 3
+    assert L.rsfp4_kext_select(FAKE, 100, 2, FAKE, None) == 2
+    assert L.rsfp4_kext_select(FAKE, 64, 5, FAKE, None) == 2
+    assert L.rsfp4_channel_abs_sum(FAKE, 0, 0, 64, FAKE, 0, None) == 2
+    assert L.rsfp4_channel_abs_sum(FAKE, 0, 4, 64, ctypes.c_void_p(0x100004), 0, None) == 3

@@ -172,6 +172,9 @@ SMALL_CASES = [  # (M, N, K): several tiles, ragged N and K tails, both row-tile
     # row tiles, channel tiles and K tails
     (17, 264, 384), (33, 130, 160), (40, 512, 1056), (64, 128, 256), (100, 72, 2048),
     (129, 300, 512),
+    # K past one narrow launch (two launches over the K steps, the second
+    # adding to y), up to the longest supported K, and a wide operand there
+    (4, 200, 20480), (2, 64, 32768), (40, 64, 24576),
 ]
 
 
@@ -258,7 +261,7 @@ def test_linear_limits_rejected():
     act = torch.zeros(rs.packed_act_bytes(0, 17, 512, True), dtype=torch.uint8, device="cuda")
     blob = torch.zeros(rs.packed_weight_bytes(0, 64, 512), dtype=torch.uint8, device="cuda")
     with pytest.raises(RuntimeError, match="unsupported"):
-        rs.fp4_linear_compensated(act, blob, 1, 64, 16416, 0)
+        rs.fp4_linear_compensated(act, blob, 1, 64, 32800, 0)
     with pytest.raises(RuntimeError, match="outside"):
         rs.fp4_linear_compensated(act, blob, 65536, 64, 512, 0)
     with pytest.raises(RuntimeError, match="too small"):
