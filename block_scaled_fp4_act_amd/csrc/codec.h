@@ -63,6 +63,28 @@ __device__ __forceinline__ uint32_t e4m3_encode(float t) {
     return t > 0.0f ? code : 0u;                                          // NaN and <= 0 -> 0
 }
 
+// gfx950 conversions between fp32 and E2M1 (v_cvt_scalef32_pk_fp4_f32 and
+// v_cvt_scalef32_pk_f32_fp4).  Measured on the MI355X: the encoder divides by
+// the power of two given by the scale operand's exponent field (the mantissa is
+// ignored; a denormal scale acts as 2^-127) and rounds to nearest, ties to the
+// even code, saturating at 6 (infinities too); the sign of zero and of inputs
+// that round to zero is kept, and denormal inputs are not flushed.  So with a
+// power-of-two scale X in [2^-127, 2^127] the code is exactly E2M1_RNE(v / X),
+// the rule of e2m1_mag plus the input's sign bit.  The decoder returns the
+// signed value times the scale's power of two.
+//
+// Codes of a and b into byte SEL of `old` (a in the low nibble).
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1_pack2(uint32_t old, float a, float b, float pow2_scale) {
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, pow2_scale, SEL);
+}
+// Signed values of the two codes in byte SEL of `packed`, times pow2_scale.
+typedef float rsfp4_float2v __attribute__((ext_vector_type(2)));
+template <int SEL>
+__device__ __forceinline__ rsfp4_float2v e2m1_unpack2(uint32_t packed, float pow2_scale) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(packed, pow2_scale, SEL);
+}
+
 // MXFP4: E8M0 byte for a block whose largest magnitude is a >= 0:
 // floor(log2 a) - 2 biased by 127, clamped to [0, 254]; a == 0 -> 0.
 __device__ __forceinline__ uint32_t e8m0_for_amax(float a) {

@@ -10,9 +10,12 @@
 //   2. block amax over the adjacent lanes that share a block (DPP lane swaps),
 //      then the block scale:
 //      NVFP4 E4M3_RNE(blockmax / (6 s_g)), MXFP4 E8M0 (Section 2, Figure 1)
-//   3. element codes E2M1_RNE(v / s~) (Eq. 10), packed into one store per thread
+//   3. element codes E2M1_RNE(v / s~) (Eq. 10) with the gfx950 FP4 conversion
+//      (NVFP4: on the IEEE quotient; MXFP4: straight from v with the power-of-
+//      two scale), packed into one store per thread
 //   4. residue r = v - fl(s~ e) kept in the same registers (Section 4.4: the
-//      residue is formed in registers, no second read of x)
+//      residue is formed in registers, no second read of x), e from the
+//      hardware decoder
 //   5. steps 1-3 again on r with its own row amax; the row goes to record M+m.
 #include <hip/hip_runtime.h>
 #include <hip/hip_bf16.h>
@@ -112,12 +115,52 @@ __device__ __forceinline__ float block_scale(float bm, float s_g, uint32_t& sbyt
     return e8m0_val(sbyte);
 }
 
-// Signed E2M1 code of x at element scale st (0 magnitude when st == 0).
-__device__ __forceinline__ uint32_t e2m1_code(float x, float st) {
-    // (st == 0 gives inf or NaN here; the select discards it)
-    const uint32_t mq = e2m1_mag(fabsf(x / st));
-    const uint32_t mag = st != 0.0f ? mq : 0u;
-    return (__float_as_uint(x) >> 28 & 8u) | mag;
+// Element codes with the hardware conversion (codec.h): MXFP4 converts v with
+// the block's power-of-two scale directly; NVFP4 first forms the IEEE quotient
+// v / s~ and converts it with scale 1.  A zero s~ (zero block, or a block scale
+// that rounds to 0) divides by infinity instead, so the code is a zero of v's
+// sign.  Dequantized values come back through the decoder: fl(s~ * e) for
+// NVFP4 (the decoder's e is exact), X * e exactly for MXFP4.
+template <int FMT>
+__device__ __forceinline__ float quot_div(float st) {
+    return FMT == kNV ? (st != 0.0f ? st : __builtin_inff()) : st;
+}
+
+template <int FMT, int SEL>
+__device__ __forceinline__ uint32_t enc2(uint32_t packed, float a, float b, float st, float sd) {
+    if (FMT == kNV) return e2m1_pack2<SEL>(packed, a / sd, b / sd, 1.0f);
+    return e2m1_pack2<SEL>(packed, a, b, st);
+}
+
+template <int FMT, int SEL>
+__device__ __forceinline__ rsfp4_float2v dec2(uint32_t packed, float st) {
+    if (FMT == kNV) {
+        const rsfp4_float2v e = e2m1_unpack2<SEL>(packed, 1.0f);
+        return rsfp4_float2v{st * e[0], st * e[1]};
+    }
+    return e2m1_unpack2<SEL>(packed, st);
+}
+
+// Encode EPT (4 or 8) values into packed nibbles (element e at bits 4e..4e+3)
+// and replace them by their residues v - deq.
+template <int FMT, int EPT>
+__device__ __forceinline__ uint32_t encode_residue(float (&v)[EPT], float st) {
+    const float sd = quot_div<FMT>(st);
+    uint32_t packed = 0u;
+    packed = enc2<FMT, 0>(packed, v[0], v[1], st, sd);
+    packed = enc2<FMT, 1>(packed, v[2], v[3], st, sd);
+    if (EPT == 8) {
+        packed = enc2<FMT, 2>(packed, v[4], v[5], st, sd);
+        packed = enc2<FMT, 3>(packed, v[6], v[7], st, sd);
+    }
+    rsfp4_float2v d;
+    d = dec2<FMT, 0>(packed, st); v[0] -= d[0]; v[1] -= d[1];
+    d = dec2<FMT, 1>(packed, st); v[2] -= d[0]; v[3] -= d[1];
+    if (EPT == 8) {
+        d = dec2<FMT, 2>(packed, st); v[4] -= d[0]; v[5] -= d[1];
+        d = dec2<FMT, 3>(packed, st); v[6] -= d[0]; v[7] -= d[1];
+    }
+    return packed;
 }
 
 // Record header: the row's fp32 tensor scale (0 for MXFP4) and zero padding.
@@ -146,15 +189,8 @@ __device__ __forceinline__ void quantize_chunks(float (&v)[NC][EPT], int nchunks
         if (LPB >= 8) bm = fmaxf(bm, dpp<kDppHalfMirror>(bm));
         uint32_t sbyte;
         const float st = block_scale<FMT>(bm, s_g, sbyte);   // effective element scale
-        uint32_t packed = 0u;
-#pragma unroll
-        for (int e = 0; e < EPT; ++e) {
-            const float x = v[c][e];
-            const uint32_t code = e2m1_code(x, st);
-            packed |= code << (4 * e);
-            const float d = st * e2m1_val(code);
-            v[c][e] = x - d;                          // residue, exact (Sterbenz)
-        }
+        // codes, and v becomes the residue x - fl(s~ e) (exact: Sterbenz)
+        const uint32_t packed = encode_residue<FMT, EPT>(v[c], st);
         if (j < nchunks) {
             if (EPT == 8)
                 *reinterpret_cast<uint32_t*>(codes + 4 * (int64_t)j) = packed;
@@ -331,9 +367,18 @@ __global__ __launch_bounds__(kQMaxThreads) void quant_kext_kernel(const TIn* __r
         bm = run_max<LPE>(bm);
         uint32_t sbyte;
         const float st = block_scale<FMT>(bm, s_g, sbyte);
+        const float sd = quot_div<FMT>(st);
         uint32_t packed = 0u;
-#pragma unroll
-        for (int q = 0; q < KS; ++q) packed |= e2m1_code(rs[q], st) << (4 * q);
+        if (KS == 1) {
+            packed = enc2<FMT, 0>(0u, rs[0], 0.0f, st, sd) & 15u;
+        } else {
+            packed = enc2<FMT, 0>(packed, rs[0], rs[KS > 1 ? 1 : 0], st, sd);
+            if (KS >= 4) packed = enc2<FMT, 1>(packed, rs[KS >= 4 ? 2 : 0], rs[KS >= 4 ? 3 : 0], st, sd);
+            if (KS == 8) {
+                packed = enc2<FMT, 2>(packed, rs[KS == 8 ? 4 : 0], rs[KS == 8 ? 5 : 0], st, sd);
+                packed = enc2<FMT, 3>(packed, rs[KS == 8 ? 6 : 0], rs[KS == 8 ? 7 : 0], st, sd);
+            }
+        }
         uint32_t pair = 0u;
         if (KS == 1) pair = packed | (dpp_xor1_u32(packed) << 4);   // even lane: its nibble low
         if (j < nchunks) {
