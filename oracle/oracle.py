@@ -5,7 +5,8 @@ oracle and back; the arithmetic lives in the C file, which follows the ResServe
 page (arXiv 2611.08713): Section 2 / Figure 1 for the formats, Appendix B.2
 Eqs. 8-10 for the NVFP4 scale computation, Section 4.2 Eq. 1 and Section 4.3
 Eq. 2 for the compensated product and its Fold; Section 5.3, Eq. 6 and
-Appendix B.1, Eq. 7 for selective compensation (K-Ext).
+Appendix B.1, Eq. 7 for selective compensation (K-Ext); Appendix B.2 (Eq. 8 and
+Algorithm 1) for the paper-numerics NVFP4 quantizer with a tensor scale alpha.
 """
 import ctypes
 import os
@@ -27,6 +28,7 @@ __all__ = [
     "quantize_act", "quantize_weight", "quantize_weight_rows", "dequant_rows",
     "linear", "unpack_codes",
     "channel_abs_sum", "kext_select", "kext_dim", "kext_extend_weight", "kext_quantize_act",
+    "nvfp4_alpha", "quantize_row_alg1", "quantize_act_alg1",
 ]
 
 
@@ -77,6 +79,11 @@ def lib():
         L.oracle_kext_extend_weight.argtypes = [P, i64, i64, P, i32, P]
         L.oracle_kext_quantize_act.restype = None
         L.oracle_kext_quantize_act.argtypes = [i32, P, i64, i64, P, i32, P, P, P, P, P]
+        L.oracle_nvfp4_alpha.restype, L.oracle_nvfp4_alpha.argtypes = f32, [P, i64]
+        L.oracle_nvfp4_quantize_row_alg1.restype = None
+        L.oracle_nvfp4_quantize_row_alg1.argtypes = [P, i64, f32, P, P, P, P]
+        L.oracle_quantize_act_alg1.restype = None
+        L.oracle_quantize_act_alg1.argtypes = [P, i64, i64, f32, i32, P, P, P, P, P, P]
         _lib = L
     return _lib
 
@@ -274,3 +281,39 @@ def kext_quantize_act(x, fmt, masks, k):
     lib().oracle_kext_quantize_act(fmt, _p(x), M, K, _p(masks), int(k), _p(codes), _p(scales),
                                    _p(globs), _p(deq), _p(work))
     return {"codes": codes, "scales": scales, "globals": globs, "deq": deq}
+
+
+# ------------------------------------------------- paper numerics (alg1) --
+
+def nvfp4_alpha(x):
+    """alpha = fl(fl(amax / 6) / 448) over the whole tensor."""
+    x = _f32(x).ravel()
+    return np.float32(lib().oracle_nvfp4_alpha(_p(x), x.size))
+
+
+def quantize_row_alg1(v, alpha):
+    """One NVFP4 row with tensor scale alpha: codes, scales, deq, resid."""
+    v = _f32(v).ravel()
+    K = v.size
+    codes = np.zeros((K // 2,), np.uint8)
+    scales = np.zeros((K // 16,), np.uint8)
+    deq = np.zeros((K,), np.float32)
+    resid = np.zeros((K,), np.float32)
+    lib().oracle_nvfp4_quantize_row_alg1(_p(v), K, float(alpha), _p(codes), _p(scales), _p(deq), _p(resid))
+    return {"codes": codes, "scales": scales, "deq": deq, "resid": resid}
+
+
+def quantize_act_alg1(x, alpha, with_residue=True):
+    """Rows of x[M, K] with one tensor scale alpha (rows stacked [X^; R^])."""
+    x = _f32(x)
+    M, K = x.shape
+    R = 2 * M if with_residue else M
+    codes = np.zeros((R, K // 2), np.uint8)
+    scales = np.zeros((R, K // 16), np.uint8)
+    globs = np.zeros((R,), np.float32)
+    deq = np.zeros((R, K), np.float32)
+    resid = np.zeros((M, K), np.float32) if with_residue else None
+    work = np.zeros((K,), np.float32)
+    lib().oracle_quantize_act_alg1(_p(x), M, K, float(alpha), 1 if with_residue else 0, _p(codes), _p(scales),
+                                   _p(globs), _p(deq), _p(resid) if with_residue else None, _p(work))
+    return {"codes": codes, "scales": scales, "globals": globs, "deq": deq, "resid": resid}

@@ -429,3 +429,70 @@ ORACLE_API void oracle_kext_quantize_act(int fmt, const float* x, int64_t M, int
             oracle_mxfp4_quantize_row(work, ext, c + K / 2, s + K / blk, d ? d + K : (float*)0);
     }
 }
+
+/* ------------------------------- paper numerics (static tensor scale) ---- */
+/* The operator as the page's fused quantizer computes it (Appendix B.2: Eq. 8
+ * and the pack8 description, Algorithm 1), in the reading listed in the design
+ * notes, NVFP4 only:
+ *   - one tensor scale alpha per activation tensor, an input (static or
+ *     calibrated); when derived from the data, alpha = (amax / 6) / 448 with
+ *     both divisions rounded (Eq. 8: s_i = Max_i / 6, alpha = max_i s_i / 448);
+ *   - block scale byte E4M3_RNE((Max_i / 6) / alpha), both divisions rounded;
+ *   - the multiplier scale = 1 / (alpha * S_b) (0 when alpha * S_b is 0); the
+ *     element code is E2M1_RNE(x * scale);
+ *   - the residue r = x - e / scale (x when scale is 0): the decoded code is
+ *     rescaled by dividing by the multiplier;
+ *   - the residue shares alpha and is quantized by the same steps.
+ * The dequantized value the product uses is fl(alpha * S_b) * e. */
+
+/* alpha = fl(fl(amax / 6) / 448) over n values. */
+ORACLE_API float oracle_nvfp4_alpha(const float* x, int64_t n) {
+    const float s = oracle_absmax(x, n) / 6.0f;
+    return s / 448.0f;
+}
+
+/* One row with tensor scale alpha.  codes K/2, scales K/16, deq K (optional),
+ * resid K (optional: the residue as the algorithm forms it). */
+ORACLE_API void oracle_nvfp4_quantize_row_alg1(const float* v, int64_t K, float alpha, uint8_t* codes,
+                                               uint8_t* scales, float* deq, float* resid) {
+    for (int64_t b = 0; b < K / 16; ++b) {
+        const float* blk = v + 16 * b;
+        const float s = oracle_absmax(blk, 16) / 6.0f;
+        const uint8_t sb = oracle_e4m3_encode(s / alpha);
+        const float st = alpha * oracle_e4m3_value(sb);
+        const float mult = st > 0.0f ? 1.0f / st : 0.0f;
+        scales[b] = sb;
+        for (int j = 0; j < 16; ++j) {
+            const float x = blk[j];
+            const float u = x * mult;
+            const uint8_t code = (uint8_t)((signbit(x) ? 8u : 0u) | oracle_e2m1_encode_mag(fabsf(u)));
+            const int64_t k = 16 * b + j;
+            if ((k & 1) == 0)
+                codes[k / 2] = code;
+            else
+                codes[k / 2] = (uint8_t)(codes[k / 2] | (code << 4));
+            const float e = oracle_e2m1_value(code);
+            if (deq) deq[k] = st * e;
+            if (resid) resid[k] = mult > 0.0f ? x - e / mult : x;
+        }
+    }
+}
+
+/* M rows (and, with_residue, their residues as rows M..2M-1) with one tensor
+ * scale alpha for all of them.  Layout as oracle_quantize_act; globals = alpha;
+ * resid: M x K (optional). */
+ORACLE_API void oracle_quantize_act_alg1(const float* x, int64_t M, int64_t K, float alpha, int with_residue,
+                                         uint8_t* codes, uint8_t* scales, float* globals, float* deq,
+                                         float* resid, float* work) {
+    for (int64_t m = 0; m < M; ++m) {
+        float* r = with_residue ? (resid ? resid + m * K : work) : (float*)0;
+        oracle_nvfp4_quantize_row_alg1(x + m * K, K, alpha, codes + m * (K / 2), scales + m * (K / 16),
+                                       deq ? deq + m * K : (float*)0, r);
+        globals[m] = alpha;
+        if (!with_residue) continue;
+        const int64_t rr = M + m;
+        oracle_nvfp4_quantize_row_alg1(r, K, alpha, codes + rr * (K / 2), scales + rr * (K / 16),
+                                       deq ? deq + rr * K : (float*)0, (float*)0);
+        globals[rr] = alpha;
+    }
+}
