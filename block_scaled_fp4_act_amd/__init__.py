@@ -11,7 +11,9 @@ format-generic ``prepack_weights``, ``quantize_act_with_residue``, ``fp4_linear`
 and ``fp4_linear_compensated``.  Selective compensation (K-Ext):
 ``channel_abs_sum``, ``kext_select``, ``kext_dim``, ``prepack_weights_kext``,
 ``quantize_act_kext`` (and the ``nvfp4_`` / ``mxfp4_`` forms); the product is
-then the plain ``fp4_linear`` over K_eff = kext_dim(K, k).
+then the plain ``fp4_linear`` over K_eff = kext_dim(K, k).  Paper numerics:
+``nvfp4_tensor_alpha``, ``nvfp4_quantize_act_alpha`` and the bf16-output
+``fp4_linear_bf16`` / ``fp4_linear_compensated_bf16``.
 """
 import ctypes
 
@@ -135,13 +137,14 @@ def act_views(act, fmt, M, K, with_residue=True):
 
 # ----------------------------------------------------------------- linear --
 
-def _linear(act, w_packed, M, N, K, fmt, comp, out):
+def _linear(act, w_packed, M, N, K, fmt, comp, out, bf16=False):
     import torch
     fmt = _fmt(fmt)
+    dt = torch.bfloat16 if bf16 else torch.float32
     if out is None:
-        out = torch.empty((M, N), dtype=torch.float32, device=act.device)
-    assert out.is_cuda and out.dtype == torch.float32 and out.is_contiguous() and out.numel() >= M * N
-    name = f"rsfp4_{_FMT_NAME[fmt]}_linear" + ("_compensated" if comp else "")
+        out = torch.empty((M, N), dtype=dt, device=act.device)
+    assert out.is_cuda and out.dtype == dt and out.is_contiguous() and out.numel() >= M * N
+    name = f"rsfp4_{_FMT_NAME[fmt]}_linear" + ("_compensated" if comp else "") + ("_bf16" if bf16 else "")
     _check(getattr(lib(), name)(_ptr(act), act.numel(), _ptr(w_packed), w_packed.numel(), M, N, K,
                                 _ptr(out), None, 0, _stream(act)))
     return out
@@ -155,6 +158,16 @@ def fp4_linear(act, w_packed, M, N, K, fmt, out=None):
 def fp4_linear_compensated(act, w_packed, M, N, K, fmt, out=None):
     """y = deq(q(x)) W^T + deq(q(r)) W^T (residue-compensated), fp32 [M, N]."""
     return _linear(act, w_packed, M, N, K, fmt, True, out)
+
+
+def fp4_linear_bf16(act, w_packed, M, N, K, fmt, out=None):
+    """As fp4_linear, bf16 output (round to nearest even)."""
+    return _linear(act, w_packed, M, N, K, fmt, False, out, bf16=True)
+
+
+def fp4_linear_compensated_bf16(act, w_packed, M, N, K, fmt, out=None):
+    """As fp4_linear_compensated, bf16 output (round to nearest even)."""
+    return _linear(act, w_packed, M, N, K, fmt, True, out, bf16=True)
 
 
 def nvfp4_linear(act, w_packed, M, N, K, out=None):
@@ -171,6 +184,35 @@ def mxfp4_linear(act, w_packed, M, N, K, out=None):
 
 def mxfp4_linear_compensated(act, w_packed, M, N, K, out=None):
     return _linear(act, w_packed, M, N, K, MXFP4, True, out)
+
+
+# ------------------------------------------- paper numerics (tensor scale) --
+
+def nvfp4_tensor_alpha(x, out=None):
+    """alpha = ((max|x|) / 6) / 448 of a whole tensor, as a 1-element fp32 tensor."""
+    import torch
+    assert x.is_cuda and x.is_contiguous()
+    M = x.shape[0] if x.dim() > 1 else 1
+    K = x.numel() // M
+    if out is None:
+        out = torch.empty(1, dtype=torch.float32, device=x.device)
+    _check(lib().rsfp4_nvfp4_tensor_alpha(_ptr(x), _dtype_code(x), M, K, _ptr(out), _stream(x)))
+    return out
+
+
+def nvfp4_quantize_act_alpha(x, alpha, with_residue=True, out=None):
+    """Paper-numerics NVFP4 quantization of x[M, K] with tensor scale alpha
+    (a 1-element fp32 cuda tensor), shared by x and r."""
+    import torch
+    assert x.is_cuda and x.dim() == 2 and x.is_contiguous()
+    assert alpha.is_cuda and alpha.dtype == torch.float32
+    M, K = x.shape
+    nbytes = packed_act_bytes(NVFP4, M, K, with_residue)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+    _check(lib().rsfp4_nvfp4_quantize_act_alpha(_ptr(x), _dtype_code(x), M, K, _ptr(alpha),
+                                                1 if with_residue else 0, _ptr(out), out.numel(), _stream(x)))
+    return out
 
 
 # ---------------------------------------------------------------- K-Ext --

@@ -30,6 +30,12 @@ SIGNATURES = {
     "rsfp4_mxfp4_linear": (INT, [P, SZ, P, SZ, I64, I64, I64, P, P, SZ, P]),
     "rsfp4_mxfp4_linear_compensated": (INT, [P, SZ, P, SZ, I64, I64, I64, P, P, SZ, P]),
     "rsfp4_unpack_weights_canonical": (INT, [P, SZ, INT, I64, I64, P, P, P, P]),
+    "rsfp4_nvfp4_linear_bf16": (INT, [P, SZ, P, SZ, I64, I64, I64, P, P, SZ, P]),
+    "rsfp4_nvfp4_linear_compensated_bf16": (INT, [P, SZ, P, SZ, I64, I64, I64, P, P, SZ, P]),
+    "rsfp4_mxfp4_linear_bf16": (INT, [P, SZ, P, SZ, I64, I64, I64, P, P, SZ, P]),
+    "rsfp4_mxfp4_linear_compensated_bf16": (INT, [P, SZ, P, SZ, I64, I64, I64, P, P, SZ, P]),
+    "rsfp4_nvfp4_quantize_act_alpha": (INT, [P, INT, I64, I64, P, INT, P, SZ, P]),
+    "rsfp4_nvfp4_tensor_alpha": (INT, [P, INT, I64, I64, P, P]),
     "rsfp4_kext_dim": (I64, [I64, INT]),
     "rsfp4_channel_abs_sum": (INT, [P, INT, I64, I64, P, INT, P]),
     "rsfp4_kext_select": (INT, [P, I64, INT, P, P]),

@@ -99,7 +99,7 @@ rsfp4_status quantize(int fmt, const void* x, int xt, int64_t M, int64_t K, int 
 }
 
 rsfp4_status linear(int fmt, bool comp, const void* act, size_t act_bytes, const void* w_packed,
-                    size_t w_bytes, int64_t M, int64_t N, int64_t K, float* y, void* ws,
+                    size_t w_bytes, int64_t M, int64_t N, int64_t K, void* y, bool out_bf16, void* ws,
                     size_t ws_bytes, void* stream) {
     (void)ws;
     (void)ws_bytes;
@@ -112,8 +112,8 @@ rsfp4_status linear(int fmt, bool comp, const void* act, size_t act_bytes, const
     if (K > kMaxLinearK) return fail(RSFP4_ERR_UNSUPPORTED, "the linear supports K <= %lld (K = %lld)",
                                      (long long)kMaxLinearK, (long long)K);
     const int64_t B = comp ? 2 * M : M;
-    if (!aligned(act, 16) || !aligned(w_packed, 256) || !aligned(y, 4))
-        return fail(RSFP4_ERR_ALIGN, "act must be 16-, w_packed 256- and y 4-byte aligned");
+    if (!aligned(act, 16) || !aligned(w_packed, 256) || !aligned(y, out_bf16 ? 2 : 4))
+        return fail(RSFP4_ERR_ALIGN, "act must be 16-, w_packed 256- and y element aligned");
     const int64_t rb = act_row_bytes(fmt, K);
     const size_t need_a = (size_t)rb * (size_t)B;
     if (act_bytes < need_a) return fail(RSFP4_ERR_BUFFER_TOO_SMALL, "act holds %zu bytes, needs %zu", act_bytes, need_a);
@@ -121,14 +121,17 @@ rsfp4_status linear(int fmt, bool comp, const void* act, size_t act_bytes, const
     if (w_bytes < need_w) return fail(RSFP4_ERR_BUFFER_TOO_SMALL, "w_packed holds %zu bytes, needs %zu", w_bytes, need_w);
     // The tiled kernel addresses the activation operand with 32-bit offsets
     // below its out-of-range marker 2^31.
-    if (B > kNarrowRows) {
+    // bf16 output cannot take the narrow kernel's second, accumulating launch:
+    // K above one narrow launch goes to the tiled kernel (one pass over K)
+    if (B > kNarrowRows || (out_bf16 && K > kMaxNarrowK)) {
         if ((int64_t)rb * B >= ((int64_t)1 << 31))
             return fail(RSFP4_ERR_UNSUPPORTED, "activation operand of %lld bytes: the linear needs < 2^31",
                         (long long)((int64_t)rb * B));
         if (std::getenv("RSFP4_LOG"))
             std::fprintf(stderr, "[rsfp4] linear fmt=%d comp=%d M=%lld N=%lld K=%lld tiled\n", fmt, (int)comp,
                          (long long)M, (long long)N, (long long)K);
-        return hip_status(launch_gemm_tile(fmt, comp, act, rb, w_packed, (int)M, N, K, y, (hipStream_t)stream),
+        return hip_status(launch_gemm_tile(fmt, comp, act, rb, w_packed, (int)M, N, K, y, out_bf16,
+                                           (hipStream_t)stream),
                           "linear launch");
     }
     int cus = 0;
@@ -146,8 +149,8 @@ rsfp4_status linear(int fmt, bool comp, const void* act, size_t act_bytes, const
             std::fprintf(stderr, "[rsfp4] linear fmt=%d comp=%d M=%lld N=%lld K=%lld steps=[%d,%d) rt=%d maxs=%d "
                          "kw=%d grid=%lld ngl=%d\n", fmt, (int)comp, (long long)M, (long long)N, (long long)K,
                          s_lo, s_hi, pl.rt, pl.maxs, pl.kw, (long long)pl.grid, pl.ngl);
-        st = hip_status(launch_gemm_small(fmt, pl, comp, act, rb, w_packed, (int)M, N, K, y, s_lo, s_hi,
-                                          pass == 1, (hipStream_t)stream),
+        st = hip_status(launch_gemm_small(fmt, pl, comp, act, rb, w_packed, (int)M, N, K, y, out_bf16, s_lo,
+                                          s_hi, pass == 1, (hipStream_t)stream),
                         "linear launch");
         if (st != RSFP4_OK) return st;
     }
@@ -209,6 +212,24 @@ rsfp4_status quantize_kext(int fmt, const void* x, int xt, int64_t M, int64_t K,
     if (bytes < need) return fail(RSFP4_ERR_BUFFER_TOO_SMALL, "act holds %zu bytes, needs %zu", bytes, need);
     return hip_status(launch_quantize_act_kext(fmt, xt == RSFP4_BF16, x, (int)M, K, masks, k, act,
                                                (hipStream_t)stream),
+                      "quantize launch");
+}
+
+rsfp4_status quantize_alpha(const void* x, int xt, int64_t M, int64_t K, const float* alpha, int with_res,
+                            void* act, size_t bytes, void* stream) {
+    g_err[0] = 0;
+    rsfp4_status st = check_common(RSFP4_NVFP4, K);
+    if (st != RSFP4_OK) return st;
+    if (!x || !act || !alpha) return fail(RSFP4_ERR_NULL, "x, alpha and act must be non-NULL");
+    if (xt != RSFP4_F32 && xt != RSFP4_BF16) return fail(RSFP4_ERR_FORMAT, "unknown activation dtype %d", xt);
+    if (M < 1 || M > 65535) return fail(RSFP4_ERR_SHAPE, "M = %lld outside [1, 65535]", (long long)M);
+    if (K > kMaxQuantK) return fail(RSFP4_ERR_SHAPE, "quantize needs K <= 32768 (K = %lld)", (long long)K);
+    if (!aligned(x, 16) || !aligned(act, 16) || !aligned(alpha, 4))
+        return fail(RSFP4_ERR_ALIGN, "x and act must be 16-byte and alpha 4-byte aligned");
+    const size_t need = (size_t)act_row_bytes(RSFP4_NVFP4, K) * (size_t)(with_res ? 2 * M : M);
+    if (bytes < need) return fail(RSFP4_ERR_BUFFER_TOO_SMALL, "act holds %zu bytes, needs %zu", bytes, need);
+    return hip_status(launch_quantize_act_alpha(xt == RSFP4_BF16, x, (int)M, K, alpha, with_res ? 1 : 0, act,
+                                                (hipStream_t)stream),
                       "quantize launch");
 }
 
@@ -277,22 +298,22 @@ rsfp4_status rsfp4_mxfp4_quantize_act_with_residue(const void* x, int xt, int64_
 rsfp4_status rsfp4_nvfp4_linear(const void* act, size_t act_bytes, const void* w_packed, size_t w_packed_bytes,
                                 int64_t M, int64_t N, int64_t K, float* y, void* ws, size_t ws_bytes,
                                 void* stream) {
-    return linear(RSFP4_NVFP4, false, act, act_bytes, w_packed, w_packed_bytes, M, N, K, y, ws, ws_bytes, stream);
+    return linear(RSFP4_NVFP4, false, act, act_bytes, w_packed, w_packed_bytes, M, N, K, y, false, ws, ws_bytes, stream);
 }
 rsfp4_status rsfp4_nvfp4_linear_compensated(const void* act, size_t act_bytes, const void* w_packed,
                                             size_t w_packed_bytes, int64_t M, int64_t N, int64_t K, float* y,
                                             void* ws, size_t ws_bytes, void* stream) {
-    return linear(RSFP4_NVFP4, true, act, act_bytes, w_packed, w_packed_bytes, M, N, K, y, ws, ws_bytes, stream);
+    return linear(RSFP4_NVFP4, true, act, act_bytes, w_packed, w_packed_bytes, M, N, K, y, false, ws, ws_bytes, stream);
 }
 rsfp4_status rsfp4_mxfp4_linear(const void* act, size_t act_bytes, const void* w_packed, size_t w_packed_bytes,
                                 int64_t M, int64_t N, int64_t K, float* y, void* ws, size_t ws_bytes,
                                 void* stream) {
-    return linear(RSFP4_MXFP4, false, act, act_bytes, w_packed, w_packed_bytes, M, N, K, y, ws, ws_bytes, stream);
+    return linear(RSFP4_MXFP4, false, act, act_bytes, w_packed, w_packed_bytes, M, N, K, y, false, ws, ws_bytes, stream);
 }
 rsfp4_status rsfp4_mxfp4_linear_compensated(const void* act, size_t act_bytes, const void* w_packed,
                                             size_t w_packed_bytes, int64_t M, int64_t N, int64_t K, float* y,
                                             void* ws, size_t ws_bytes, void* stream) {
-    return linear(RSFP4_MXFP4, true, act, act_bytes, w_packed, w_packed_bytes, M, N, K, y, ws, ws_bytes, stream);
+    return linear(RSFP4_MXFP4, true, act, act_bytes, w_packed, w_packed_bytes, M, N, K, y, false, ws, ws_bytes, stream);
 }
 
 rsfp4_status rsfp4_unpack_weights_canonical(const void* w_packed, size_t w_packed_bytes, int fmt, int64_t N,
@@ -353,6 +374,43 @@ rsfp4_status rsfp4_nvfp4_quantize_act_kext(const void* x, int xt, int64_t M, int
 rsfp4_status rsfp4_mxfp4_quantize_act_kext(const void* x, int xt, int64_t M, int64_t K, const uint8_t* masks,
                                            int k, void* act, size_t act_bytes, void* stream) {
     return quantize_kext(RSFP4_MXFP4, x, xt, M, K, masks, k, act, act_bytes, stream);
+}
+
+rsfp4_status rsfp4_nvfp4_tensor_alpha(const void* x, int xt, int64_t M, int64_t K, float* alpha, void* stream) {
+    g_err[0] = 0;
+    if (!x || !alpha) return fail(RSFP4_ERR_NULL, "x and alpha must be non-NULL");
+    if (xt != RSFP4_F32 && xt != RSFP4_BF16) return fail(RSFP4_ERR_FORMAT, "unknown activation dtype %d", xt);
+    if (M < 1 || K < 1 || M > ((int64_t)1 << 40) / K)
+        return fail(RSFP4_ERR_SHAPE, "M = %lld, K = %lld outside M, K >= 1, M*K <= 2^40", (long long)M, (long long)K);
+    if (!aligned(alpha, 4) || !aligned(x, xt == RSFP4_BF16 ? 2 : 4))
+        return fail(RSFP4_ERR_ALIGN, "alpha must be 4-byte and x element aligned");
+    return hip_status(launch_tensor_alpha(xt == RSFP4_BF16, x, M * K, alpha, (hipStream_t)stream), "alpha launch");
+}
+
+rsfp4_status rsfp4_nvfp4_quantize_act_alpha(const void* x, int xt, int64_t M, int64_t K, const float* alpha,
+                                            int with_residue, void* act, size_t act_bytes, void* stream) {
+    return quantize_alpha(x, xt, M, K, alpha, with_residue, act, act_bytes, stream);
+}
+
+rsfp4_status rsfp4_nvfp4_linear_bf16(const void* act, size_t act_bytes, const void* w_packed, size_t w_packed_bytes,
+                                     int64_t M, int64_t N, int64_t K, void* y, void* ws, size_t ws_bytes,
+                                     void* stream) {
+    return linear(RSFP4_NVFP4, false, act, act_bytes, w_packed, w_packed_bytes, M, N, K, y, true, ws, ws_bytes, stream);
+}
+rsfp4_status rsfp4_nvfp4_linear_compensated_bf16(const void* act, size_t act_bytes, const void* w_packed,
+                                                 size_t w_packed_bytes, int64_t M, int64_t N, int64_t K, void* y,
+                                                 void* ws, size_t ws_bytes, void* stream) {
+    return linear(RSFP4_NVFP4, true, act, act_bytes, w_packed, w_packed_bytes, M, N, K, y, true, ws, ws_bytes, stream);
+}
+rsfp4_status rsfp4_mxfp4_linear_bf16(const void* act, size_t act_bytes, const void* w_packed, size_t w_packed_bytes,
+                                     int64_t M, int64_t N, int64_t K, void* y, void* ws, size_t ws_bytes,
+                                     void* stream) {
+    return linear(RSFP4_MXFP4, false, act, act_bytes, w_packed, w_packed_bytes, M, N, K, y, true, ws, ws_bytes, stream);
+}
+rsfp4_status rsfp4_mxfp4_linear_compensated_bf16(const void* act, size_t act_bytes, const void* w_packed,
+                                                 size_t w_packed_bytes, int64_t M, int64_t N, int64_t K, void* y,
+                                                 void* ws, size_t ws_bytes, void* stream) {
+    return linear(RSFP4_MXFP4, true, act, act_bytes, w_packed, w_packed_bytes, M, N, K, y, true, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -102,4 +102,19 @@ __device__ __forceinline__ float e8m0_val(uint32_t b) {
     return b ? __uint_as_float(b << 23) : __uint_as_float(0x00400000u);
 }
 
+// fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint16_t bf16_rne(float v) {
+    const uint32_t b = __float_as_uint(v);
+    if ((b & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((b >> 16) | 0x0040u);
+    return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
+}
+
+// Output store of the linear kernels: fp32, or bf16 rounded to nearest even.
+__device__ __forceinline__ void store_y(void* y, int64_t idx, float v, int bf16) {
+    if (bf16)
+        reinterpret_cast<uint16_t*>(y)[idx] = bf16_rne(v);
+    else
+        reinterpret_cast<float*>(y)[idx] = v;
+}
+
 }  // namespace rsfp4

@@ -144,11 +144,12 @@ struct GemmArgs {
     int M;
     int64_t N;
     int64_t K;
-    float* y;
+    void* y;          // fp32 or (out_bf16) bf16 output
     int ngl;          // LDS slots for partial sums (groups in flight per workgroup)
     int s_lo;         // first K step of this launch (wave w owns s_lo + w*MAXS ..)
     int64_t k_hi;     // K elements at or past k_hi are left to another launch
-    int accum;        // add to y instead of overwriting it
+    int accum;        // add to y instead of overwriting it (fp32 output only)
+    int out_bf16;     // store y as bf16 (round to nearest even)
 };
 
 // APRE: the activation fragments are dequantized to f16 once, before the
@@ -302,8 +303,8 @@ __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmArgs p) {
                         } else {
                             out = v0 + v1;
                         }
-                        if (p.accum) out += p.y[(int64_t)m * p.N + n];
-                        p.y[(int64_t)m * p.N + n] = out;
+                        if (p.accum) out += reinterpret_cast<const float*>(p.y)[(int64_t)m * p.N + n];
+                        store_y(p.y, (int64_t)m * p.N + n, out, p.out_bf16);
                     }
                 } else {
 #pragma unroll
@@ -314,8 +315,8 @@ __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmArgs p) {
                             float out = v;
                             if (FMT == kNV)
                                 out = s_gw * (*reinterpret_cast<const float*>(p.act + (int64_t)m * p.row_bytes) * v);
-                            if (p.accum) out += p.y[(int64_t)m * p.N + n];
-                            p.y[(int64_t)m * p.N + n] = out;
+                            if (p.accum) out += reinterpret_cast<const float*>(p.y)[(int64_t)m * p.N + n];
+                            store_y(p.y, (int64_t)m * p.N + n, out, p.out_bf16);
                         }
                     }
                 }
@@ -533,10 +534,10 @@ GemmPlan plan_gemm_small(int64_t M, int64_t N, int64_t S, bool comp, int num_cus
 
 hipError_t launch_gemm_small(int fmt, const GemmPlan& pl, bool comp, const void* act,
                              int64_t row_bytes, const void* blob, int M, int64_t N, int64_t K,
-                             float* y, int s_lo, int s_hi, bool accum, hipStream_t s) {
+                             void* y, bool out_bf16, int s_lo, int s_hi, bool accum, hipStream_t s) {
     const int64_t k_hi = (int64_t)s_hi * kStepK < K ? (int64_t)s_hi * kStepK : K;
     GemmArgs a{static_cast<const uint8_t*>(act), row_bytes, static_cast<const uint8_t*>(blob), M,
-               N, K, y, pl.ngl, s_lo, k_hi, accum ? 1 : 0};
+               N, K, y, pl.ngl, s_lo, k_hi, accum ? 1 : 0, out_bf16 ? 1 : 0};
     const bool single = num_groups(N) <= pl.grid;             // one group per workgroup
     if (fmt == kNV) return launch_fmt<kNV>(a, pl.rt, comp, pl.maxs, pl.kw, pl.grid, s, single);
     return launch_fmt<kMX>(a, pl.rt, comp, pl.maxs, pl.kw, pl.grid, s, single);

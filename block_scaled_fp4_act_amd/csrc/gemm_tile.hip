@@ -34,6 +34,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "codec.h"
 #include "kernels.h"
 #include "layout.h"
 
@@ -117,10 +118,11 @@ struct TileArgs {
     int M;
     int64_t N;
     int64_t K;
-    float* y;
+    void* y;            // fp32 or (out_bf16) bf16 output
     int row_tiles;      // ceil(B / TB)
     int64_t tiles;      // row_tiles * ceil(N / TN)
     int64_t per_xcd;    // ceil(tiles / 8)
+    int out_bf16;       // store y as bf16 (round to nearest even)
 };
 
 // LDS layout of one activation stage.
@@ -441,7 +443,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_tile_kernel(TileArgs p) {
                         } else {
                             out = v0 + v1;
                         }
-                        p.y[(int64_t)m * p.N + n] = out;
+                        store_y(p.y, (int64_t)m * p.N + n, out, p.out_bf16);
                     }
                 } else {
 #pragma unroll
@@ -452,7 +454,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_tile_kernel(TileArgs p) {
                             float out = v;
                             if (FMT == kNV)
                                 out = s_gw * (*reinterpret_cast<const float*>(p.act + (int64_t)m * p.row_bytes) * v);
-                            p.y[(int64_t)m * p.N + n] = out;
+                            store_y(p.y, (int64_t)m * p.N + n, out, p.out_bf16);
                         }
                     }
                 }
@@ -502,9 +504,9 @@ hipError_t launch_fmt(const TileArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_gemm_tile(int fmt, bool comp, const void* act, int64_t row_bytes, const void* blob,
-                            int M, int64_t N, int64_t K, float* y, hipStream_t s) {
+                            int M, int64_t N, int64_t K, void* y, bool out_bf16, hipStream_t s) {
     TileArgs a{static_cast<const uint8_t*>(act), row_bytes, static_cast<const uint8_t*>(blob), M, N, K, y,
-               0, 0, 0};
+               0, 0, 0, out_bf16 ? 1 : 0};
     if (fmt == kNV) return comp ? launch_fmt<kNV, true>(a, s) : launch_fmt<kNV, false>(a, s);
     return comp ? launch_fmt<kMX, true>(a, s) : launch_fmt<kMX, false>(a, s);
 }

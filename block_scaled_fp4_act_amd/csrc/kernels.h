@@ -41,11 +41,17 @@ GemmPlan plan_gemm_small(int64_t M, int64_t N, int64_t steps, bool comp, int num
 // the result to y (the second launch of a K longer than one launch covers).
 hipError_t launch_gemm_small(int fmt, const GemmPlan& pl, bool comp, const void* act,
                              int64_t row_bytes, const void* blob, int M, int64_t N, int64_t K,
-                             float* y, int s_lo, int s_hi, bool accum, hipStream_t s);
+                             void* y, bool out_bf16, int s_lo, int s_hi, bool accum, hipStream_t s);
 
 // Wide-operand linear (any number of activation rows): 2-D tiles of 128 rows x
 // 128 channels per workgroup, each wave walking all of K.
 hipError_t launch_gemm_tile(int fmt, bool comp, const void* act, int64_t row_bytes, const void* blob,
-                            int M, int64_t N, int64_t K, float* y, hipStream_t s);
+                            int M, int64_t N, int64_t K, void* y, bool out_bf16, hipStream_t s);
+
+// Paper-numerics NVFP4 quantizer (tensor scale alpha from device memory, shared
+// by x and r; multiplier-scale codes and residue) and the alpha of a tensor.
+hipError_t launch_quantize_act_alpha(int xt_bf16, const void* x, int M, int64_t K, const float* alpha,
+                                     int with_res, void* act, hipStream_t s);
+hipError_t launch_tensor_alpha(int xt_bf16, const void* x, int64_t n, float* alpha, hipStream_t s);
 
 }  // namespace rsfp4

@@ -404,6 +404,141 @@ hipError_t launch_kext_f(const void* x, int M, int64_t K, const uint8_t* masks, 
     }
 }
 
+// ------------------------------------------------- paper numerics (alpha) --
+// The operator of the page's fused quantizer (Appendix B.2, Eq. 8 and
+// Algorithm 1), NVFP4: one tensor scale alpha for the whole activation tensor,
+// read from device memory (static or calibrated; rsfp4_nvfp4_tensor_alpha
+// derives it from the data) and shared by x and r, so no row reduction runs.
+// Per 16-block: S_b = E4M3_RNE((Max / 6) / alpha), the multiplier scale
+// 1 / (alpha S_b) (0 when alpha S_b is 0), codes E2M1_RNE(v * scale) and the
+// residue v - e / scale (v when the scale is 0).  One thread per 8 elements,
+// two threads per block.
+
+template <int NC, bool RES>
+__device__ __forceinline__ void alg1_chunks(float (&v)[NC][8], int nchunks, float alpha, uint8_t* codes,
+                                            uint8_t* scales) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int j = tid + (int)blockDim.x * c;
+        float bm = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) bm = fmaxf(bm, fabsf(v[c][e]));
+        bm = fmaxf(bm, dpp<kDppXor1>(bm));          // the block's two lanes
+        const uint32_t sbyte = e4m3_encode((bm / 6.0f) / alpha);
+        const float st = alpha * e4m3_val(sbyte);
+        const float mult = st > 0.0f ? 1.0f / st : 0.0f;
+        float u[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) u[e] = v[c][e] * mult;
+        if (__builtin_expect(mult > 3.402823466e38f, 0)) {
+            // 1 / (alpha S_b) overflowed: a zero element gives 0 * inf; its code
+            // is the zero of its sign, as for any finite multiplier
+#pragma unroll
+            for (int e = 0; e < 8; ++e) u[e] = v[c][e] == 0.0f ? v[c][e] : u[e];
+        }
+        uint32_t packed = 0u;
+        packed = e2m1_pack2<0>(packed, u[0], u[1], 1.0f);
+        packed = e2m1_pack2<1>(packed, u[2], u[3], 1.0f);
+        packed = e2m1_pack2<2>(packed, u[4], u[5], 1.0f);
+        packed = e2m1_pack2<3>(packed, u[6], u[7], 1.0f);
+        if (RES) {
+            rsfp4_float2v d[4];
+            d[0] = e2m1_unpack2<0>(packed, 1.0f);
+            d[1] = e2m1_unpack2<1>(packed, 1.0f);
+            d[2] = e2m1_unpack2<2>(packed, 1.0f);
+            d[3] = e2m1_unpack2<3>(packed, 1.0f);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float em = mult > 0.0f ? d[e >> 1][e & 1] / mult : 0.0f;
+                v[c][e] = v[c][e] - em;
+            }
+        }
+        if (j < nchunks) {
+            *reinterpret_cast<uint32_t*>(codes + 4 * (int64_t)j) = packed;
+            if ((j & 1) == 0) scales[j >> 1] = (uint8_t)sbyte;
+        }
+    }
+}
+
+template <int NC, typename TIn>
+__global__ __launch_bounds__(kQMaxThreads) void quant_alpha_kernel(const TIn* __restrict__ x, int M, int64_t K,
+                                                                   const float* __restrict__ alpha_p,
+                                                                   int with_res, uint8_t* __restrict__ act,
+                                                                   int64_t row_bytes) {
+    const int m = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int nchunks = (int)(K / 8);
+    const TIn* xr = x + (int64_t)m * K;
+    const float alpha = *alpha_p;
+    float v[NC][8];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int j = tid + (int)blockDim.x * c;
+        if (j < nchunks) {
+            load_chunk<TIn, 8>(xr + 8 * (int64_t)j, v[c]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[c][e] = 0.0f;
+        }
+    }
+    uint8_t* rec = act + (int64_t)m * row_bytes;
+    store_head(rec, alpha);
+    if (!with_res) {
+        alg1_chunks<NC, false>(v, nchunks, alpha, rec + kActHead, rec + kActHead + K / 2);
+        return;
+    }
+    alg1_chunks<NC, true>(v, nchunks, alpha, rec + kActHead, rec + kActHead + K / 2);
+    uint8_t* rrec = act + (int64_t)(M + m) * row_bytes;
+    store_head(rrec, alpha);
+    alg1_chunks<NC, false>(v, nchunks, alpha, rrec + kActHead, rrec + kActHead + K / 2);
+}
+
+template <int NC, typename TIn>
+hipError_t launch_alpha_t(const void* x, int M, int64_t K, const float* alpha, int with_res, void* act,
+                          hipStream_t s) {
+    const int64_t rb = act_row_bytes(kNV, K);
+    const int64_t nch = K / 8;
+    const int threads = nch >= kQMaxThreads ? kQMaxThreads : (int)((nch + 63) / 64 * 64);
+    hipLaunchKernelGGL((quant_alpha_kernel<NC, TIn>), dim3(M), dim3(threads), 0, s,
+                       static_cast<const TIn*>(x), M, K, alpha, with_res, static_cast<uint8_t*>(act), rb);
+    return hipGetLastError();
+}
+
+template <typename TIn>
+hipError_t launch_alpha_f(const void* x, int M, int64_t K, const float* alpha, int with_res, void* act,
+                          hipStream_t s) {
+    const int64_t nch = K / 8;
+    if (nch <= kQMaxThreads) return launch_alpha_t<1, TIn>(x, M, K, alpha, with_res, act, s);
+    if (nch <= 2 * kQMaxThreads) return launch_alpha_t<2, TIn>(x, M, K, alpha, with_res, act, s);
+    return launch_alpha_t<4, TIn>(x, M, K, alpha, with_res, act, s);
+}
+
+// alpha = fl(fl(amax / 6) / 448) over n elements: clear, reduce the maximum
+// (atomicMax on the binary32 bits, which order like the values for x >= 0),
+// then finish in one thread.
+__global__ void alpha_clear_kernel(float* alpha) { *reinterpret_cast<uint32_t*>(alpha) = 0u; }
+
+template <typename TIn>
+__global__ __launch_bounds__(256) void alpha_amax_kernel(const TIn* __restrict__ x, int64_t n, float* alpha) {
+    float m = 0.0f;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        float v;
+        if (sizeof(TIn) == 2)
+            v = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(x)[i] << 16);
+        else
+            v = reinterpret_cast<const float*>(x)[i];
+        m = fmaxf(m, fabsf(v));
+    }
+    m = wave_max(m);
+    if ((threadIdx.x & 63) == 0) atomicMax(reinterpret_cast<uint32_t*>(alpha), __float_as_uint(m));
+}
+
+__global__ void alpha_finish_kernel(float* alpha) {
+    const float amax = *alpha;
+    *alpha = (amax / 6.0f) / 448.0f;
+}
+
 }  // namespace
 
 hipError_t launch_quantize_act(int fmt, int xt_bf16, const void* x, int M, int64_t K, int with_res,
@@ -423,6 +558,30 @@ hipError_t launch_quantize_act_kext(int fmt, int xt_bf16, const void* x, int M, 
                        : launch_kext_f<kNV, float>(x, M, K, masks, k, act, s);
     return xt_bf16 ? launch_kext_f<kMX, __hip_bfloat16>(x, M, K, masks, k, act, s)
                    : launch_kext_f<kMX, float>(x, M, K, masks, k, act, s);
+}
+
+hipError_t launch_quantize_act_alpha(int xt_bf16, const void* x, int M, int64_t K, const float* alpha,
+                                     int with_res, void* act, hipStream_t s) {
+    return xt_bf16 ? launch_alpha_f<__hip_bfloat16>(x, M, K, alpha, with_res, act, s)
+                   : launch_alpha_f<float>(x, M, K, alpha, with_res, act, s);
+}
+
+hipError_t launch_tensor_alpha(int xt_bf16, const void* x, int64_t n, float* alpha, hipStream_t s) {
+    hipLaunchKernelGGL(alpha_clear_kernel, dim3(1), dim3(1), 0, s, alpha);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 2048) blocks = 2048;
+    if (xt_bf16)
+        hipLaunchKernelGGL(alpha_amax_kernel<__hip_bfloat16>, dim3((unsigned)blocks), dim3(256), 0, s,
+                           static_cast<const __hip_bfloat16*>(x), n, alpha);
+    else
+        hipLaunchKernelGGL(alpha_amax_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, s,
+                           static_cast<const float*>(x), n, alpha);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(alpha_finish_kernel, dim3(1), dim3(1), 0, s, alpha);
+    return hipGetLastError();
 }
 
 }  // namespace rsfp4

@@ -23,8 +23,12 @@
  *   MXFP4: 32-element blocks, E8M0 scale 2^(floor(log2 blockmax) - 2) clamped to
  *     [2^-127, 2^127] (byte 0 for an all-zero block), no tensor scale;
  *     element = E2M1_RNE(v / X); value = X * e.
- *   The output y is fp32, accumulated in fp32 on the matrix cores.
+ *   The output y is fp32 (the *_bf16 linears: bf16, rounded to nearest even
+ *   from the fp32 result), accumulated in fp32 on the matrix cores.
  *   NaN or infinite inputs give unspecified codes and outputs.
+ *   The paper-numerics NVFP4 quantizer (rsfp4_nvfp4_quantize_act_alpha) takes
+ *   a tensor scale alpha instead and follows the page's fused quantizer; see
+ *   its comment.
  *
  * Conventions for every call:
  *   - Pointers named W, x, act, w_packed, y, codes, scales, s_g are DEVICE
@@ -166,6 +170,52 @@ rsfp4_status rsfp4_mxfp4_linear(const void* act, size_t act_bytes, const void* w
 rsfp4_status rsfp4_mxfp4_linear_compensated(const void* act, size_t act_bytes, const void* w_packed,
                                             size_t w_packed_bytes, int64_t M, int64_t N, int64_t K,
                                             float* y, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------- bf16 output (the same sums) --
+ * As the linears above, with y [M, N] stored as bf16 (uint16 bit patterns,
+ * 2-byte aligned): the fp32 Fold result rounded to nearest even, as the
+ * page's Fold epilogue writes BF16 (Appendix C.1: linear timing includes the
+ * GEMM/Fold to BF16 output).  With up to 32 rows and K above 16384 these run
+ * the tiled kernel (one pass over K) instead of two narrow launches. */
+rsfp4_status rsfp4_nvfp4_linear_bf16(const void* act, size_t act_bytes, const void* w_packed,
+                                     size_t w_packed_bytes, int64_t M, int64_t N, int64_t K, void* y,
+                                     void* ws, size_t ws_bytes, void* stream);
+rsfp4_status rsfp4_nvfp4_linear_compensated_bf16(const void* act, size_t act_bytes, const void* w_packed,
+                                                 size_t w_packed_bytes, int64_t M, int64_t N, int64_t K,
+                                                 void* y, void* ws, size_t ws_bytes, void* stream);
+rsfp4_status rsfp4_mxfp4_linear_bf16(const void* act, size_t act_bytes, const void* w_packed,
+                                     size_t w_packed_bytes, int64_t M, int64_t N, int64_t K, void* y,
+                                     void* ws, size_t ws_bytes, void* stream);
+rsfp4_status rsfp4_mxfp4_linear_compensated_bf16(const void* act, size_t act_bytes, const void* w_packed,
+                                                 size_t w_packed_bytes, int64_t M, int64_t N, int64_t K,
+                                                 void* y, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------- paper numerics: given tensor scale (NVFP4) --
+ * The operator as the ResServe page's fused quantizer computes it (Appendix
+ * B.2: Eq. 8 and the pack8 description; Algorithm 1), in place of the per-row
+ * dynamic scale of rsfp4_nvfp4_quantize_act_with_residue:
+ *   - one tensor scale alpha (fp32, device memory) for every row of x and of r
+ *     (the page loads calibrated tensor scales, and the residue shares the base
+ *     operand's tensor scale);
+ *   - block byte S_b = E4M3_RNE((Max_b / 6) / alpha), both divisions rounded;
+ *   - multiplier scale = 1 / (alpha * S_b), or 0 when alpha * S_b is 0;
+ *   - element code E2M1_RNE(v * scale), sign from v;
+ *   - residue r = v - e / scale (v when the scale is 0), quantized by the same
+ *     steps with the same alpha.
+ * Records as for rsfp4_nvfp4_quantize_act_with_residue, every record's tensor
+ * scale field holding alpha; the linears above consume them unchanged (the
+ * dequantized value is alpha * S_b * e).  One pass per row, x read once, no row
+ * reduction. */
+rsfp4_status rsfp4_nvfp4_quantize_act_alpha(const void* x, int xt, int64_t M, int64_t K,
+                                            const float* alpha, int with_residue, void* act,
+                                            size_t act_bytes, void* stream);
+
+/* alpha of a whole tensor x [M, K] (dtype xt) when it is derived from the data
+ * (Eq. 8: s_i = Max_i / 6, alpha = max_i s_i / 448): *alpha = ((max|x|) / 6) /
+ * 448 with both divisions rounded; alpha is a device pointer to one float,
+ * written by three kernels in stream order.  M * K <= 2^40. */
+rsfp4_status rsfp4_nvfp4_tensor_alpha(const void* x, int xt, int64_t M, int64_t K, float* alpha,
+                                      void* stream);
 
 /* --------------------------------------- selective compensation (K-Ext) --
  * ResServe Section 5.3 ("Selective Prefill Execution", Eq. 6) and Appendix B.1
