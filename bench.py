@@ -173,6 +173,32 @@ def run_kext(rs, torch, wl, M, ks, steps, warmup):
     return out
 
 
+def paper_numerics_step(rs, torch, S, ref, steps, warmup):
+    """The headline step with the page's operator numerics: the tensor scale
+    alpha computed once from the batch (calibration-like, outside the timing),
+    the shared-alpha multiplier-scale quantizer and the compensated linear with
+    bf16 output."""
+    alpha = rs.nvfp4_tensor_alpha(S.xs[0])
+    ys = [torch.empty((S.M, S.N), dtype=torch.bfloat16, device="cuda") for _ in range(S.R)]
+
+    def quant(i):
+        r = i % S.R
+        rs.nvfp4_quantize_act_alpha(S.xs[r], alpha, True, out=S.acts[r])
+
+    def step(i):
+        r = i % S.R
+        quant(i)
+        rs.fp4_linear_compensated_bf16(S.acts[r], S.blobs[r], S.M, S.N, S.K, 0, out=ys[r])
+
+    t = time_graph(torch, step, steps, warmup)
+    tq = time_graph(torch, quant, steps, warmup)
+    step(0)
+    y = ys[0].float().cpu().numpy()
+    return {"us_per_call": round(t * 1e3, 3), "quant_us": round(tq * 1e3, 3),
+            "nmse_comp_bf16": round(nmse(y, ref), 6), "alpha": float(alpha.item()),
+            "what": "shared tensor scale alpha, multiplier-scale quantizer, bf16 output"}
+
+
 def time_graph(torch, fn, steps, warmup):
     """Run `warmup` eager iterations, capture `steps` iterations in one HIP
     graph, replay it once untimed, then time one replay with HIP events on the
@@ -386,6 +412,8 @@ def main():
     yp = rs.fp4_linear(S.acts[0], S.blobs[0], wl.M, wl.N, wl.K, fmt).cpu().numpy()
     head["nmse_comp"] = nmse(yc, ref)
     head["nmse_plain"] = nmse(yp, ref)
+    if not args.only_headline:
+        head["paper_numerics"] = paper_numerics_step(rs, torch, S, ref, args.steps, args.warmup)
     del S
     torch.cuda.empty_cache()
 
@@ -449,7 +477,7 @@ def main():
         "cpu_baseline": cpu,
     }
     for k in ("plain_us_per_call", "comp_overhead", "gemm_us", "plain_gemm_us", "quant_us",
-              "gemm_GBps", "nmse_comp", "nmse_plain"):
+              "gemm_GBps", "nmse_comp", "nmse_plain", "paper_numerics"):
         if k in head:
             line[k] = round(head[k], 6) if isinstance(head[k], float) else head[k]
     line["step_hbm_frac"] = round(head["GBps"] / HBM_PEAK_GBS, 4)
