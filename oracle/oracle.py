@@ -6,7 +6,8 @@ page (arXiv 2611.08713): Section 2 / Figure 1 for the formats, Appendix B.2
 Eqs. 8-10 for the NVFP4 scale computation, Section 4.2 Eq. 1 and Section 4.3
 Eq. 2 for the compensated product and its Fold; Section 5.3, Eq. 6 and
 Appendix B.1, Eq. 7 for selective compensation (K-Ext); Appendix B.2 (Eq. 8 and
-Algorithm 1) for the paper-numerics NVFP4 quantizer with a tensor scale alpha.
+Algorithm 1) for the paper-numerics NVFP4 quantizer with a tensor scale alpha;
+Section 4.3 Eq. 3 and Section 5.2 for compensated decode attention (ResAttn).
 """
 import ctypes
 import os
@@ -29,6 +30,7 @@ __all__ = [
     "linear", "unpack_codes",
     "channel_abs_sum", "kext_select", "kext_dim", "kext_extend_weight", "kext_quantize_act",
     "nvfp4_alpha", "quantize_row_alg1", "quantize_act_alg1",
+    "kv_quantize", "attention_decode",
 ]
 
 
@@ -84,6 +86,8 @@ def lib():
         L.oracle_nvfp4_quantize_row_alg1.argtypes = [P, i64, f32, P, P, P, P]
         L.oracle_quantize_act_alg1.restype = None
         L.oracle_quantize_act_alg1.argtypes = [P, i64, i64, f32, i32, P, P, P, P, P, P]
+        L.oracle_attention_decode.restype = None
+        L.oracle_attention_decode.argtypes = [P, P, P, P, i64, i64, i64, i64, dbl, P, P]
         _lib = L
     return _lib
 
@@ -317,3 +321,37 @@ def quantize_act_alg1(x, alpha, with_residue=True):
     lib().oracle_quantize_act_alg1(_p(x), M, K, float(alpha), 1 if with_residue else 0, _p(codes), _p(scales),
                                    _p(globs), _p(deq), _p(resid) if with_residue else None, _p(work))
     return {"codes": codes, "scales": scales, "globals": globs, "deq": deq, "resid": resid}
+
+
+# ------------------------------------------------- decode attention (ResAttn) --
+
+def kv_quantize(x, g):
+    """NVFP4 rows of a K or V tensor [..., d] with a given global scale g (the
+    cache's tensor scale): codes [..., d/2], scales [..., d/16], deq [..., d]."""
+    x = _f32(x)
+    shp = x.shape
+    d = shp[-1]
+    rows = x.reshape(-1, d)
+    q = quantize_weight_rows(rows, NVFP4, float(g), True)
+    return {"codes": q["codes"].reshape(shp[:-1] + (d // 2,)),
+            "scales": q["scales"].reshape(shp[:-1] + (d // 16,)),
+            "deq": q["deq"].reshape(shp)}
+
+
+def attention_decode(qb, qr, kd, vd, sm_scale):
+    """binary64 decode attention of one sequence: qb, qr [H_q, d] dequantized
+    query base / residue (qr None: uncompensated), kd, vd [L, H_kv, d]."""
+    qb = _f32(qb)
+    H_q, d = qb.shape
+    kd = _f32(kd)
+    vd = _f32(vd)
+    L, H_kv, _ = kd.shape
+    out = np.zeros((H_q, d), np.float64)
+    work = np.zeros((max(L, 1),), np.float64)
+    qrp = _p(_f32(qr)) if qr is not None else None
+    if qr is not None:
+        qr = _f32(qr)
+        qrp = _p(qr)
+    lib().oracle_attention_decode(_p(qb), qrp, _p(kd), _p(vd), L, H_q, H_kv, d, float(sm_scale), _p(out),
+                                  _p(work))
+    return out

@@ -496,3 +496,45 @@ ORACLE_API void oracle_quantize_act_alg1(const float* x, int64_t M, int64_t K, f
         globals[rr] = alpha;
     }
 }
+
+/* ------------------------------------------- decode attention (ResAttn) ---- */
+/* ResServe Section 4.3 (Eq. 3) and Section 5.2 "ResAttn Execution": for the
+ * query heads sharing one KV head, the scores are Q^ K^T + R^ K^T (base and
+ * quantized residue of each query row against the NVFP4 keys), scaled, folded
+ * before the softmax; the output is softmax(S) V^ with V^ the dequantized
+ * NVFP4 values.  Here in binary64 from dequantized operands:
+ *   qb, qr: [H_q, d] dequantized query base / residue rows of one sequence
+ *           (qr NULL: the uncompensated scores Q^ K^T);
+ *   kd, vd: [L, H_kv, d] dequantized keys / values of its L cached tokens;
+ *   out:    [H_q, d].  Query head h reads KV head h / (H_q / H_kv).
+ * score_t = sm_scale * sum_i (qb_i + qr_i) k_ti, with every product exact in
+ * binary64; p_t = exp(score_t - max_t score_t); out = sum_t p_t v_t / sum_t p_t. */
+ORACLE_API void oracle_attention_decode(const float* qb, const float* qr, const float* kd, const float* vd,
+                                        int64_t L, int64_t H_q, int64_t H_kv, int64_t d, double sm_scale,
+                                        double* out, double* work) {
+    const int64_t G = H_q / H_kv;
+    double* s = work;                         /* L scores */
+    for (int64_t h = 0; h < H_q; ++h) {
+        const int64_t hk = h / G;
+        double mx = -INFINITY;
+        for (int64_t t = 0; t < L; ++t) {
+            const float* k = kd + (t * H_kv + hk) * d;
+            double acc = 0.0;
+            for (int64_t i = 0; i < d; ++i) {
+                acc += (double)qb[h * d + i] * (double)k[i];
+                if (qr) acc += (double)qr[h * d + i] * (double)k[i];
+            }
+            s[t] = sm_scale * acc;
+            if (s[t] > mx) mx = s[t];
+        }
+        double den = 0.0;
+        for (int64_t i = 0; i < d; ++i) out[h * d + i] = 0.0;
+        for (int64_t t = 0; t < L; ++t) {
+            const double p = exp(s[t] - mx);
+            den += p;
+            const float* v = vd + (t * H_kv + hk) * d;
+            for (int64_t i = 0; i < d; ++i) out[h * d + i] += p * (double)v[i];
+        }
+        for (int64_t i = 0; i < d; ++i) out[h * d + i] /= den;
+    }
+}
