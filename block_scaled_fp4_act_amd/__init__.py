@@ -13,7 +13,9 @@ and ``fp4_linear_compensated``.  Selective compensation (K-Ext):
 ``quantize_act_kext`` (and the ``nvfp4_`` / ``mxfp4_`` forms); the product is
 then the plain ``fp4_linear`` over K_eff = kext_dim(K, k).  Paper numerics:
 ``nvfp4_tensor_alpha``, ``nvfp4_quantize_act_alpha`` and the bf16-output
-``fp4_linear_bf16`` / ``fp4_linear_compensated_bf16``.
+``fp4_linear_bf16`` / ``fp4_linear_compensated_bf16``.  Decode attention:
+``kv_cache_write`` and ``resattn_decode`` (queries quantized with
+``nvfp4_quantize_act_with_residue``).
 """
 import ctypes
 
@@ -212,6 +214,51 @@ def nvfp4_quantize_act_alpha(x, alpha, with_residue=True, out=None):
         out = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
     _check(lib().rsfp4_nvfp4_quantize_act_alpha(_ptr(x), _dtype_code(x), M, K, _ptr(alpha),
                                                 1 if with_residue else 0, _ptr(out), out.numel(), _stream(x)))
+    return out
+
+
+# ------------------------------------------------ decode attention (ResAttn) --
+
+def kv_page_bytes(H_kv, D):
+    return int(lib().rsfp4_kv_page_bytes(H_kv, D))
+
+
+def kv_cache_write(k, v, slots, cache, k_scale=1.0, v_scale=1.0):
+    """Quantize k, v [T, H_kv, D] (cuda, fp32/bf16) into the paged NVFP4 cache
+    (uint8 cuda tensor) at slots [T] (int32: page * 32 + row)."""
+    import torch
+    assert k.is_cuda and k.dim() == 3 and k.is_contiguous() and v.shape == k.shape and v.dtype == k.dtype
+    assert slots.is_cuda and slots.dtype == torch.int32 and cache.is_cuda and cache.dtype == torch.uint8
+    T, H_kv, D = k.shape
+    _check(lib().rsfp4_kv_cache_write(_ptr(k), _ptr(v.contiguous()), _dtype_code(k), T, H_kv, D, _ptr(slots),
+                                      float(k_scale), float(v_scale), _ptr(cache), cache.numel(), _stream(k)))
+    return cache
+
+
+def resattn_splits(B, H_kv, max_seq_len):
+    return int(lib().rsfp4_resattn_splits(B, H_kv, max_seq_len))
+
+
+def resattn_decode(q_act, cache, block_table, seq_lens, max_seq_len, B, H_q, H_kv, D, compensated=True,
+                   k_scale=1.0, v_scale=1.0, sm_scale=None, splits=0, out=None, out_bf16=False, ws=None):
+    """Compensated (or plain) decode attention; returns out [B, H_q, D]."""
+    import math
+    import torch
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    if splits <= 0:
+        splits = resattn_splits(B, H_kv, max_seq_len)
+    need = int(lib().rsfp4_resattn_workspace_bytes(B, H_q, D, splits))
+    if need and ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=cache.device)
+    if out is None:
+        out = torch.empty((B, H_q, D), dtype=torch.bfloat16 if out_bf16 else torch.float32, device=cache.device)
+    max_pages = block_table.shape[1]
+    _check(lib().rsfp4_resattn_decode(_ptr(q_act), q_act.numel(), 1 if compensated else 0, _ptr(cache),
+                                      cache.numel(), _ptr(block_table), max_pages, _ptr(seq_lens), max_seq_len, B,
+                                      H_q, H_kv, D, float(k_scale), float(v_scale), float(sm_scale), int(splits),
+                                      _ptr(out), 1 if out_bf16 else 0, _ptr(ws) if ws is not None else None,
+                                      ws.numel() if ws is not None else 0, _stream(cache)))
     return out
 
 

@@ -36,6 +36,12 @@ SIGNATURES = {
     "rsfp4_mxfp4_linear_compensated_bf16": (INT, [P, SZ, P, SZ, I64, I64, I64, P, P, SZ, P]),
     "rsfp4_nvfp4_quantize_act_alpha": (INT, [P, INT, I64, I64, P, INT, P, SZ, P]),
     "rsfp4_nvfp4_tensor_alpha": (INT, [P, INT, I64, I64, P, P]),
+    "rsfp4_kv_page_bytes": (SZ, [I64, I64]),
+    "rsfp4_kv_cache_write": (INT, [P, P, INT, I64, I64, I64, P, ctypes.c_float, ctypes.c_float, P, SZ, P]),
+    "rsfp4_resattn_splits": (INT, [I64, I64, I64]),
+    "rsfp4_resattn_workspace_bytes": (SZ, [I64, I64, I64, INT]),
+    "rsfp4_resattn_decode": (INT, [P, SZ, INT, P, SZ, P, I64, P, I64, I64, I64, I64, I64, ctypes.c_float,
+                                   ctypes.c_float, ctypes.c_float, INT, P, INT, P, SZ, P]),
     "rsfp4_kext_dim": (I64, [I64, INT]),
     "rsfp4_channel_abs_sum": (INT, [P, INT, I64, I64, P, INT, P]),
     "rsfp4_kext_select": (INT, [P, I64, INT, P, P]),

@@ -233,6 +233,16 @@ rsfp4_status quantize_alpha(const void* x, int xt, int64_t M, int64_t K, const f
                       "quantize launch");
 }
 
+// ---- decode attention ----
+bool attn_dims_ok(int64_t H_q, int64_t H_kv, int64_t D) {
+    return (D == 128 || D == 256) && H_kv >= 1 && H_q >= H_kv && H_q % H_kv == 0 && H_q / H_kv <= 8 &&
+           H_q <= 4096;
+}
+
+int64_t attn_ws_bytes(int64_t B, int64_t H_q, int64_t D, int splits) {
+    return splits > 1 ? B * H_q * (int64_t)splits * (D + 2) * 4 : 0;
+}
+
 }  // namespace
 
 extern "C" {
@@ -411,6 +421,82 @@ rsfp4_status rsfp4_mxfp4_linear_compensated_bf16(const void* act, size_t act_byt
                                                  size_t w_packed_bytes, int64_t M, int64_t N, int64_t K, void* y,
                                                  void* ws, size_t ws_bytes, void* stream) {
     return linear(RSFP4_MXFP4, true, act, act_bytes, w_packed, w_packed_bytes, M, N, K, y, true, ws, ws_bytes, stream);
+}
+
+size_t rsfp4_kv_page_bytes(int64_t H_kv, int64_t D) {
+    if (H_kv < 1 || (D != 128 && D != 256)) return 0;
+    return (size_t)kv_page_bytes(H_kv, D);
+}
+
+rsfp4_status rsfp4_kv_cache_write(const void* k, const void* v, int xt, int64_t T, int64_t H_kv, int64_t D,
+                                  const int32_t* slots, float k_scale, float v_scale, void* cache, size_t cache_bytes,
+                                  void* stream) {
+    g_err[0] = 0;
+    if (!k || !v || !slots || !cache) return fail(RSFP4_ERR_NULL, "k, v, slots and cache must be non-NULL");
+    if (xt != RSFP4_F32 && xt != RSFP4_BF16) return fail(RSFP4_ERR_FORMAT, "unknown dtype %d", xt);
+    if (H_kv < 1 || H_kv > 1024 || (D != 128 && D != 256))
+        return fail(RSFP4_ERR_SHAPE, "H_kv = %lld, D = %lld: D must be 128 or 256", (long long)H_kv, (long long)D);
+    if (T < 1 || T > ((int64_t)1 << 31) / (H_kv * 2 * (D / 16)))
+        return fail(RSFP4_ERR_SHAPE, "T = %lld outside [1, 2^31 / (H_kv * D / 8)]", (long long)T);
+    if (!(k_scale > 0.0f) || !(v_scale > 0.0f)) return fail(RSFP4_ERR_SHAPE, "k_scale and v_scale must be > 0");
+    if (!aligned(cache, 256) || !aligned(k, 4) || !aligned(v, 4) || !aligned(slots, 4))
+        return fail(RSFP4_ERR_ALIGN, "cache must be 256-byte, k, v and slots 4-byte aligned");
+    const int64_t pb = kv_page_bytes(H_kv, D);
+    const int64_t num_pages = (int64_t)(cache_bytes / (size_t)pb);
+    if (num_pages < 1) return fail(RSFP4_ERR_BUFFER_TOO_SMALL, "cache holds %zu bytes, one page needs %lld", cache_bytes, (long long)pb);
+    return hip_status(launch_kv_write(xt == RSFP4_BF16, k, v, slots, T, (int)H_kv, (int)D, k_scale, v_scale, cache,
+                                      num_pages, (hipStream_t)stream),
+                      "kv write launch");
+}
+
+int rsfp4_resattn_splits(int64_t B, int64_t H_kv, int64_t max_seq_len) {
+    int cus = 0;
+    if (num_cus(&cus) != RSFP4_OK || B < 1 || H_kv < 1 || max_seq_len < 1) return 1;
+    return attn_auto_splits(B, H_kv, max_seq_len, cus);
+}
+
+size_t rsfp4_resattn_workspace_bytes(int64_t B, int64_t H_q, int64_t D, int splits) {
+    if (B < 1 || H_q < 1 || (D != 128 && D != 256) || splits < 1) return 0;
+    return (size_t)attn_ws_bytes(B, H_q, D, splits);
+}
+
+rsfp4_status rsfp4_resattn_decode(const void* q_act, size_t q_act_bytes, int compensated, const void* cache,
+                                  size_t cache_bytes, const int32_t* block_table, int64_t max_pages,
+                                  const int32_t* seq_lens, int64_t max_seq_len, int64_t B, int64_t H_q, int64_t H_kv,
+                                  int64_t D, float k_scale, float v_scale, float sm_scale, int splits, void* out,
+                                  int out_bf16, void* ws, size_t ws_bytes, void* stream) {
+    g_err[0] = 0;
+    if (!q_act || !cache || !block_table || !seq_lens || !out)
+        return fail(RSFP4_ERR_NULL, "q_act, cache, block_table, seq_lens and out must be non-NULL");
+    if (!attn_dims_ok(H_q, H_kv, D))
+        return fail(RSFP4_ERR_SHAPE, "H_q = %lld, H_kv = %lld, D = %lld: D in {128, 256}, H_q a multiple of H_kv, "
+                    "at most 8 query heads per KV head", (long long)H_q, (long long)H_kv, (long long)D);
+    if (B < 1 || B > 65535 || max_pages < 1 || max_seq_len < 1 || max_seq_len > max_pages * 32 ||
+        max_seq_len > ((int64_t)1 << 30))
+        return fail(RSFP4_ERR_SHAPE, "B = %lld, max_pages = %lld, max_seq_len = %lld: need 1 <= B <= 65535 and "
+                    "1 <= max_seq_len <= 32 * max_pages", (long long)B, (long long)max_pages, (long long)max_seq_len);
+    int cus = 0;
+    rsfp4_status st = num_cus(&cus);
+    if (st != RSFP4_OK) return st;
+    if (splits <= 0) splits = attn_auto_splits(B, H_kv, max_seq_len, cus);
+    if (splits > 4096) return fail(RSFP4_ERR_SHAPE, "splits = %d above 4096", splits);
+    if (!aligned(q_act, 16) || !aligned(cache, 256) || !aligned(out, out_bf16 ? 2 : 4) || !aligned(ws, 4) ||
+        !aligned(block_table, 4) || !aligned(seq_lens, 4))
+        return fail(RSFP4_ERR_ALIGN, "q_act 16-, cache 256-byte aligned; out, ws, tables element aligned");
+    const int64_t rb = act_row_bytes(RSFP4_NVFP4, D);
+    const size_t need_q = (size_t)rb * (size_t)(B * H_q) * (compensated ? 2 : 1);
+    if (q_act_bytes < need_q) return fail(RSFP4_ERR_BUFFER_TOO_SMALL, "q_act holds %zu bytes, needs %zu", q_act_bytes, need_q);
+    const int64_t pb = kv_page_bytes(H_kv, D);
+    const int64_t num_pages = (int64_t)(cache_bytes / (size_t)pb);
+    if (num_pages < 1) return fail(RSFP4_ERR_BUFFER_TOO_SMALL, "cache holds %zu bytes, one page needs %lld", cache_bytes, (long long)pb);
+    const size_t need_ws = (size_t)attn_ws_bytes(B, H_q, D, splits);
+    if (need_ws > 0 && (!ws || ws_bytes < need_ws))
+        return fail(RSFP4_ERR_BUFFER_TOO_SMALL, "workspace holds %zu bytes, %d splits need %zu", ws_bytes, splits, need_ws);
+    return hip_status(launch_resattn(q_act, rb, compensated ? 1 : 0, cache, num_pages, block_table, max_pages,
+                                     seq_lens, (int)B, (int)H_q, (int)H_kv, (int)D, k_scale, v_scale, sm_scale,
+                                     splits, max_seq_len, out, out_bf16 ? 1 : 0, static_cast<float*>(ws),
+                                     (hipStream_t)stream),
+                      "attention launch");
 }
 
 }  // extern "C"

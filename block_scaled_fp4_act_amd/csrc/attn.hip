@@ -1,0 +1,448 @@
+// attn.hip -- residue-compensated decode attention (ResAttn) over a paged
+// NVFP4 KV cache, for gfx950.
+//
+// What is computed (ResServe, arXiv 2611.08713, Section 4.3 Eq. 3 and Section
+// 5.2 "ResAttn Execution"): for the G query heads sharing one KV head, the
+// scores are the products of the query's NVFP4 base Q^ and quantized residue
+// R^ with the cached NVFP4 keys, added before the softmax, and the output is
+// softmax(S) V^ over the cached NVFP4 values:
+//   S[g, t] = k_scale * sm_scale * (s_q[g] (Q^_g . K^_t) + s_r[g] (R^_g . K^_t))
+//   O[g]    = v_scale * sum_t p[g, t] V^_t / sum_t p[g, t],  p = exp(S - max S)
+// The query rows come from the activation quantizer (base and residue records,
+// each with its own tensor scale); keys and values are read from the cache in
+// its own layout, 16-element E4M3 scale blocks along the head dimension.
+//
+// Mapping to the matrix cores (one wave per (sequence, KV head, KV split)):
+//   * QK: the 16x16x32 f16 MFMA takes a 16-token key tile as A and the 16 query
+//     rows (2g = base, 2g+1 = residue of head g; the operand swap of Section
+//     5.1) as B, so a lane ends up with 4 tokens' scores of one query row and
+//     its neighbour lane holds the partner row: the fold of base and residue is
+//     one lane swap and an add.  NVFP4 values enter as exact f16 (e * S_b).
+//   * online softmax in the base-2 domain (scores pre-multiplied by log2 e),
+//     row maxima and sums over the four lanes that share a query row.
+//   * PV: the page cannot feed the MFMA's token dimension directly (the scale
+//     blocks run along d, the reduction along tokens -- the page converts V to
+//     FP8 on chip for this).  Here each lane loads 4 bytes (8 d-elements) of 8
+//     tokens, dequantizes them to exact f16 and transposes the 8 x 8 block in
+//     its own registers, so P (already in the A-operand layout the QK output
+//     leaves) times V runs on the same f16 MFMA with fp32 accumulation.
+//   * KV splits: a split writes unnormalized partial outputs with its row
+//     maxima and sums; a second kernel combines them (Section 5.2: splits
+//     expose parallelism when batch x KV heads give too few work items).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "codec.h"
+#include "kernels.h"
+#include "layout.h"
+
+namespace rsfp4 {
+
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kRsrcWord3 = 0x00020000;     // raw buffer, 32-bit dwords, range checked
+
+// E4M3 byte -> S_b * 2^-8 as f16 (the exponent and mantissa fields line up).
+__device__ __forceinline__ _Float16 scale_h(uint32_t byte) {
+    return __builtin_bit_cast(_Float16, (unsigned short)((byte & 0x7Fu) << 7));
+}
+
+// 8 E2M1 codes (low nibble first) -> 8 exact f16 values e * S_b: the FP4
+// conversion supplies the factor 2^8, a packed f16 multiply S_b * 2^-8.
+__device__ __forceinline__ half8 dequant8(uint32_t w, _Float16 s) {
+    half2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 0);
+    half2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 1);
+    half2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 2);
+    half2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 3);
+    const half2v s2 = {s, s};
+    p0 *= s2; p1 *= s2; p2 *= s2; p3 *= s2;
+    half8 r;
+    r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+    r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+    return r;
+}
+
+__device__ __forceinline__ uint32_t word(const uint4& v, int u) {
+    return u == 0 ? v.x : (u == 1 ? v.y : (u == 2 ? v.z : v.w));
+}
+
+__device__ __forceinline__ uint4 ld128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;   // quad_perm [1,0,3,2]: lane l <-> l ^ 1
+
+// Reductions over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one query row).
+__device__ __forceinline__ float rowgroup_max(float v) {
+    v = fmaxf(v, __shfl_xor(v, 16, 64));
+    return fmaxf(v, __shfl_xor(v, 32, 64));
+}
+__device__ __forceinline__ float rowgroup_sum(float v) {
+    v += __shfl_xor(v, 16, 64);
+    return v + __shfl_xor(v, 32, 64);
+}
+
+struct AttnArgs {
+    const uint8_t* q;          // query records: B*H_q base rows, then (comp) B*H_q residue rows
+    int64_t q_row_bytes;
+    const uint8_t* cache;
+    int64_t page_bytes;        // H_kv * 36 * D
+    int64_t num_pages;
+    const int32_t* block_table;
+    int64_t max_pages;         // columns of block_table
+    const int32_t* seq_lens;
+    int B, H_q, H_kv, G;
+    int comp;
+    float score_mult;          // k_scale * sm_scale * log2(e)
+    float v_scale;
+    int splits;
+    int pages_per_split;
+    void* out;
+    int out_bf16;
+    float* ws_o;               // [B*H_q][splits][D] partial outputs (splits > 1)
+    float* ws_ml;              // [B*H_q][splits][2] row maximum (base 2) and sum
+};
+
+// Page layout, per KV head (36 * D bytes, KV heads consecutive in a page):
+//   [0, 16D)    K codes, token-major: token t at t * D/2 (element 2k low nibble)
+//   [16D, 18D)  K scales: token t at 16D + t * D/16
+//   [18D, 34D)  V codes, token-major
+//   [34D, 36D)  V scales
+template <int D>
+__global__ __launch_bounds__(64) void resattn_kernel(AttnArgs p) {
+    constexpr int NC = D / 128;          // 16-byte chunks of a row per lane
+    constexpr int KS = D / 32;           // f16 MFMA k-steps over the head dimension
+    const int lane = threadIdx.x;
+    const int i = lane & 15, j = lane >> 4;
+    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int L = p.seq_lens[b] > 0 ? p.seq_lens[b] : 0;
+    const int npages = (int)((L + 31) >> 5) < p.max_pages ? (L + 31) >> 5 : (int)p.max_pages;
+    const int pg0 = split * p.pages_per_split;
+    const int pg1 = pg0 + p.pages_per_split < npages ? pg0 + p.pages_per_split : npages;
+
+    // ---- query operand (B of QK): row i = 2g (base) or 2g+1 (residue) of head h*G + g ----
+    const int g = i >> 1;
+    const bool qvalid = g < p.G && ((i & 1) == 0 || p.comp);
+    half8 qf[KS];
+    float qs = 0.0f;
+    {
+        const int64_t row = (int64_t)b * p.H_q + (int64_t)h * p.G + g + ((i & 1) ? (int64_t)p.B * p.H_q : 0);
+        const uint8_t* rec = p.q + (qvalid ? row : 0) * p.q_row_bytes;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            uint4 w = make_uint4(0u, 0u, 0u, 0u);
+            uint32_t sc = 0u;
+            if (qvalid) {
+                w = *reinterpret_cast<const uint4*>(rec + kActHead + 64 * c + 16 * j);
+                sc = *reinterpret_cast<const uint16_t*>(rec + kActHead + D / 2 + 8 * c + 2 * j);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) qf[4 * c + u] = dequant8(word(w, u), scale_h(u < 2 ? (sc & 0xFFu) : (sc >> 8)));
+        }
+        if (qvalid) qs = *reinterpret_cast<const float*>(rec);
+    }
+
+    // V tokens of this lane's k-slots: the order the QK output leaves P in
+    int vtok[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) vtok[u] = u < 4 ? 4 * j + u : 16 + 4 * j + (u - 4);
+
+    floatx4 o[NC][8];
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[c][e] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    float m = -__builtin_inff(), l = 0.0f;
+
+    struct Raw {
+        uint4 kc[2][NC];
+        uint32_t ks[2][NC];
+        uint32_t vc[8][NC];
+        uint32_t vs[8][NC];
+    };
+    const int64_t hb = (int64_t)h * 36 * D;
+    auto load_page = [&](int pg, Raw& R) {
+        const int64_t pidx = pg < pg1 ? p.block_table[(int64_t)b * p.max_pages + pg] : -1;
+        const bool ok = pidx >= 0 && pidx < p.num_pages;
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(p.cache + (ok ? pidx : 0) * p.page_bytes + hb), (short)0, ok ? 36 * D : 0, kRsrcWord3);
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            const int t = 16 * tt + i;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                R.kc[tt][c] = ld128(r, (uint32_t)(t * (D / 2) + 64 * c + 16 * j));
+                R.ks[tt][c] = __builtin_amdgcn_raw_buffer_load_b16(r, (uint32_t)(16 * D + t * (D / 16) + 8 * c + 2 * j), 0, 0);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                R.vc[u][c] = __builtin_amdgcn_raw_buffer_load_b32(r, (uint32_t)(18 * D + vtok[u] * (D / 2) + 64 * c + 4 * i), 0, 0);
+                R.vs[u][c] = __builtin_amdgcn_raw_buffer_load_b8(r, (uint32_t)(34 * D + vtok[u] * (D / 16) + 8 * c + (i >> 1)), 0, 0);
+            }
+        }
+    };
+
+    Raw cur, nxt;
+    if (pg0 < pg1) load_page(pg0, cur);
+    for (int pg = pg0; pg < pg1; ++pg) {
+        load_page(pg + 1, nxt);                 // past pg1: a zero-sized resource (no traffic)
+
+        // ---- scores of the page's 32 tokens: two 16-token tiles ----
+        floatx4 acc[2];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            acc[tt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const uint32_t sc = cur.ks[tt][s >> 2];
+                const half8 a = dequant8(word(cur.kc[tt][s >> 2], s & 3), scale_h((s & 3) < 2 ? (sc & 0xFFu) : (sc >> 8)));
+                acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qf[s], acc[tt], 0, 0, 0);
+            }
+        }
+        // fold base and residue rows (neighbour lanes), scale, mask past L
+        float sc[2][4];
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float mine = acc[tt][r] * qs;
+                const float fold = mine + dpp_f<kDppXor1>(mine);
+                const int tok = 32 * pg + 16 * tt + 4 * j + r;
+                sc[tt][r] = tok < L ? fold * p.score_mult : -__builtin_inff();
+                mx = fmaxf(mx, sc[tt][r]);
+            }
+        mx = rowgroup_max(mx);
+        const float m_new = fmaxf(m, mx);
+        const bool live = m_new > -__builtin_inff();
+        const float corr = live ? __builtin_amdgcn_exp2f(m - m_new) : 1.0f;
+        float ps = 0.0f;
+        half8 pa;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float pv = live ? __builtin_amdgcn_exp2f(sc[tt][r] - m_new) : 0.0f;
+                const _Float16 ph = (_Float16)pv;
+                pa[4 * tt + r] = ph;
+                ps += pv;
+            }
+        l = l * corr + rowgroup_sum(ps);
+        m = m_new;
+
+        // rescale the accumulators: lane holds query rows 4j + r
+        float cr[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) cr[r] = __shfl(corr, 4 * j + r, 64);
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) o[c][e][r] *= cr[r];
+
+        // ---- P V: 8 tokens x 8 d-elements per lane, transposed in registers.
+        // Tokens past L have p = 0; their cache bytes (whatever they hold)
+        // decode to finite f16 (FP4 codes are finite, and the scale conversion
+        // maps every byte to a finite value), so they add exact zeros. ----
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            half8 vv[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) vv[u] = dequant8(cur.vc[u][c], scale_h(cur.vs[u][c]));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                half8 bv;
+#pragma unroll
+                for (int u = 0; u < 8; ++u) bv[u] = vv[u][e];
+                o[c][e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, bv, o[c][e], 0, 0, 0);
+            }
+        }
+        cur = nxt;
+    }
+
+    // ---- outputs: rows 4j + r of column d = 128c + 8i + e (even rows = heads) ----
+    float lr[4], mr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        lr[r] = __shfl(l, 4 * j + r, 64);
+        mr[r] = __shfl(m, 4 * j + r, 64);
+    }
+    const int64_t D64 = D;
+#pragma unroll
+    for (int r = 0; r < 4; r += 2) {          // even rows only
+        const int q = 4 * j + r;
+        const int gg = q >> 1;
+        if (gg >= p.G) continue;
+        const int64_t head = (int64_t)b * p.H_q + (int64_t)h * p.G + gg;
+        if (p.splits == 1) {
+            const float inv = lr[r] > 0.0f ? p.v_scale / lr[r] : 0.0f;
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    store_y(p.out, head * D64 + 128 * c + 8 * i + e, o[c][e][r] * inv, p.out_bf16);
+        } else {
+            float* dst = p.ws_o + (head * p.splits + split) * D64;
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) dst[128 * c + 8 * i + e] = o[c][e][r] * p.v_scale;
+            if (i == 0) {
+                p.ws_ml[(head * p.splits + split) * 2 + 0] = mr[r];
+                p.ws_ml[(head * p.splits + split) * 2 + 1] = lr[r];
+            }
+        }
+    }
+}
+
+// Combine the splits of one head: weights 2^(m_s - M) over the splits' row
+// maxima (base 2); empty splits (m = -inf) weigh 0.
+template <int D>
+__global__ __launch_bounds__(D) void resattn_reduce_kernel(AttnArgs p) {
+    const int64_t head = blockIdx.x;
+    const int d = threadIdx.x;
+    const float* ml = p.ws_ml + head * p.splits * 2;
+    float M = -__builtin_inff();
+    for (int s = 0; s < p.splits; ++s) M = fmaxf(M, ml[2 * s]);
+    float num = 0.0f, den = 0.0f;
+    if (M > -__builtin_inff()) {
+        for (int s = 0; s < p.splits; ++s) {
+            const float w = __builtin_amdgcn_exp2f(ml[2 * s] - M);
+            num += w * p.ws_o[(head * p.splits + s) * D + d];
+            den += w * ml[2 * s + 1];
+        }
+    }
+    store_y(p.out, head * D + d, den > 0.0f ? num / den : 0.0f, p.out_bf16);
+}
+
+template <int D>
+hipError_t launch_attn_d(const AttnArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL(resattn_kernel<D>, dim3((unsigned)a.splits, (unsigned)a.H_kv, (unsigned)a.B), dim3(64), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.splits == 1) return e;
+    hipLaunchKernelGGL(resattn_reduce_kernel<D>, dim3((unsigned)(a.B * a.H_q)), dim3(D), 0, s, a);
+    return hipGetLastError();
+}
+
+// ---- KV cache write: one thread per (token, head, K|V, 16-block) ----
+template <typename TIn>
+__global__ __launch_bounds__(256) void kv_write_kernel(const TIn* __restrict__ k, const TIn* __restrict__ v,
+                                                       const int32_t* __restrict__ slots, int64_t T, int H_kv, int D,
+                                                       float k_scale, float v_scale, uint8_t* __restrict__ cache,
+                                                       int64_t page_bytes, int64_t num_pages) {
+    const int nb = D / 16;
+    const int64_t per_tok = (int64_t)H_kv * 2 * nb;
+    const int64_t gid = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (gid >= T * per_tok) return;
+    const int64_t t = gid / per_tok;
+    const int rem = (int)(gid % per_tok);
+    const int hh = rem / (2 * nb), kv = (rem / nb) & 1, blk = rem % nb;
+    const int64_t slot = slots[t];
+    if (slot < 0 || slot >= num_pages * 32) return;          // padding or out of the cache: skipped
+    const int64_t page = slot >> 5;
+    const int off = (int)(slot & 31);
+    const TIn* src = (kv ? v : k) + (t * H_kv + hh) * D + 16 * blk;
+    float x[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        if (sizeof(TIn) == 2)
+            x[e] = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(src)[e] << 16);
+        else
+            x[e] = reinterpret_cast<const float*>(src)[e];
+    }
+    const float gs = kv ? v_scale : k_scale;
+    float bm = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) bm = fmaxf(bm, fabsf(x[e]));
+    const uint32_t sbyte = e4m3_encode(bm / (6.0f * gs));
+    const float st = e4m3_val(sbyte) * gs;
+    const float sd = st != 0.0f ? st : __builtin_inff();
+    uint32_t w0 = 0u, w1 = 0u;
+    w0 = e2m1_pack2<0>(w0, x[0] / sd, x[1] / sd, 1.0f);
+    w0 = e2m1_pack2<1>(w0, x[2] / sd, x[3] / sd, 1.0f);
+    w0 = e2m1_pack2<2>(w0, x[4] / sd, x[5] / sd, 1.0f);
+    w0 = e2m1_pack2<3>(w0, x[6] / sd, x[7] / sd, 1.0f);
+    w1 = e2m1_pack2<0>(w1, x[8] / sd, x[9] / sd, 1.0f);
+    w1 = e2m1_pack2<1>(w1, x[10] / sd, x[11] / sd, 1.0f);
+    w1 = e2m1_pack2<2>(w1, x[12] / sd, x[13] / sd, 1.0f);
+    w1 = e2m1_pack2<3>(w1, x[14] / sd, x[15] / sd, 1.0f);
+    uint8_t* base = cache + page * page_bytes + (int64_t)hh * 36 * D + (kv ? 18 * D : 0);
+    *reinterpret_cast<uint2*>(base + off * (D / 2) + 8 * blk) = make_uint2(w0, w1);
+    base[16 * D + off * (D / 16) + blk] = (uint8_t)sbyte;
+}
+
+}  // namespace
+
+int64_t kv_page_bytes(int64_t H_kv, int64_t D) { return H_kv * 36 * D; }
+
+hipError_t launch_kv_write(int xt_bf16, const void* k, const void* v, const int32_t* slots, int64_t T, int H_kv,
+                           int D, float k_scale, float v_scale, void* cache, int64_t num_pages, hipStream_t s) {
+    const int64_t n = T * H_kv * 2 * (D / 16);
+    const unsigned blocks = (unsigned)((n + 255) / 256);
+    const int64_t pb = kv_page_bytes(H_kv, D);
+    if (xt_bf16)
+        hipLaunchKernelGGL(kv_write_kernel<uint16_t>, dim3(blocks), dim3(256), 0, s, static_cast<const uint16_t*>(k),
+                           static_cast<const uint16_t*>(v), slots, T, H_kv, D, k_scale, v_scale,
+                           static_cast<uint8_t*>(cache), pb, num_pages);
+    else
+        hipLaunchKernelGGL(kv_write_kernel<float>, dim3(blocks), dim3(256), 0, s, static_cast<const float*>(k),
+                           static_cast<const float*>(v), slots, T, H_kv, D, k_scale, v_scale,
+                           static_cast<uint8_t*>(cache), pb, num_pages);
+    return hipGetLastError();
+}
+
+int attn_auto_splits(int64_t B, int64_t H_kv, int64_t max_seq_len, int num_cus) {
+    // Preset rule: aim for ~8 waves per compute unit, at least 8 pages per split.
+    const int64_t pages = (max_seq_len + 31) / 32;
+    const int64_t items = B * H_kv;
+    int64_t want = (8 * (int64_t)num_cus + items - 1) / items;
+    const int64_t cap = pages / 8 > 1 ? pages / 8 : 1;
+    if (want > cap) want = cap;
+    if (want < 1) want = 1;
+    if (want > 1024) want = 1024;
+    return (int)want;
+}
+
+hipError_t launch_resattn(const void* q_act, int64_t q_row_bytes, int comp, const void* cache, int64_t num_pages,
+                          const int32_t* block_table, int64_t max_pages, const int32_t* seq_lens, int B, int H_q,
+                          int H_kv, int D, float k_scale, float v_scale, float sm_scale, int splits,
+                          int64_t max_seq_len, void* out, int out_bf16, float* ws, hipStream_t s) {
+    AttnArgs a;
+    a.q = static_cast<const uint8_t*>(q_act);
+    a.q_row_bytes = q_row_bytes;
+    a.cache = static_cast<const uint8_t*>(cache);
+    a.page_bytes = kv_page_bytes(H_kv, D);
+    a.num_pages = num_pages;
+    a.block_table = block_table;
+    a.max_pages = max_pages;
+    a.seq_lens = seq_lens;
+    a.B = B; a.H_q = H_q; a.H_kv = H_kv; a.G = H_q / H_kv;
+    a.comp = comp;
+    a.score_mult = k_scale * sm_scale * 1.4426950408889634f;
+    a.v_scale = v_scale;
+    a.splits = splits;
+    const int64_t pages = (max_seq_len + 31) / 32;
+    a.pages_per_split = (int)((pages + splits - 1) / splits);
+    a.out = out;
+    a.out_bf16 = out_bf16;
+    a.ws_o = ws;
+    a.ws_ml = ws + (int64_t)B * H_q * splits * D;
+    if (D == 128) return launch_attn_d<128>(a, s);
+    return launch_attn_d<256>(a, s);
+}
+
+}  // namespace rsfp4

@@ -11,6 +11,16 @@ hipError_t launch_quantize_act(int fmt, int xt_bf16, const void* x, int M, int64
 hipError_t launch_prepack(int fmt, int wt_bf16, const void* W, int64_t N, int64_t K, void* blob,
                           hipStream_t s);
 
+// Compensated decode attention (ResAttn) over the paged NVFP4 KV cache.
+int64_t kv_page_bytes(int64_t H_kv, int64_t D);
+hipError_t launch_kv_write(int xt_bf16, const void* k, const void* v, const int32_t* slots, int64_t T, int H_kv,
+                           int D, float k_scale, float v_scale, void* cache, int64_t num_pages, hipStream_t s);
+int attn_auto_splits(int64_t B, int64_t H_kv, int64_t max_seq_len, int num_cus);
+hipError_t launch_resattn(const void* q_act, int64_t q_row_bytes, int comp, const void* cache, int64_t num_pages,
+                          const int32_t* block_table, int64_t max_pages, const int32_t* seq_lens, int B, int H_q,
+                          int H_kv, int D, float k_scale, float v_scale, float sm_scale, int splits,
+                          int64_t max_seq_len, void* out, int out_bf16, float* ws, hipStream_t s);
+
 // Selective compensation (K-Ext): extended quantizer, [W | W_S] prepack and the
 // calibration kernels.
 hipError_t launch_quantize_act_kext(int fmt, int xt_bf16, const void* x, int M, int64_t K,

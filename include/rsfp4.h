@@ -285,6 +285,65 @@ rsfp4_status rsfp4_mxfp4_quantize_act_kext(const void* x, int xt, int64_t M, int
                                            const uint8_t* masks, int k, void* act, size_t act_bytes,
                                            void* stream);
 
+/* ------------------------------------ compensated decode attention --------
+ * ResAttn (ResServe Section 4.3, Eq. 3; Section 5.2 "ResAttn Execution"): one
+ * decode token per sequence; the query heads of a KV head (grouped-query
+ * attention, G = H_q / H_kv <= 8) are quantized to an NVFP4 base and residue,
+ * both are multiplied with the cached NVFP4 keys, and their scores are added
+ * before the softmax; the output is softmax(S) V^ over the cached values:
+ *   S[h, t] = k_scale * sm_scale * (s_q[h] (Q^_h . K^_t) + s_r[h] (R^_h . K^_t))
+ *   out[h]  = v_scale * sum_t p[h, t] V^_t / sum_t p[h, t],  p = exp(S - max S)
+ * where Q^_h, R^_h, K^_t, V^_t are FP4 codes times their E4M3 block scales
+ * and s_q, s_r the query rows' tensor scales.
+ *
+ * KV cache: pages of 32 tokens; a page holds, for each KV head in turn,
+ * 36 * D bytes: K codes [32][D/2] (token-major, element 2k in the low nibble),
+ * K block scales [32][D/16] (E4M3, 16 elements along the head dimension), V
+ * codes [32][D/2], V scales [32][D/16].  Token t of a sequence sits at page
+ * block_table[b][t / 32], row t % 32.  k_scale / v_scale are the cache's
+ * global scales (the page's tests use 1.0): a stored value is k_scale * S_b * e.
+ * D is 128 or 256. */
+size_t rsfp4_kv_page_bytes(int64_t H_kv, int64_t D);
+
+/* Quantize and write T tokens' keys and values (k, v: [T, H_kv, D], dtype xt,
+ * row-major) into the cache: token t goes to slot slots[t] = page * 32 + row
+ * (slots < 0 or beyond the cache are skipped).  Each 16-element block:
+ * S_b = E4M3_RNE(max|x| / (6 g)), codes E2M1_RNE(x / (S_b g)), g = k_scale or
+ * v_scale (> 0).  The page's timings exclude cache construction; this call is
+ * how the cache is built here.  cache: device, 256-byte aligned, cache_bytes /
+ * rsfp4_kv_page_bytes pages. */
+rsfp4_status rsfp4_kv_cache_write(const void* k, const void* v, int xt, int64_t T, int64_t H_kv, int64_t D,
+                                  const int32_t* slots, float k_scale, float v_scale, void* cache,
+                                  size_t cache_bytes, void* stream);
+
+/* KV splits the preset rule picks (about 8 waves per compute unit, at least 8
+ * pages per split; ResServe Section 5.2: preset rules from batch size, KV heads,
+ * sequence length and the unit count), and the workspace they need (0 for one
+ * split): B * H_q * splits * (D + 2) * 4 bytes. */
+int rsfp4_resattn_splits(int64_t B, int64_t H_kv, int64_t max_seq_len);
+size_t rsfp4_resattn_workspace_bytes(int64_t B, int64_t H_q, int64_t D, int splits);
+
+/* Decode attention of B sequences.
+ *   q_act:       query records from rsfp4_nvfp4_quantize_act_with_residue over
+ *                q viewed as [B * H_q, D] rows (with_residue = compensated);
+ *   compensated: 0 = scores from the base only (plain NVFP4 query);
+ *   block_table: [B, max_pages] int32 page indices (device); seq_lens: [B]
+ *                int32 (device), each <= max_seq_len <= 32 * max_pages (tokens
+ *                beyond max_seq_len are not read);
+ *   sm_scale:    usually 1 / sqrt(D);
+ *   splits:      KV splits (<= 0: the preset rule); with more than one, the
+ *                workspace ws (device, >= rsfp4_resattn_workspace_bytes) holds
+ *                the partial outputs and a second kernel combines them;
+ *   out:         [B, H_q, D], fp32 or (out_bf16) bf16, fully overwritten
+ *                (a sequence of length 0 gives zeros).
+ * Page indices outside the cache read as zeros. */
+rsfp4_status rsfp4_resattn_decode(const void* q_act, size_t q_act_bytes, int compensated, const void* cache,
+                                  size_t cache_bytes, const int32_t* block_table, int64_t max_pages,
+                                  const int32_t* seq_lens, int64_t max_seq_len, int64_t B, int64_t H_q,
+                                  int64_t H_kv, int64_t D, float k_scale, float v_scale, float sm_scale,
+                                  int splits, void* out, int out_bf16, void* ws, size_t ws_bytes,
+                                  void* stream);
+
 /* ------------------------------------------------------- test / debug ----
  * Rewrite a packed blob in canonical row-major form: codes[N, K/2] (low nibble
  * = even K index), scales[N, K/blk], and (NVFP4) the tensor scale to *s_g

@@ -1,0 +1,212 @@
+"""GPU parity of compensated decode attention (ResAttn; ResServe Section 4.3
+Eq. 3 and Section 5.2) over the paged NVFP4 KV cache: the cache writer must
+match the oracle's NVFP4 rows bit for bit; the attention output must satisfy
+|o_gpu - o_oracle| <= 2^-10 * (sum_t p_t |v_t| / sum_t p_t) + 1e-6 * max|v|
+elementwise -- the f16 rounding of the probabilities (relative 2^-11, on the
+numerator only) bounds the first term; scores are exact products summed in
+fp32."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from block_scaled_fp4_act_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: the gpu tests need an MI355X")
+    import block_scaled_fp4_act_amd as rs
+    rs.lib()
+    oracle.build()
+
+
+def _rs():
+    import block_scaled_fp4_act_amd as rs
+    return rs
+
+
+def _t(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _rand(shape, seed, scale=1.0):
+    return (np.random.Generator(np.random.PCG64(seed)).standard_normal(shape, dtype=np.float32) * np.float32(scale))
+
+
+class Problem:
+    """B sequences of given lengths in a shuffled paged cache."""
+
+    def __init__(self, lens, H_q, H_kv, D, seed, k_scale=1.0, v_scale=1.0, spare_pages=3, bf16=True):
+        import torch
+        rs = _rs()
+        self.lens, self.H_q, self.H_kv, self.D = list(lens), H_q, H_kv, D
+        self.B = len(lens)
+        self.k_scale, self.v_scale = k_scale, v_scale
+        npg = [(L + 31) // 32 for L in lens]
+        self.max_pages = max(max(npg), 1)
+        total = sum(npg) + spare_pages
+        perm = np.random.default_rng(seed).permutation(total)
+        self.table = np.zeros((self.B, self.max_pages), np.int32)
+        slots, ks, vs = [], [], []
+        pos = 0
+        for b, L in enumerate(lens):
+            pages = perm[pos:pos + npg[b]]
+            pos += npg[b]
+            self.table[b, :npg[b]] = pages
+            t = np.arange(L)
+            slots.append(pages[t // 32] * 32 + t % 32)
+        self.k = [_rand((L, H_kv, D), seed * 10 + b + 1) for b, L in enumerate(lens)]
+        self.v = [_rand((L, H_kv, D), seed * 10 + b + 101) for b, L in enumerate(lens)]
+        if bf16:
+            self.k = [inputs.round_to_bf16(x) for x in self.k]
+            self.v = [inputs.round_to_bf16(x) for x in self.v]
+        self.cache = torch.full((total * rs.kv_page_bytes(H_kv, D),), 0x5A, dtype=torch.uint8, device="cuda")
+        kk = np.concatenate(self.k) if sum(lens) else np.zeros((0, H_kv, D), np.float32)
+        vv = np.concatenate(self.v) if sum(lens) else np.zeros((0, H_kv, D), np.float32)
+        sl = np.concatenate(slots).astype(np.int32)
+        if len(sl):
+            dt = torch.bfloat16 if bf16 else torch.float32
+            rs.kv_cache_write(_t(kk).to(dt), _t(vv).to(dt), _t(sl), self.cache, k_scale, v_scale)
+        self.slots = sl
+        q = _rand((self.B * H_q, D), seed + 7)
+        q[:, ::29] *= 20.0                       # outlier channels, then bf16 (what the kernel receives)
+        self.q = inputs.round_to_bf16(q)
+
+    def run(self, comp=True, splits=0, out_bf16=False):
+        import torch
+        rs = _rs()
+        qa = rs.quantize_act_with_residue(_t(self.q).to(torch.bfloat16), 0, comp)
+        out = rs.resattn_decode(qa, self.cache, _t(self.table), _t(np.array(self.lens, np.int32)),
+                                max(max(self.lens), 1), self.B, self.H_q, self.H_kv, self.D, compensated=comp,
+                                k_scale=self.k_scale, v_scale=self.v_scale, splits=splits, out_bf16=out_bf16)
+        torch.cuda.synchronize()
+        return out
+
+    def reference(self, comp=True):
+        q = oracle.quantize_act(self.q, 0, with_residue=comp)
+        n = self.B * self.H_q
+        ref = np.zeros((self.B, self.H_q, self.D))
+        mag = np.zeros_like(ref)
+        vmax = np.zeros((self.B,))
+        sm = 1.0 / math.sqrt(self.D)
+        for b, L in enumerate(self.lens):
+            if L == 0:
+                continue
+            kd = oracle.kv_quantize(self.k[b], self.k_scale)["deq"]
+            vd = oracle.kv_quantize(self.v[b], self.v_scale)["deq"]
+            rows = slice(b * self.H_q, (b + 1) * self.H_q)
+            qb = q["deq"][rows]
+            qr = q["deq"][n + b * self.H_q: n + (b + 1) * self.H_q] if comp else None
+            ref[b] = oracle.attention_decode(qb, qr, kd, vd, sm)
+            mag[b] = oracle.attention_decode(qb, qr, kd, np.abs(vd), sm)
+            vmax[b] = np.abs(vd).max()
+        return ref, mag, vmax
+
+
+def _check(out, ref, mag, vmax):
+    o = out.float().cpu().numpy().astype(np.float64)
+    bound = 2.0 ** -10 * mag + 1e-6 * vmax[:, None, None]
+    err = np.abs(o - ref)
+    bad = err > bound
+    assert not bad.any(), (f"{int(bad.sum())} of {bad.size} outside; worst ratio "
+                           f"{float((err / np.maximum(bound, 1e-30)).max()):.3e}")
+
+
+def test_kv_cache_write_bitexact():
+    import torch
+    rs = _rs()
+    P = Problem([70, 33], 8, 2, 128, seed=3, k_scale=1.0, v_scale=0.5)
+    pb = rs.kv_page_bytes(2, 128)
+    cache = P.cache.cpu().numpy().reshape(-1, pb)
+    D = 128
+    for b in range(P.B):
+        qk = oracle.kv_quantize(P.k[b], 1.0)
+        qv = oracle.kv_quantize(P.v[b], 0.5)
+        for t in range(P.lens[b]):
+            page, row = divmod(int(P.table[b, t // 32]) * 32 + t % 32, 32)
+            for h in range(2):
+                base = h * 36 * D
+                kc = cache[page, base + row * 64: base + row * 64 + 64]
+                ksc = cache[page, base + 16 * D + row * 8: base + 16 * D + row * 8 + 8]
+                vc = cache[page, base + 18 * D + row * 64: base + 18 * D + row * 64 + 64]
+                vsc = cache[page, base + 34 * D + row * 8: base + 34 * D + row * 8 + 8]
+                assert np.array_equal(kc, qk["codes"][t, h]) and np.array_equal(ksc, qk["scales"][t, h])
+                assert np.array_equal(vc, qv["codes"][t, h]) and np.array_equal(vsc, qv["scales"][t, h])
+
+
+CASES = [  # (lens, H_q, H_kv, D)
+    ([1, 37, 300], 16, 2, 128),      # GQA 8, one token, a partial page, several pages
+    ([64, 5, 129], 8, 2, 128),       # GQA 4
+    ([45, 200], 12, 2, 256),         # GQA 6, D = 256
+    ([1000], 8, 1, 128),
+]
+
+
+@pytest.mark.parametrize("comp", [True, False])
+@pytest.mark.parametrize("splits", [1, 3, 0])
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "L%s_Hq%d_Hkv%d_D%d" % ("-".join(map(str, c[0])), c[1], c[2], c[3]))
+def test_resattn_parity(case, splits, comp):
+    lens, H_q, H_kv, D = case
+    P = Problem(lens, H_q, H_kv, D, seed=sum(lens) + H_q)
+    out = P.run(comp=comp, splits=splits)
+    _check(out, *P.reference(comp=comp))
+
+
+def test_resattn_global_scales_and_bf16_output():
+    import torch
+    P = Problem([77, 150], 16, 2, 128, seed=5, k_scale=0.75, v_scale=2.0)
+    o32 = P.run(splits=1)
+    o16 = P.run(splits=1, out_bf16=True)
+    assert o16.dtype == torch.bfloat16 and torch.equal(o16, o32.to(torch.bfloat16))
+    _check(o32, *P.reference())
+
+
+def test_resattn_zero_length_and_empty_splits():
+    """A sequence of length 0 gives zeros; splits beyond a short sequence are
+    empty and weigh nothing."""
+    P = Problem([0, 40, 2], 8, 1, 128, seed=9)
+    out = P.run(splits=5)
+    assert (out[0] == 0).all()
+    ref, mag, vmax = P.reference()
+    _check(out[1:], ref[1:], mag[1:], vmax[1:])
+
+
+def test_resattn_compensation_reduces_error():
+    """Against attention with the unquantized query over the same cache, the
+    compensated scores beat the plain ones (the page's Fig. 10d comparison)."""
+    P = Problem([512, 512], 16, 2, 128, seed=11)
+    ref_exact = np.zeros((2, 16, 128))
+    sm = 1 / math.sqrt(128)
+    for b in range(2):
+        kd = oracle.kv_quantize(P.k[b], 1.0)["deq"]
+        vd = oracle.kv_quantize(P.v[b], 1.0)["deq"]
+        ref_exact[b] = oracle.attention_decode(P.q[b * 16:(b + 1) * 16], None, kd, vd, sm)
+    e = lambda o: float(np.sum((o.float().cpu().numpy() - ref_exact) ** 2))
+    assert e(P.run(comp=True)) < 0.6 * e(P.run(comp=False))
+
+
+@pytest.mark.parametrize("cfg", [(8, 64, 8, 128, 8192), (2, 24, 4, 256, 4096)],
+                         ids=["D128_GQA8_B8_L8192", "D256_GQA6_B2_L4096"])
+def test_resattn_workload_sampled(cfg):
+    """Decode shapes of the page's Figure 10 at moderate length, with the
+    preset split rule; heads of the first and last sequences checked."""
+    B, H_q, H_kv, D, L = cfg
+    P = Problem([L] * B, H_q, H_kv, D, seed=L + B)
+    out = P.run()
+    keep = [0, B - 1]
+    sub = Problem.__new__(Problem)
+    sub.__dict__.update(P.__dict__)
+    sub.lens = [P.lens[b] for b in keep]
+    sub.k = [P.k[b] for b in keep]
+    sub.v = [P.v[b] for b in keep]
+    sub.q = np.concatenate([P.q[b * H_q:(b + 1) * H_q] for b in keep])
+    sub.B = len(keep)
+    ref, mag, vmax = sub.reference()
+    _check(out[keep], ref, mag, vmax)
