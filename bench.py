@@ -11,9 +11,10 @@ graph so host launch cost does not enter the timing.
 Prints ONE JSON line.  Extra keys: the uncompensated (plain W4A4) pair and the
 compensation overhead, per-kernel averages, NMSE against the fp32 product, the
 roofline of the dominant kernel, the oracle timed on the host cores, a sweep
-over the other decode workloads, and selective compensation (K-Ext) at
+over the other decode workloads, selective compensation (K-Ext) at
 rho = 0.125 / 0.25 / 0.5 on the prefill-sized operands beside their plain and
-full-residue steps.
+full-residue steps, and compensated decode attention (ResAttn) over the paged
+NVFP4 KV cache at decode shapes of the page's Figure 10.
 """
 import argparse
 import hashlib
@@ -197,6 +198,59 @@ def paper_numerics_step(rs, torch, S, ref, steps, warmup):
     return {"us_per_call": round(t * 1e3, 3), "quant_us": round(tq * 1e3, 3),
             "nmse_comp_bf16": round(nmse(y, ref), 6), "alpha": float(alpha.item()),
             "what": "shared tensor scale alpha, multiplier-scale quantizer, bf16 output"}
+
+
+ATTN_CASES = [  # (name, H_q, H_kv, D, B, L): decode shapes of the page's Figure 10
+    ("D128_GQA8", 64, 8, 128, 1, 8192), ("D128_GQA8", 64, 8, 128, 1, 32768), ("D128_GQA8", 64, 8, 128, 1, 131072),
+    ("D128_GQA8", 64, 8, 128, 8, 8192), ("D128_GQA8", 64, 8, 128, 8, 32768), ("D128_GQA8", 64, 8, 128, 32, 8192),
+    ("D128_GQA4", 32, 8, 128, 8, 32768), ("D256_GQA6", 24, 4, 256, 8, 32768),
+]
+
+
+def attn_kv_bytes(B, L, H_kv, D):
+    """K and V codes plus their block scales of every cached token read once."""
+    return 2 * B * L * H_kv * (D // 2 + D // 16)
+
+
+def run_attn(rs, torch, case, steps, warmup):
+    """Decode attention step (query quantize + compensated attention over the
+    paged NVFP4 cache), beside the plain-query step.  The cache is filled with
+    random bytes (every byte decodes to a finite value); R disjoint copies of
+    the sequences' pages rotate so each step reads its KV from HBM."""
+    import math
+    name, H_q, H_kv, D, B, L = case
+    pb = rs.kv_page_bytes(H_kv, D)
+    pages_per_seq = (L + 31) // 32
+    step_bytes = B * pages_per_seq * pb
+    R = max(2, int(math.ceil(ROTATE_BYTES / step_bytes)))
+    total_pages = R * B * pages_per_seq
+    g = torch.Generator(device="cuda").manual_seed(7)
+    cache = torch.randint(0, 256, (total_pages * pb,), dtype=torch.uint8, device="cuda", generator=g)
+    perm = torch.randperm(total_pages, device="cuda", generator=g).to(torch.int32)
+    tables = [perm[r * B * pages_per_seq:(r + 1) * B * pages_per_seq].view(B, pages_per_seq).contiguous()
+              for r in range(R)]
+    seq = torch.full((B,), L, dtype=torch.int32, device="cuda")
+    q = (torch.randn((B * H_q, D), device="cuda", generator=g)).to(torch.bfloat16)
+    splits = rs.resattn_splits(B, H_kv, L)
+    ws = torch.empty(max(1, int(rs.lib().rsfp4_resattn_workspace_bytes(B, H_q, D, splits))), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty((B, H_q, D), dtype=torch.bfloat16, device="cuda")
+    acts = {c: rs.quantize_act_with_residue(q, 0, c) for c in (True, False)}
+
+    def step(i, comp):
+        rs.quantize_act_with_residue(q, 0, comp, out=acts[comp])
+        rs.resattn_decode(acts[comp], cache, tables[i % R], seq, L, B, H_q, H_kv, D, compensated=comp,
+                          splits=splits, out=out, out_bf16=True, ws=ws)
+
+    t_c = time_graph(torch, lambda i: step(i, True), steps, warmup)
+    t_p = time_graph(torch, lambda i: step(i, False), steps, warmup)
+    kvb = attn_kv_bytes(B, L, H_kv, D)
+    del cache
+    torch.cuda.empty_cache()
+    return {"config": name, "B": B, "L": L, "H_q": H_q, "H_kv": H_kv, "D": D, "splits": splits,
+            "us_per_call": round(t_c * 1e3, 3), "plain_us_per_call": round(t_p * 1e3, 3),
+            "comp_overhead": round(t_c / t_p - 1.0, 4), "kv_GBps": round(kvb / (t_c * 1e-3) / 1e9, 1),
+            "kv_hbm_frac": round(kvb / (t_c * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def time_graph(torch, fn, steps, warmup):
@@ -386,6 +440,12 @@ def main():
                  "large_mlp": inputs.LARGE_MLP, "mx": inputs.MX, "small": inputs.SMALL}
         for item in args.cases.split(","):
             parts = item.split(":")
+            if parts[0] == "resattn":   # resattn:<index into ATTN_CASES> or resattn:all
+                idx = range(len(ATTN_CASES)) if parts[1] == "all" else [int(parts[1])]
+                for ci in idx:
+                    print(json.dumps(run_attn(rs, torch, ATTN_CASES[ci], min(args.steps, 50), min(args.warmup, 5))),
+                          flush=True)
+                continue
             name, m = parts[0], int(parts[1])
             if len(parts) > 2:      # name:M:k1/k2/..  -> selective compensation at those k
                 ks = [int(v) for v in parts[2].split("/")]
@@ -440,6 +500,7 @@ def main():
             del S2
             torch.cuda.empty_cache()
             sweep.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()})
+        attn = [run_attn(rs, torch, c, min(args.steps, 50), min(args.warmup, 5)) for c in ATTN_CASES]
         # selective compensation (prefill-sized operands): rho = 0.125, 0.25, 0.5
         kext = []
         for w, m in ((inputs.LARGE_MLP, 128), (inputs.MX, 256)):
@@ -484,6 +545,7 @@ def main():
     if sweep:
         line["sweep"] = sweep
         line["kext"] = kext
+        line["attention"] = attn
     print(json.dumps(line), flush=True)
 
 
