@@ -195,20 +195,17 @@ __global__ __launch_bounds__(64) void resattn_kernel(AttnArgs p) {
         }
     };
 
-    Raw cur, nxt;
-    if (pg0 < pg1) load_page(pg0, cur);
-    for (int pg = pg0; pg < pg1; ++pg) {
-        load_page(pg + 1, nxt);                 // past pg1: a zero-sized resource (no traffic)
-
-        // ---- scores of the page's 32 tokens: two 16-token tiles ----
+    // ---- one page: scores, online softmax, P V ----
+    auto process = [&](const Raw& cur, int pg) {
+        // scores of the page's 32 tokens: two 16-token tiles
         floatx4 acc[2];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
             acc[tt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
-                const uint32_t sc = cur.ks[tt][s >> 2];
-                const half8 a = dequant8(word(cur.kc[tt][s >> 2], s & 3), scale_h((s & 3) < 2 ? (sc & 0xFFu) : (sc >> 8)));
+                const uint32_t kb = cur.ks[tt][s >> 2];
+                const half8 a = dequant8(word(cur.kc[tt][s >> 2], s & 3), scale_h((s & 3) < 2 ? (kb & 0xFFu) : (kb >> 8)));
                 acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qf[s], acc[tt], 0, 0, 0);
             }
         }
@@ -236,28 +233,30 @@ __global__ __launch_bounds__(64) void resattn_kernel(AttnArgs p) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const float pv = live ? __builtin_amdgcn_exp2f(sc[tt][r] - m_new) : 0.0f;
-                const _Float16 ph = (_Float16)pv;
-                pa[4 * tt + r] = ph;
+                pa[4 * tt + r] = (_Float16)pv;
                 ps += pv;
             }
         l = l * corr + rowgroup_sum(ps);
         m = m_new;
 
-        // rescale the accumulators: lane holds query rows 4j + r
-        float cr[4];
+        // rescale the accumulators (rows 4j + r) -- skipped when no row's
+        // maximum moved, the common case once the first pages have been seen
+        if (__builtin_amdgcn_ballot_w64(corr != 1.0f) != 0) {
+            float cr[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) cr[r] = __shfl(corr, 4 * j + r, 64);
+            for (int r = 0; r < 4; ++r) cr[r] = __shfl(corr, 4 * j + r, 64);
 #pragma unroll
-        for (int c = 0; c < NC; ++c)
+            for (int c = 0; c < NC; ++c)
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
+                for (int e = 0; e < 8; ++e)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) o[c][e][r] *= cr[r];
+                    for (int r = 0; r < 4; ++r) o[c][e][r] *= cr[r];
+        }
 
-        // ---- P V: 8 tokens x 8 d-elements per lane, transposed in registers.
+        // P V: 8 tokens x 8 d-elements per lane, transposed in registers.
         // Tokens past L have p = 0; their cache bytes (whatever they hold)
         // decode to finite f16 (FP4 codes are finite, and the scale conversion
-        // maps every byte to a finite value), so they add exact zeros. ----
+        // maps every byte to a finite value), so they add exact zeros.
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             half8 vv[8];
@@ -271,7 +270,28 @@ __global__ __launch_bounds__(64) void resattn_kernel(AttnArgs p) {
                 o[c][e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, bv, o[c][e], 0, 0, 0);
             }
         }
-        cur = nxt;
+    };
+
+    // Pages in flight: the loads of pages pg+1 and pg+2 are out while page pg
+    // is computed (three register sets in fixed roles, loop unrolled by three;
+    // a load past the split's last page uses a zero-sized resource).
+    Raw r0, r1, r2;
+    if (pg0 < pg1) {
+        load_page(pg0, r0);
+        load_page(pg0 + 1, r1);
+    }
+    for (int pg = pg0; pg < pg1; pg += 3) {
+        load_page(pg + 2, r2);
+        __builtin_amdgcn_sched_barrier(0);
+        process(r0, pg);
+        if (pg + 1 >= pg1) break;
+        load_page(pg + 3, r0);
+        __builtin_amdgcn_sched_barrier(0);
+        process(r1, pg + 1);
+        if (pg + 2 >= pg1) break;
+        load_page(pg + 4, r1);
+        __builtin_amdgcn_sched_barrier(0);
+        process(r2, pg + 2);
     }
 
     // ---- outputs: rows 4j + r of column d = 128c + 8i + e (even rows = heads) ----
@@ -310,22 +330,56 @@ __global__ __launch_bounds__(64) void resattn_kernel(AttnArgs p) {
 }
 
 // Combine the splits of one head: weights 2^(m_s - M) over the splits' row
-// maxima (base 2); empty splits (m = -inf) weigh 0.
+// maxima (base 2); empty splits (m = -inf) weigh 0.  The splits' (m, l) pairs
+// go to LDS once (coalesced), the weights are formed there, and each thread
+// then sums its output element over the splits with eight loads in flight.
+constexpr int kMaxSplits = 4096;
+
 template <int D>
 __global__ __launch_bounds__(D) void resattn_reduce_kernel(AttnArgs p) {
+    __shared__ float wsh[kMaxSplits];
+    __shared__ float red[D / 64];
     const int64_t head = blockIdx.x;
     const int d = threadIdx.x;
-    const float* ml = p.ws_ml + head * p.splits * 2;
-    float M = -__builtin_inff();
-    for (int s = 0; s < p.splits; ++s) M = fmaxf(M, ml[2 * s]);
-    float num = 0.0f, den = 0.0f;
-    if (M > -__builtin_inff()) {
-        for (int s = 0; s < p.splits; ++s) {
-            const float w = __builtin_amdgcn_exp2f(ml[2 * s] - M);
-            num += w * p.ws_o[(head * p.splits + s) * D + d];
-            den += w * ml[2 * s + 1];
-        }
+    const int S = p.splits;
+    const float* ml = p.ws_ml + head * S * 2;
+    // row maximum over the splits
+    float mloc = -__builtin_inff();
+    for (int s = d; s < S; s += D) {
+        const float ms = ml[2 * s];
+        wsh[s] = ms;
+        mloc = fmaxf(mloc, ms);
     }
+    for (int off = 32; off > 0; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off, 64));
+    if ((d & 63) == 0) red[d >> 6] = mloc;
+    __syncthreads();
+    float M = red[0];
+    for (int w = 1; w < D / 64; ++w) M = fmaxf(M, red[w]);
+    __syncthreads();
+    // weights and the weighted sum of the splits' row sums
+    const bool live = M > -__builtin_inff();
+    float dl = 0.0f;
+    for (int s = d; s < S; s += D) {
+        const float w = live ? __builtin_amdgcn_exp2f(wsh[s] - M) : 0.0f;
+        wsh[s] = w;
+        dl += w * ml[2 * s + 1];
+    }
+    for (int off = 32; off > 0; off >>= 1) dl += __shfl_xor(dl, off, 64);
+    if ((d & 63) == 0) red[d >> 6] = dl;
+    __syncthreads();
+    float den = 0.0f;
+    for (int w = 0; w < D / 64; ++w) den += red[w];
+    const float* src = p.ws_o + head * S * D + d;
+    float num = 0.0f;
+    int s = 0;
+    for (; s + 8 <= S; s += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = src[(int64_t)(s + u) * D];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) num += wsh[s + u] * v[u];
+    }
+    for (; s < S; ++s) num += wsh[s] * src[(int64_t)s * D];
     store_y(p.out, head * D + d, den > 0.0f ? num / den : 0.0f, p.out_bf16);
 }
 
