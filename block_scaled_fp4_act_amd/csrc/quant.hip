@@ -102,20 +102,52 @@ __device__ __forceinline__ float block_scale(float bm, float s_g, uint32_t& sbyt
 }
 
 // Element codes with the hardware conversion (codec.h): MXFP4 converts v with
-// the block's power-of-two scale directly; NVFP4 first forms the IEEE quotient
-// v / s~ and converts it with scale 1.  A zero s~ (zero block, or a block scale
-// that rounds to 0) divides by infinity instead, so the code is a zero of v's
-// sign.  Dequantized values come back through the decoder: fl(s~ * e) for
+// the block's power-of-two scale directly; NVFP4 first forms the quotient
+// v / s~ rounded to nearest and converts it with scale 1.  A zero s~ (zero
+// block, or a block scale that rounds to 0) gives a zero of v's sign.  Dequantized values come back through the decoder: fl(s~ * e) for
 // NVFP4 (the decoder's e is exact), X * e exactly for MXFP4.
-template <int FMT>
-__device__ __forceinline__ float quot_div(float st) {
-    return FMT == kNV ? (st != 0.0f ? st : __builtin_inff()) : st;
+// The NVFP4 element quotient v / s~, rounded to nearest.  A chunk's elements
+// share s~, so the common case divides once per chunk: y = RN(1/s~) (an IEEE
+// division), then per element q = RN(v y), the remainder r = v - s~ q (exact,
+// one fma) and RN(q + r y) (one fma) -- Markstein's correction, which returns
+// RN(v / s~) when y is the correctly rounded reciprocal and q a faithful
+// quotient, with no under- or overflow on the way; the sign of zero is copied
+// from v.  FAST is taken for rows whose tensor scale lies in [2^-80, 2^80]:
+// then s~ and y are normal, |v / s~| stays below 7, and the remainders of
+// quotients near the E2M1 rounding thresholds are normal.  Other rows divide.
+// s~ = 0 (zero block) uses y = 0 with a unit divisor: every quotient is a
+// zero of v's sign, as v / inf is.
+struct Quot {
+    float b, y, sd;
+};
+
+template <int FMT, bool FAST>
+__device__ __forceinline__ Quot make_quot(float st) {
+    Quot q;
+    const bool z = st == 0.0f;
+    q.b = z ? 1.0f : st;
+    q.y = FAST ? (z ? 0.0f : 1.0f / st) : 0.0f;
+    q.sd = z ? __builtin_inff() : st;
+    return q;
 }
 
-template <int FMT, int SEL>
-__device__ __forceinline__ uint32_t enc2(uint32_t packed, float a, float b, float st, float sd) {
-    if (FMT == kNV) return e2m1_pack2<SEL>(packed, a / sd, b / sd, 1.0f);
+template <bool FAST>
+__device__ __forceinline__ float quot(float a, const Quot& d) {
+    if (!FAST) return a / d.sd;
+    const float q0 = a * d.y;
+    const float r = __builtin_fmaf(-d.b, q0, a);
+    return __builtin_copysignf(__builtin_fmaf(r, d.y, q0), a);
+}
+
+template <int FMT, int SEL, bool FAST>
+__device__ __forceinline__ uint32_t enc2(uint32_t packed, float a, float b, float st, const Quot& d) {
+    if (FMT == kNV) return e2m1_pack2<SEL>(packed, quot<FAST>(a, d), quot<FAST>(b, d), 1.0f);
     return e2m1_pack2<SEL>(packed, a, b, st);
+}
+
+// Rows whose NVFP4 tensor scale allows the one-division quotient.
+__device__ __forceinline__ bool fast_quot_row(float s_g) {
+    return s_g >= 8.271806125530277e-25f && s_g <= 1.2089258196146292e24f;   // 2^-80, 2^80
 }
 
 template <int FMT, int SEL>
@@ -129,15 +161,15 @@ __device__ __forceinline__ rsfp4_float2v dec2(uint32_t packed, float st) {
 
 // Encode EPT (4 or 8) values into packed nibbles (element e at bits 4e..4e+3)
 // and replace them by their residues v - deq.
-template <int FMT, int EPT>
+template <int FMT, int EPT, bool FAST>
 __device__ __forceinline__ uint32_t encode_residue(float (&v)[EPT], float st) {
-    const float sd = quot_div<FMT>(st);
+    const Quot dq = make_quot<FMT, FAST>(st);
     uint32_t packed = 0u;
-    packed = enc2<FMT, 0>(packed, v[0], v[1], st, sd);
-    packed = enc2<FMT, 1>(packed, v[2], v[3], st, sd);
+    packed = enc2<FMT, 0, FAST>(packed, v[0], v[1], st, dq);
+    packed = enc2<FMT, 1, FAST>(packed, v[2], v[3], st, dq);
     if (EPT == 8) {
-        packed = enc2<FMT, 2>(packed, v[4], v[5], st, sd);
-        packed = enc2<FMT, 3>(packed, v[6], v[7], st, sd);
+        packed = enc2<FMT, 2, FAST>(packed, v[4], v[5], st, dq);
+        packed = enc2<FMT, 3, FAST>(packed, v[6], v[7], st, dq);
     }
     rsfp4_float2v d;
     d = dec2<FMT, 0>(packed, st); v[0] -= d[0]; v[1] -= d[1];
@@ -158,9 +190,9 @@ __device__ __forceinline__ void store_head(uint8_t* rec, float s_g) {
 // residue): chunk j's codes go to codes[j * EPT / 2 ..], its block scale byte
 // to scales[j / lanes-per-block].  s_g is the row's tensor scale (NVFP4);
 // nchunks = K / EPT.
-template <int FMT, int NC, int EPT>
-__device__ __forceinline__ void quantize_chunks(float (&v)[NC][EPT], int nchunks, float s_g,
-                                                uint8_t* codes, uint8_t* scales) {
+template <int FMT, int NC, int EPT, bool FAST>
+__device__ __forceinline__ void quantize_chunks_q(float (&v)[NC][EPT], int nchunks, float s_g,
+                                                  uint8_t* codes, uint8_t* scales) {
     constexpr int LPB = (FMT == kNV ? 16 : 32) / EPT;   // lanes sharing one block
     const int tid = threadIdx.x;
 #pragma unroll
@@ -176,7 +208,7 @@ __device__ __forceinline__ void quantize_chunks(float (&v)[NC][EPT], int nchunks
         uint32_t sbyte;
         const float st = block_scale<FMT>(bm, s_g, sbyte);   // effective element scale
         // codes, and v becomes the residue x - fl(s~ e) (exact: Sterbenz)
-        const uint32_t packed = encode_residue<FMT, EPT>(v[c], st);
+        const uint32_t packed = encode_residue<FMT, EPT, FAST>(v[c], st);
         if (j < nchunks) {
             if (EPT == 8)
                 *reinterpret_cast<uint32_t*>(codes + 4 * (int64_t)j) = packed;
@@ -185,6 +217,17 @@ __device__ __forceinline__ void quantize_chunks(float (&v)[NC][EPT], int nchunks
             if ((j & (LPB - 1)) == 0) scales[j / LPB] = (uint8_t)sbyte;
         }
     }
+}
+
+// The row's quotient path is chosen once per row (the tensor scale is the same
+// in every thread of the workgroup, so the branch does not diverge).
+template <int FMT, int NC, int EPT>
+__device__ __forceinline__ void quantize_chunks(float (&v)[NC][EPT], int nchunks, float s_g,
+                                                uint8_t* codes, uint8_t* scales) {
+    if (FMT == kNV && !fast_quot_row(s_g))
+        quantize_chunks_q<FMT, NC, EPT, false>(v, nchunks, s_g, codes, scales);
+    else
+        quantize_chunks_q<FMT, NC, EPT, true>(v, nchunks, s_g, codes, scales);
 }
 
 template <int FMT, int NC, int EPT, typename TIn>
@@ -351,16 +394,16 @@ __global__ __launch_bounds__(kQMaxThreads) void quant_kext_kernel(const TIn* __r
         bm = run_max<LPE>(bm);
         uint32_t sbyte;
         const float st = block_scale<FMT>(bm, s_g, sbyte);
-        const float sd = quot_div<FMT>(st);
+        const Quot dq = make_quot<FMT, false>(st);       // the extension divides
         uint32_t packed = 0u;
         if (KS == 1) {
-            packed = enc2<FMT, 0>(0u, rs[0], 0.0f, st, sd) & 15u;
+            packed = enc2<FMT, 0, false>(0u, rs[0], 0.0f, st, dq) & 15u;
         } else {
-            packed = enc2<FMT, 0>(packed, rs[0], rs[KS > 1 ? 1 : 0], st, sd);
-            if (KS >= 4) packed = enc2<FMT, 1>(packed, rs[KS >= 4 ? 2 : 0], rs[KS >= 4 ? 3 : 0], st, sd);
+            packed = enc2<FMT, 0, false>(packed, rs[0], rs[KS > 1 ? 1 : 0], st, dq);
+            if (KS >= 4) packed = enc2<FMT, 1, false>(packed, rs[KS >= 4 ? 2 : 0], rs[KS >= 4 ? 3 : 0], st, dq);
             if (KS == 8) {
-                packed = enc2<FMT, 2>(packed, rs[KS == 8 ? 4 : 0], rs[KS == 8 ? 5 : 0], st, sd);
-                packed = enc2<FMT, 3>(packed, rs[KS == 8 ? 6 : 0], rs[KS == 8 ? 7 : 0], st, sd);
+                packed = enc2<FMT, 2, false>(packed, rs[KS == 8 ? 4 : 0], rs[KS == 8 ? 5 : 0], st, dq);
+                packed = enc2<FMT, 3, false>(packed, rs[KS == 8 ? 6 : 0], rs[KS == 8 ? 7 : 0], st, dq);
             }
         }
         uint32_t pair = 0u;

@@ -85,6 +85,40 @@ def test_quantize_adversarial_bitexact(fmt, K):
     assert_quant_equal(x, fmt, True, True)
 
 
+def _near_tie_rows(K, n_rows, seed):
+    """Rows whose element quotients v / s~ sit on and within three ulps of
+    every E2M1 rounding tie, with s~ = S_b s_g not a power of two: the cases
+    where the one-division quotient must reproduce the IEEE division exactly."""
+    rng = np.random.default_rng(seed)
+    ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], np.float32)
+    rows = []
+    for _ in range(n_rows):
+        amax = np.float32(rng.uniform(50.0, 900.0))
+        s_g = np.float32(oracle.nvfp4_global_scale(float(amax)))
+        row = np.zeros(K, np.float32)
+        for b in range(K // 16):
+            bm = np.float32(amax if b == 0 else amax * rng.uniform(0.05, 1.0))
+            sb = oracle.e4m3_value(oracle.e4m3_encode(float(np.float32(bm / np.float32(np.float32(6.0) * s_g)))))
+            st = np.float32(np.float32(sb) * s_g)
+            blk = np.empty(16, np.float32)
+            blk[0] = bm
+            for j in range(1, 16):
+                x = np.float32(np.float32(rng.choice(ties)) * st)
+                for _ in range(int(rng.integers(-3, 4))):
+                    x = np.nextafter(x, np.float32(np.inf))
+                x = min(x, bm)
+                blk[j] = x if rng.random() < 0.5 else -x
+            row[16 * b:16 * b + 16] = blk
+        rows.append(row)
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("K", [256, 4096])
+def test_quantize_quotient_near_ties(K):
+    x = _near_tie_rows(K, 8, K + 3)
+    assert_quant_equal(x, 0, False, True)
+
+
 @pytest.mark.parametrize("fmt", [0, 1])
 def test_quantize_exact_residue_identity(fmt):
     """The buffer's base and residue rows dequantize to d and d_r with
