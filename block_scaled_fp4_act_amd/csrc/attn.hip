@@ -33,48 +33,13 @@
 #include <stdint.h>
 
 #include "codec.h"
+#include "fp4_frag.h"
 #include "kernels.h"
 #include "layout.h"
 
 namespace rsfp4 {
 
 namespace {
-
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef _Float16 half2v __attribute__((ext_vector_type(2)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kRsrcWord3 = 0x00020000;     // raw buffer, 32-bit dwords, range checked
-
-// E4M3 byte -> S_b * 2^-8 as f16 (the exponent and mantissa fields line up).
-__device__ __forceinline__ _Float16 scale_h(uint32_t byte) {
-    return __builtin_bit_cast(_Float16, (unsigned short)((byte & 0x7Fu) << 7));
-}
-
-// 8 E2M1 codes (low nibble first) -> 8 exact f16 values e * S_b: the FP4
-// conversion supplies the factor 2^8, a packed f16 multiply S_b * 2^-8.
-__device__ __forceinline__ half8 dequant8(uint32_t w, _Float16 s) {
-    half2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 0);
-    half2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 1);
-    half2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 2);
-    half2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 3);
-    const half2v s2 = {s, s};
-    p0 *= s2; p1 *= s2; p2 *= s2; p3 *= s2;
-    half8 r;
-    r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
-    r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
-    return r;
-}
-
-__device__ __forceinline__ uint32_t word(const uint4& v, int u) {
-    return u == 0 ? v.x : (u == 1 ? v.y : (u == 2 ? v.z : v.w));
-}
-
-__device__ __forceinline__ uint4 ld128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-    return make_uint4(v[0], v[1], v[2], v[3]);
-}
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {

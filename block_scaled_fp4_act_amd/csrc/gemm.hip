@@ -44,6 +44,7 @@
 #include <cstdlib>
 
 #include "codec.h"
+#include "fp4_frag.h"
 #include "kernels.h"
 #include "layout.h"
 
@@ -51,54 +52,9 @@ namespace rsfp4 {
 
 namespace {
 
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef _Float16 half2v __attribute__((ext_vector_type(2)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-typedef int intx8 __attribute__((ext_vector_type(8)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-
 constexpr int kMaxWaves = 16;
 constexpr int kRedBytesMax = 128 * 1024;   // LDS for partial sums per workgroup
 constexpr int kLdsPerCu = 160 * 1024;      // gfx950
-constexpr int kRsrcWord3 = 0x00020000;     // raw buffer, 32-bit dwords, range checked
-
-// NVFP4 block-scale byte -> f16 holding S_b * 2^-8.  E4M3 (bias 7) and f16
-// (bias 15) line up field by field: the E4M3 exponent and mantissa bits moved to
-// f16's exponent and top mantissa bits give the same value times 2^-8,
-// subnormals included.  The 2^8 comes back through the conversion's power-of-
-// two scale below, so e * S_b is formed exactly.
-__device__ __forceinline__ _Float16 scale_h(uint32_t byte) {
-    return __builtin_bit_cast(_Float16, (unsigned short)((byte & 0x7Fu) << 7));
-}
-
-// Eight E2M1 codes (one dword, element 2j in the low nibble of byte j) times the
-// block scale -> eight exact f16.  The gfx950 scaled conversion applies only the
-// exponent of its fp32 scale operand, so it is used for the exact factor 2^8 and
-// the E4M3 scale (times 2^-8) is applied with a packed f16 multiply; every
-// product e * S_b has at most 6 significant bits and lies in [2^-10, 2688], so
-// both steps are exact.
-__device__ __forceinline__ half8 dequant8(uint32_t w, _Float16 s) {
-    half2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 0);
-    half2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 1);
-    half2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 2);
-    half2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 3);
-    const half2v s2 = {s, s};
-    p0 *= s2; p1 *= s2; p2 *= s2; p3 *= s2;
-    half8 r;
-    r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
-    r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
-    return r;
-}
-
-__device__ __forceinline__ uint32_t get(const uint4& v, int u) {
-    return u == 0 ? v.x : (u == 1 ? v.y : (u == 2 ? v.z : v.w));
-}
-
-__device__ __forceinline__ uint4 ld128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-    return make_uint4(v[0], v[1], v[2], v[3]);
-}
 
 // Scale bytes of a wave's MAXS steps, per lane: NVFP4 2 bytes per step, MXFP4
 // 1.  Up to four steps sit in one quad entry and come with one load; eight
@@ -269,7 +225,7 @@ __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmArgs p) {
             if (kPre) {
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
-                    a_h[rt][t][u] = dequant8(get(a_raw[rt][t], u), scale_h((a_rsc[rt][t] >> (u < 2 ? 0 : 8)) & 0xFFu));
+                    a_h[rt][t][u] = dequant8(word(a_raw[rt][t], u), scale_h((a_rsc[rt][t] >> (u < 2 ? 0 : 8)) & 0xFFu));
             } else {
                 a_codes[rt][t] = a_raw[rt][t];
                 a_sc[rt][t] = a_rsc[rt][t];
@@ -337,7 +293,7 @@ __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmArgs p) {
                 const _Float16 sw0 = scale_h(w_sc.byte(t, 0)), sw1 = scale_h(w_sc.byte(t, 1));
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    const half8 b = dequant8(get(w_codes[t], u), u < 2 ? sw0 : sw1);
+                    const half8 b = dequant8(word(w_codes[t], u), u < 2 ? sw0 : sw1);
 #pragma unroll
                     for (int rt = 0; rt < RT; ++rt) {
                         half8 a;
@@ -347,7 +303,7 @@ __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmArgs p) {
                             // the empty asm keeps the compiler from hoisting this
                             // loop-invariant dequantization out of the group loop,
                             // which would hold every f16 fragment in registers
-                            uint32_t ac = get(a_codes[rt][t], u), as = a_sc[rt][t];
+                            uint32_t ac = word(a_codes[rt][t], u), as = a_sc[rt][t];
                             asm volatile("" : "+v"(ac), "+v"(as));
                             a = dequant8(ac, scale_h((as >> (u < 2 ? 0 : 8)) & 0xFFu));
                         }
