@@ -41,8 +41,8 @@ METRIC = "compensated FP4 linear µs/call + HBM GB/s (% of peak) at M=1–8, K,N
 # calibration factors (FETCH_SIZE x2.0, WRITE_SIZE x1.0).  Valid only for the
 # kernel sources whose hash is recorded; reported as null otherwise.
 TRAFFIC = {
-    "sources_sha256": "8bcad022e50e04b1f0485d6865f80b422f7ec4922f923d92411a631f5aa4d324",
-    "fetch_bytes": 2.0 * 4725 * 1024,   # FETCH_SIZE 4725 KiB per launch
+    "sources_sha256": "cf0fa1731979a6a153ed9529fb9d447e9fcf6a0fb701d50b8f47aeabebedac9e",
+    "fetch_bytes": 2.0 * 4726 * 1024,   # FETCH_SIZE 4726 KiB per launch
     "write_bytes": 1.0 * 64 * 1024,     # WRITE_SIZE 64 KiB per launch
 }
 KERNEL_SOURCES = ["gemm.hip", "layout.h", "codec.h", "fp4_frag.h"]

@@ -210,6 +210,27 @@ __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmArgs p) {
         }
     }
 
+    // NVFP4 tensor scales of the rows this lane folds and stores (the
+    // epilogue's only global reads), fetched with the fragments: item (rt, pr)
+    // covers tile rows ti0 = 16rt + 4g + 2pr and ti0 + 1, i.e. token row ti0/2
+    // (base and residue) when compensated, rows ti0 and ti0 + 1 otherwise.
+    float row_s0[2 * RT], row_s1[2 * RT];
+#pragma unroll
+    for (int item = 0; item < 2 * RT; ++item) {
+        row_s0[item] = row_s1[item] = 0.0f;
+        if (FMT == kNV) {
+            const int ti0 = 16 * (item >> 1) + 4 * g + 2 * (item & 1);
+            const int r0 = COMP ? ti0 >> 1 : ti0;
+            const int r1 = COMP ? p.M + (ti0 >> 1) : ti0 + 1;
+            const bool v0 = COMP ? (ti0 >> 1) < p.M : r0 < p.M;
+            const bool v1 = COMP ? v0 : r1 < p.M;
+            row_s0[item] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                ra, v0 ? (uint32_t)(r0 * p.row_bytes) : act_bytes, 0, 0));
+            row_s1[item] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                ra, v1 ? (uint32_t)(r1 * p.row_bytes) : act_bytes, 0, 0));
+        }
+    }
+
 #pragma unroll
     for (int q = 0; q < PD; ++q) load_w(c0 + q * grid, wb[q], wsc[q]);
 
@@ -253,9 +274,7 @@ __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmArgs p) {
                     if (m < p.M) {
                         float out;
                         if (FMT == kNV) {
-                            const float sx = *reinterpret_cast<const float*>(p.act + (int64_t)m * p.row_bytes);
-                            const float sr = *reinterpret_cast<const float*>(p.act + (int64_t)(p.M + m) * p.row_bytes);
-                            out = s_gw * (sx * v0 + sr * v1);
+                            out = s_gw * (row_s0[item] * v0 + row_s1[item] * v1);
                         } else {
                             out = v0 + v1;
                         }
@@ -269,8 +288,7 @@ __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmArgs p) {
                         if (m < p.M) {
                             const float v = h ? v1 : v0;
                             float out = v;
-                            if (FMT == kNV)
-                                out = s_gw * (*reinterpret_cast<const float*>(p.act + (int64_t)m * p.row_bytes) * v);
+                            if (FMT == kNV) out = s_gw * ((h ? row_s1[item] : row_s0[item]) * v);
                             if (p.accum) out += reinterpret_cast<const float*>(p.y)[(int64_t)m * p.N + n];
                             store_y(p.y, (int64_t)m * p.N + n, out, p.out_bf16);
                         }
