@@ -37,29 +37,25 @@ __device__ __forceinline__ float e2m1_val(uint32_t code) {
     return (code & 8u) ? -v : v;
 }
 
-// E4M3 (FN variant) byte -> value, for bytes 0x00..0x7e (non-negative scales).
+// E4M3 (FN variant) through gfx950's FP8 conversions (v_cvt_pk_fp8_f32 and
+// v_cvt_f32_fp8), which use the OCP E4M3FN format on this chip.  Measured on
+// the MI355X against the software rule (nearest finite value, ties to the even
+// code, saturating at 448 = 0x7e): the encoder rounds to nearest even into the
+// subnormals and agrees for every 0 < t <= 464 tried (all grid points, their
+// midpoints and one ulp either side of each, 2^20 log-uniform values); above
+// 464 it returns the NaN code 0x7f, so t is clamped to 448 first (every
+// t >= 448 saturates to 448 anyway).  The decoder returns the exact value of
+// every finite code.
+//
+// E4M3 byte -> value, for bytes 0x00..0x7e (non-negative scales).
 __device__ __forceinline__ float e4m3_val(uint32_t b) {
-    const uint32_t e = (b >> 3) & 15u, m = b & 7u;
-    const float sub = (float)m * 0.001953125f;               // m * 2^-9
-    const float nrm = __uint_as_float(((e + 120u) << 23) | (m << 20));
-    return e ? nrm : sub;
+    return __builtin_amdgcn_cvt_f32_fp8((int)b, 0);
 }
 
 // Non-negative t -> E4M3 byte: nearest finite value, ties to even code,
 // saturating at 448 (0x7e, never the NaN code 0x7f); t NaN or <= 0 -> 0.
-// The subnormal range [0, 2^-6) is a uniform grid of step 2^-9, so the code is
-// rint(t * 2^9); above it the 3-bit mantissa of t is rounded with rint.  Both
-// candidates are computed and selected (no branches: this sits on the
-// quantizer's critical path).
 __device__ __forceinline__ uint32_t e4m3_encode(float t) {
-    const uint32_t sub = (uint32_t)__builtin_rintf(fminf(t, 0.015625f) * 512.0f);  // t < 2^-6: 0..8
-    const uint32_t bits = __float_as_uint(t);
-    const int e = (int)((bits >> 23) & 255u) - 127;
-    const float m = __uint_as_float((bits & 0x007FFFFFu) | 0x3F800000u);   // [1,2)
-    const uint32_t mm = (uint32_t)__builtin_rintf((m - 1.0f) * 8.0f);     // 0..8, 8 carries
-    const uint32_t nrm = (uint32_t)((e + 7) << 3) + mm;
-    uint32_t code = t < 0.015625f ? sub : nrm;
-    code = t >= 448.0f ? 0x7Eu : code;
+    const uint32_t code = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(t, 448.0f), 0.0f, 0, false) & 0xFFu;
     return t > 0.0f ? code : 0u;                                          // NaN and <= 0 -> 0
 }
 

@@ -88,17 +88,47 @@ __device__ __forceinline__ void load_chunk<__hip_bfloat16, 8>(const __hip_bfloat
     }
 }
 
+// The NVFP4 block-scale quotient bm / b, b = RN(6 s_g) shared by the row.
+// FAST rows (tensor scale in [2^-80, 2^80], as for the element quotients
+// below) divide once per row, y = RN(1/b), and per block apply Markstein's
+// correction: q = RN(bm y), the remainder bm - b q (exact), RN(q + r y) =
+// RN(bm / b).  b and y are normal there and the quotient is at most 448;
+// quotients below 2^-22 (which encode to byte 0 however they round) aside,
+// bm >= 2^-100, so q is faithful and the remainder is exact and normal.
+struct BlockDiv {
+    float b, y;
+};
+
+template <bool FAST>
+__device__ __forceinline__ BlockDiv make_block_div(float s_g) {
+    BlockDiv d;
+    d.b = 6.0f * s_g;
+    d.y = FAST ? 1.0f / d.b : 0.0f;
+    return d;
+}
+
 // Block scale of a block whose largest magnitude is bm: the scale byte and the
 // effective element scale s~ (NVFP4: E4M3_RNE(bm / (6 s_g)) and S_b * s_g;
 // MXFP4: the E8M0 rule and its power of two).
-template <int FMT>
-__device__ __forceinline__ float block_scale(float bm, float s_g, uint32_t& sbyte) {
+template <int FMT, bool FAST>
+__device__ __forceinline__ float block_scale(float bm, float s_g, const BlockDiv& bd, uint32_t& sbyte) {
     if (FMT == kNV) {
-        sbyte = e4m3_encode(bm / (6.0f * s_g));
+        float q;
+        if (FAST) {
+            const float q0 = bm * bd.y;
+            q = __builtin_fmaf(__builtin_fmaf(-bd.b, q0, bm), bd.y, q0);
+        } else {
+            q = bm / bd.b;
+        }
+        sbyte = e4m3_encode(q);
         return e4m3_val(sbyte) * s_g;
     }
     sbyte = e8m0_for_amax(bm);
     return e8m0_val(sbyte);
+}
+template <int FMT>
+__device__ __forceinline__ float block_scale(float bm, float s_g, uint32_t& sbyte) {
+    return block_scale<FMT, false>(bm, s_g, make_block_div<false>(s_g), sbyte);
 }
 
 // Element codes with the hardware conversion (codec.h): MXFP4 converts v with
@@ -195,6 +225,7 @@ __device__ __forceinline__ void quantize_chunks_q(float (&v)[NC][EPT], int nchun
                                                   uint8_t* codes, uint8_t* scales) {
     constexpr int LPB = (FMT == kNV ? 16 : 32) / EPT;   // lanes sharing one block
     const int tid = threadIdx.x;
+    const BlockDiv bd = make_block_div<FAST>(s_g);
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
         const int j = tid + (int)blockDim.x * c;     // chunk index
@@ -206,7 +237,7 @@ __device__ __forceinline__ void quantize_chunks_q(float (&v)[NC][EPT], int nchun
         if (LPB >= 4) bm = fmaxf(bm, dpp<kDppXor2>(bm));
         if (LPB >= 8) bm = fmaxf(bm, dpp<kDppHalfMirror>(bm));
         uint32_t sbyte;
-        const float st = block_scale<FMT>(bm, s_g, sbyte);   // effective element scale
+        const float st = block_scale<FMT, FAST>(bm, s_g, bd, sbyte);   // effective element scale
         // codes, and v becomes the residue x - fl(s~ e) (exact: Sterbenz)
         const uint32_t packed = encode_residue<FMT, EPT, FAST>(v[c], st);
         if (j < nchunks) {
