@@ -139,18 +139,27 @@ rsfp4_status linear(int fmt, bool comp, const void* act, size_t act_bytes, const
     if (st != RSFP4_OK) return st;
     // one launch covers up to kMaxNarrowK; a longer K takes two launches over
     // consecutive step ranges (the first a multiple of 8 steps), the second
-    // adding its part to y
+    // adding its part to y.  Compensated NVFP4 with two row tiles (B > 16)
+    // runs launches of at most 32 steps (2 per wave), where the activation
+    // fragments fit in registers as f16 (dequantized once, not at every use):
+    // the extra launches and read-modify-writes of y cost less than the
+    // dequantization they save.
     const int S = (int)num_steps(K);
-    const int split = K > kMaxNarrowK ? 8 * ((S + 15) / 16) : S;
-    for (int pass = 0; pass < (split < S ? 2 : 1); ++pass) {
-        const int s_lo = pass ? split : 0, s_hi = pass ? S : split;
+    int chunk = S;
+    if (K > kMaxNarrowK)
+        chunk = 8 * ((S + 15) / 16);
+    else if (fmt == RSFP4_NVFP4 && comp && B > 16 && !out_bf16 && S > 32)
+        chunk = 32;
+    const int passes = (S + chunk - 1) / chunk;
+    for (int pass = 0; pass < passes; ++pass) {
+        const int s_lo = pass * chunk, s_hi = s_lo + chunk < S ? s_lo + chunk : S;
         const GemmPlan pl = plan_gemm_small(M, N, s_hi - s_lo, comp, cus);
         if (std::getenv("RSFP4_LOG"))
             std::fprintf(stderr, "[rsfp4] linear fmt=%d comp=%d M=%lld N=%lld K=%lld steps=[%d,%d) rt=%d maxs=%d "
                          "kw=%d grid=%lld ngl=%d\n", fmt, (int)comp, (long long)M, (long long)N, (long long)K,
                          s_lo, s_hi, pl.rt, pl.maxs, pl.kw, (long long)pl.grid, pl.ngl);
         st = hip_status(launch_gemm_small(fmt, pl, comp, act, rb, w_packed, (int)M, N, K, y, out_bf16, s_lo,
-                                          s_hi, pass == 1, (hipStream_t)stream),
+                                          s_hi, pass > 0, (hipStream_t)stream),
                         "linear launch");
         if (st != RSFP4_OK) return st;
     }

@@ -9,8 +9,10 @@
 // A operand (output rows), ordered base/residue interleaved (tile row 2m = q(x)
 // row m, 2m+1 = q(r) row m), and each lane of the 16x16 accumulator holds tile
 // rows 4g..4g+3 of one channel, i.e. two complete pairs -- the Fold is a
-// thread-local fp32 add before the only store (the idea of the row-pair packing
-// of Figure 5, realised with MFMA lane ownership instead of TMEM loads).
+// thread-local fp32 operation (the idea of the row-pair packing of Figure 5,
+// realised with MFMA lane ownership instead of TMEM loads).  The NVFP4 row
+// scales s_x, s_r are constants along K, so each wave folds its partial sums,
+// s_x Z_m + s_r Z_{M+m}, before they leave registers.
 //
 // Work decomposition (one design for all M <= 16, i.e. B <= 32; one launch
 // covers up to 16 waves x 8 steps = 16384 elements of K, and longer K runs as
@@ -33,10 +35,11 @@
 //   * MXFP4: codes and E8M0 scales go straight into the native block-scaled
 //     v_mfma_scale_f32_16x16x128_f8f6f4 (FP4 x FP4, one scale per lane = per
 //     32-element block), no dequantization at all;
-//   * the KW partial accumulators of a group meet in LDS; the last wave to
-//     deposit its partial (an LDS counter per group) sums the KW partials in a
-//     fixed order (deterministic), folds and stores, so no barrier is needed
-//     while groups are streamed.  When a workgroup owns more groups than LDS
+//   * the KW partial accumulators of a group meet in LDS (compensated: already
+//     folded, half the bytes); the last wave to deposit its partial (an LDS
+//     counter per group) sums the KW partials in a fixed order
+//     (deterministic), scales and stores, so no barrier is needed while groups
+//     are streamed.  When a workgroup owns more groups than LDS
 //     slots, the slots are recycled after a workgroup barrier.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -127,6 +130,7 @@ __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmArgs p) {
     constexpr int kAC = kPre ? 1 : MAXS;     // code registers kept per row tile
     constexpr int kAH = kPre ? MAXS : 1;     // f16 fragments kept per row tile
     constexpr int NB = PD + 1;               // weight buffers in the ring
+    constexpr int PW = COMP ? 2 : 4;         // partial sums per lane and row tile in LDS
     using SW = ScaleWord<FMT, MAXS>;
     constexpr int64_t SB1 = scale_bytes_per_step_lane(FMT);
 
@@ -260,38 +264,37 @@ __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmArgs p) {
 #pragma unroll
         for (int item = 0; item < 2 * RT; ++item) {   // (row tile, pair) per lane
             const int rt = item >> 1, pr = item & 1;
-            const float* src = red + (slot * KW * RT + rt) * 256 + (2 * pr) * 64 + lane;
-            float v0 = 0.0f, v1 = 0.0f;
-            for (int w = 0; w < KW; ++w) {
-                v0 += src[w * RT * 256];
-                v1 += src[w * RT * 256 + 64];
-            }
             const int ti0 = 16 * rt + 4 * g + 2 * pr;    // tile rows ti0, ti0 + 1
             const int64_t n = c * kGroupN + i;
+            if (COMP) {
+                // the waves' folded partials of token row ti0 / 2, in wave order
+                const float* src = red + (slot * KW * RT + rt) * (PW * 64) + pr * 64 + lane;
+                float v = 0.0f;
+                for (int w = 0; w < KW; ++w) v += src[w * RT * (PW * 64)];
+                const int m = ti0 >> 1;
+                if (n < p.N && m < p.M) {
+                    float out = FMT == kNV ? s_gw * v : v;
+                    if (p.accum) out += reinterpret_cast<const float*>(p.y)[(int64_t)m * p.N + n];
+                    store_y(p.y, (int64_t)m * p.N + n, out, p.out_bf16);
+                }
+                continue;
+            }
+            const float* src = red + (slot * KW * RT + rt) * (PW * 64) + (2 * pr) * 64 + lane;
+            float v0 = 0.0f, v1 = 0.0f;
+            for (int w = 0; w < KW; ++w) {
+                v0 += src[w * RT * (PW * 64)];
+                v1 += src[w * RT * (PW * 64) + 64];
+            }
             if (n < p.N) {
-                if (COMP) {
-                    const int m = ti0 >> 1;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int m = ti0 + h;
                     if (m < p.M) {
-                        float out;
-                        if (FMT == kNV) {
-                            out = s_gw * (row_s0[item] * v0 + row_s1[item] * v1);
-                        } else {
-                            out = v0 + v1;
-                        }
+                        const float v = h ? v1 : v0;
+                        float out = v;
+                        if (FMT == kNV) out = s_gw * ((h ? row_s1[item] : row_s0[item]) * v);
                         if (p.accum) out += reinterpret_cast<const float*>(p.y)[(int64_t)m * p.N + n];
                         store_y(p.y, (int64_t)m * p.N + n, out, p.out_bf16);
-                    }
-                } else {
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const int m = ti0 + h;
-                        if (m < p.M) {
-                            const float v = h ? v1 : v0;
-                            float out = v;
-                            if (FMT == kNV) out = s_gw * ((h ? row_s1[item] : row_s0[item]) * v);
-                            if (p.accum) out += reinterpret_cast<const float*>(p.y)[(int64_t)m * p.N + n];
-                            store_y(p.y, (int64_t)m * p.N + n, out, p.out_bf16);
-                        }
                     }
                 }
             }
@@ -340,11 +343,26 @@ __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmArgs p) {
                 }
             }
         }
-        float* dst = red + ((slot * KW + wave) * RT) * 256;
+        float* dst = red + ((slot * KW + wave) * RT) * (PW * 64);
+        if (COMP) {
+            // the Fold per wave: the row scales are constant along K, so
+            // s_x m * Z_m + s_r m * Z_M+m folds each partial before the sum
+            // over the waves (half the LDS of the unfolded pairs)
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
+            for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) dst[(rt * 4 + r) * 64 + lane] = acc[rt][r];
+                for (int pr = 0; pr < 2; ++pr) {
+                    const int item = 2 * rt + pr;
+                    const float f = FMT == kNV ? row_s0[item] * acc[rt][2 * pr] + row_s1[item] * acc[rt][2 * pr + 1]
+                                               : acc[rt][2 * pr] + acc[rt][2 * pr + 1];
+                    dst[item * 64 + lane] = f;
+                }
+        } else {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dst[(rt * 4 + r) * 64 + lane] = acc[rt][r];
+        }
         if (RM == 0) {
             // publish this wave's partial, then count it in
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -400,7 +418,7 @@ hipError_t launch_t(const GemmArgs& a, int KW, int64_t grid, hipStream_t s) {
         reinterpret_cast<const void*>(&gemm_small_kernel<FMT, MAXS, RT, COMP, PD, APRE, RM>),
         hipFuncAttributeMaxDynamicSharedMemorySize, kRedBytesMax + 1024);
     if (attr != hipSuccess) return attr;
-    const size_t lds = (size_t)((a.ngl + 63) & ~63) * 4 + (size_t)a.ngl * KW * RT * 1024;
+    const size_t lds = (size_t)((a.ngl + 63) & ~63) * 4 + (size_t)a.ngl * KW * RT * (COMP ? 512 : 1024);
     hipLaunchKernelGGL((gemm_small_kernel<FMT, MAXS, RT, COMP, PD, APRE, RM>), dim3((unsigned)grid),
                        dim3(64 * KW), lds, s, a);
     return hipGetLastError();
@@ -417,8 +435,10 @@ constexpr int pd_for(int fmt, int rt, int maxs, bool single) {
     if (fmt == kNV) return maxs <= 4 ? 1 : 0;
     return rt == 1 ? (maxs <= 4 ? 1 : 0) : (maxs <= 2 ? 1 : 0);
 }
-constexpr bool apre_for(int fmt, int rt, int maxs, bool single) {
-    return fmt == kNV && rt == 1 && maxs <= (single ? 4 : 2);
+constexpr bool apre_for(int fmt, int rt, int maxs, bool single, bool comp) {
+    // two row tiles: 2 steps per wave fit the f16 fragments without spills
+    // (the compensated kernels; the plain ones spill)
+    return fmt == kNV && (rt == 1 ? maxs <= (single ? 4 : 2) : (comp && maxs <= 2));
 }
 constexpr int rm_for(int fmt, int rt, int maxs, bool single) { return single ? 0 : 1; }
 
@@ -437,7 +457,7 @@ hipError_t launch_rm(const GemmArgs& a, int KW, int64_t grid, hipStream_t s, int
 template <int FMT, bool COMP, int MAXS>
 hipError_t launch_tune(const GemmArgs& a, int KW, int64_t grid, hipStream_t s) {
     const int pd = tune_env("RSFP4_TUNE_PD", pd_for(FMT, 1, MAXS, false));
-    const bool apre = tune_env("RSFP4_TUNE_APRE", apre_for(FMT, 1, MAXS, false)) != 0;
+    const bool apre = tune_env("RSFP4_TUNE_APRE", apre_for(FMT, 1, MAXS, false, COMP)) != 0;
     const int rm = tune_env("RSFP4_TUNE_RM", rm_for(FMT, 1, MAXS, false));
     switch (pd * 2 + (apre ? 1 : 0)) {
         case 0: return launch_rm<FMT, COMP, MAXS, 0, false>(a, KW, grid, s, rm);
@@ -458,9 +478,9 @@ hipError_t launch_v(const GemmArgs& a, int KW, int64_t grid, hipStream_t s, bool
     if (RT == 1 && COMP) return launch_tune<FMT, COMP, MAXS>(a, KW, grid, s);
 #endif
     if (single)
-        return launch_t<FMT, MAXS, RT, COMP, pd_for(FMT, RT, MAXS, true), apre_for(FMT, RT, MAXS, true),
+        return launch_t<FMT, MAXS, RT, COMP, pd_for(FMT, RT, MAXS, true), apre_for(FMT, RT, MAXS, true, COMP),
                         rm_for(FMT, RT, MAXS, true)>(a, KW, grid, s);
-    return launch_t<FMT, MAXS, RT, COMP, pd_for(FMT, RT, MAXS, false), apre_for(FMT, RT, MAXS, false),
+    return launch_t<FMT, MAXS, RT, COMP, pd_for(FMT, RT, MAXS, false), apre_for(FMT, RT, MAXS, false, COMP),
                     rm_for(FMT, RT, MAXS, false)>(a, KW, grid, s);
 }
 
@@ -500,7 +520,7 @@ GemmPlan plan_gemm_small(int64_t M, int64_t N, int64_t S, bool comp, int num_cus
     const int64_t per_wg = (G + pl.grid - 1) / pl.grid;         // groups per workgroup
     // LDS per workgroup: at most 128 KB, and small enough for per_cu of them
     const int64_t lds_cap = kRedBytesMax < kLdsPerCu / per_cu - 1024 ? kRedBytesMax : kLdsPerCu / per_cu - 1024;
-    const int64_t fit = lds_cap / ((int64_t)pl.kw * pl.rt * 1024);
+    const int64_t fit = lds_cap / ((int64_t)pl.kw * pl.rt * (comp ? 512 : 1024));
     pl.ngl = (int)(per_wg < fit ? per_wg : fit);
     if (pl.ngl < 1) pl.ngl = 1;
     return pl;

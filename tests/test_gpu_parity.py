@@ -209,6 +209,9 @@ SMALL_CASES = [  # (M, N, K): several tiles, ragged N and K tails, both row-tile
     # K past one narrow launch (two launches over the K steps, the second
     # adding to y), up to the longest supported K, and a wide operand there
     (4, 200, 20480), (2, 64, 32768), (40, 64, 24576),
+    # two row tiles, compensated NVFP4: launches of 32 steps adding into y
+    # (two full ones; one full and a ragged one; four)
+    (12, 80, 8192), (16, 48, 5120), (9, 40, 16384),
 ]
 
 
