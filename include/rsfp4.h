@@ -316,10 +316,12 @@ rsfp4_status rsfp4_kv_cache_write(const void* k, const void* v, int xt, int64_t 
                                   const int32_t* slots, float k_scale, float v_scale, void* cache,
                                   size_t cache_bytes, void* stream);
 
-/* KV splits the preset rule picks (about 8 waves per compute unit, at least 8
- * pages per split; ResServe Section 5.2: preset rules from batch size, KV heads,
- * sequence length and the unit count), and the workspace they need (0 for one
- * split): B * H_q * splits * (D + 2) * 4 bytes. */
+/* KV splits the preset rule picks (a power of two: at most about 8 waves per
+ * compute unit over B * H_kv items, and the smallest p with p^2 B > 8 pages,
+ * pages = ceil(max_seq_len / 32), i.e. about 4 sqrt(pages / B); never more than
+ * the pages or 1024; ResServe Section 5.2: preset rules from batch size, KV
+ * heads, sequence length and the unit count), and the workspace they need (0
+ * for one split): B * H_q * splits * (D + 2) * 4 bytes. */
 int rsfp4_resattn_splits(int64_t B, int64_t H_kv, int64_t max_seq_len);
 size_t rsfp4_resattn_workspace_bytes(int64_t B, int64_t H_q, int64_t D, int splits);
 

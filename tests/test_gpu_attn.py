@@ -210,3 +210,22 @@ def test_resattn_workload_sampled(cfg):
     sub.B = len(keep)
     ref, mag, vmax = sub.reference()
     _check(out[keep], ref, mag, vmax)
+
+
+def test_resattn_split_rule():
+    """The preset split count, a power of two: at most ~8 waves per compute
+    unit over B * H_kv items, and the smallest p with p^2 B > 8 pages (256
+    compute units)."""
+    import torch
+    rs = _rs()
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("rule values are for a 256-unit device")
+    assert rs.resattn_splits(1, 8, 8192) == 64          # 256 pages: 64^2 > 2048 >= 32^2
+    assert rs.resattn_splits(1, 8, 131072) == 256       # 4096 pages
+    assert rs.resattn_splits(1, 8, 16384) == 128        # 512 pages: 64^2 = 4096 is not above 4096
+    assert rs.resattn_splits(4, 8, 8192) == 32          # 32^2 * 4 > 2048
+    assert rs.resattn_splits(8, 8, 8192) == 32          # 16^2 * 8 = 2048 is not above 2048
+    assert rs.resattn_splits(4, 8, 65536) == 64         # capped: 8 waves per unit over 32 items
+    assert rs.resattn_splits(32, 8, 8192) == 8          # capped: 8 waves per unit over 256 items
+    assert rs.resattn_splits(1, 8, 32) == 1             # one page
+    assert rs.resattn_splits(1, 8, 100) == 4            # 4 pages: 8, capped at the pages
