@@ -296,75 +296,56 @@ __global__ __launch_bounds__(64) void resattn_kernel(AttnArgs p) {
 
 // Combine the splits of one head: weights 2^(m_s - M) over the splits' row
 // maxima (base 2); empty splits (m = -inf) weigh 0.  The splits' (m, l) pairs
-// go to LDS once (coalesced), the weights are formed there, and then R groups
-// of D threads (blockDim = R * D) each sum their output element over every
-// R-th split with eight loads in flight; the R partial sums meet in LDS and
-// are added in group order (deterministic).
+// go to LDS once (coalesced), the weights are formed there, and each thread
+// then sums its output element over the splits with eight loads in flight.
 constexpr int kMaxSplits = 4096;
 
 template <int D>
-__global__ __launch_bounds__(1024) void resattn_reduce_kernel(AttnArgs p) {
+__global__ __launch_bounds__(D) void resattn_reduce_kernel(AttnArgs p) {
     __shared__ float wsh[kMaxSplits];
-    __shared__ float red[1024 / 64];
-    __shared__ float part[1024];
+    __shared__ float red[D / 64];
     const int64_t head = blockIdx.x;
-    const int t = threadIdx.x, nt = blockDim.x, nw = nt >> 6;
-    const int d = t % D, grp = t / D, R = nt / D;
+    const int d = threadIdx.x;
     const int S = p.splits;
     const float* ml = p.ws_ml + head * S * 2;
     // row maximum over the splits
     float mloc = -__builtin_inff();
-    for (int s = t; s < S; s += nt) {
+    for (int s = d; s < S; s += D) {
         const float ms = ml[2 * s];
         wsh[s] = ms;
         mloc = fmaxf(mloc, ms);
     }
     for (int off = 32; off > 0; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off, 64));
-    if ((t & 63) == 0) red[t >> 6] = mloc;
+    if ((d & 63) == 0) red[d >> 6] = mloc;
     __syncthreads();
     float M = red[0];
-    for (int w = 1; w < nw; ++w) M = fmaxf(M, red[w]);
+    for (int w = 1; w < D / 64; ++w) M = fmaxf(M, red[w]);
     __syncthreads();
     // weights and the weighted sum of the splits' row sums
     const bool live = M > -__builtin_inff();
     float dl = 0.0f;
-    for (int s = t; s < S; s += nt) {
+    for (int s = d; s < S; s += D) {
         const float w = live ? __builtin_amdgcn_exp2f(wsh[s] - M) : 0.0f;
         wsh[s] = w;
         dl += w * ml[2 * s + 1];
     }
     for (int off = 32; off > 0; off >>= 1) dl += __shfl_xor(dl, off, 64);
-    if ((t & 63) == 0) red[t >> 6] = dl;
+    if ((d & 63) == 0) red[d >> 6] = dl;
     __syncthreads();
     float den = 0.0f;
-    for (int w = 0; w < nw; ++w) den += red[w];
-    // group grp: splits grp, grp + R, grp + 2R, ...
+    for (int w = 0; w < D / 64; ++w) den += red[w];
     const float* src = p.ws_o + head * S * D + d;
     float num = 0.0f;
-    int s = grp;
-    for (; s + 7 * R < S; s += 8 * R) {
+    int s = 0;
+    for (; s + 8 <= S; s += 8) {
         float v[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = src[(int64_t)(s + u * R) * D];
+        for (int u = 0; u < 8; ++u) v[u] = src[(int64_t)(s + u) * D];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) num += wsh[s + u * R] * v[u];
+        for (int u = 0; u < 8; ++u) num += wsh[s + u] * v[u];
     }
-    for (; s < S; s += R) num += wsh[s] * src[(int64_t)s * D];
-    part[t] = num;
-    __syncthreads();
-    if (grp == 0) {
-        float tot = part[d];
-        for (int g2 = 1; g2 < R; ++g2) tot += part[g2 * D + d];
-        store_y(p.out, head * D + d, den > 0.0f ? tot / den : 0.0f, p.out_bf16);
-    }
-}
-
-// Thread groups of the combining kernel: about 16 splits per group, at most
-// 1024 threads.
-inline int reduce_groups(int splits, int D) {
-    int r = 1;
-    while (r * 2 * D <= 1024 && r * 2 * 16 <= splits) r *= 2;
-    return r;
+    for (; s < S; ++s) num += wsh[s] * src[(int64_t)s * D];
+    store_y(p.out, head * D + d, den > 0.0f ? num / den : 0.0f, p.out_bf16);
 }
 
 template <int D>
@@ -372,8 +353,7 @@ hipError_t launch_attn_d(const AttnArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(resattn_kernel<D>, dim3((unsigned)a.splits, (unsigned)a.H_kv, (unsigned)a.B), dim3(64), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1) return e;
-    hipLaunchKernelGGL(resattn_reduce_kernel<D>, dim3((unsigned)(a.B * a.H_q)), dim3(D * reduce_groups(a.splits, D)),
-                       0, s, a);
+    hipLaunchKernelGGL(resattn_reduce_kernel<D>, dim3((unsigned)(a.B * a.H_q)), dim3(D), 0, s, a);
     return hipGetLastError();
 }
 
