@@ -1,8 +1,10 @@
 """Benchmark of the residue-compensated NVFP4/MXFP4 linear on one MI355X.
 
-A step is one pass of the whole hot path over one synthetic batch: the fused
-activation quantize+residue kernel followed by the compensated linear
-(weights are prepacked once, offline, as the method prescribes).  The headline
+A step is one pass of the whole hot path over one synthetic batch: activation
+quantize + residue and the compensated linear, as the library's one-call entry
+runs them (weights are prepacked once, offline, as the method prescribes):
+the quantize kernel followed by the linear, or, for few rows to quantize, one
+launch of the linear that quantizes its rows in every workgroup.  The headline
 workload is the attention projection: NVFP4, M = 4 token rows, K = N = 4096,
 x in bf16.  Steps rotate over distinct weight copies (> 2x the 256 MB Infinity
 Cache) so every step streams its weights from HBM, and are replayed from a HIP
@@ -106,9 +108,14 @@ class Setup:
         f = self.rs.fp4_linear_compensated if comp else self.rs.fp4_linear
         f(self.acts[r], self.blobs[r], self.M, self.N, self.K, self.fmt, out=self.ys[r])
 
-    def step(self, i, comp):
+    def two_launch(self, i, comp):
         self.quant(i, comp)
         self.gemm(i, comp)
+
+    def step(self, i, comp):
+        r = i % self.R
+        self.rs.fp4_linear_from_x(self.xs[r], self.blobs[r], self.N, self.fmt, comp, out=self.ys[r],
+                                  act=self.acts[r])
 
 
 class KextSetup:
@@ -301,6 +308,9 @@ def run_workload(rs, torch, wl, M, steps, warmup, want_plain=True, want_kernels=
     t_comp = time_graph(torch, lambda i: S.step(i, True), steps, warmup)
     out["us_per_call"] = t_comp * 1e3
     out["GBps"] = sb / (t_comp * 1e-3) / 1e9
+    out["launches"] = rs.from_x_launches(fmt, M, wl.N, wl.K, True)
+    if out["launches"] == 1:   # the two-launch step beside the one-launch one
+        out["two_launch_us_per_call"] = time_graph(torch, lambda i: S.two_launch(i, True), steps, warmup) * 1e3
     if want_kernels:
         t_g = time_graph(torch, lambda i: S.gemm(i, True), steps, warmup)
         t_q = time_graph(torch, lambda i: S.quant(i, True), steps, warmup)

@@ -188,6 +188,38 @@ def mxfp4_linear_compensated(act, w_packed, M, N, K, out=None):
     return _linear(act, w_packed, M, N, K, MXFP4, True, out)
 
 
+# ------------------------------------------- quantize + linear in one call --
+
+def from_x_launches(fmt, M, N, K, compensated=True, x_dtype=None):
+    """1 or 2: the kernel launches fp4_linear_from_x makes for this shape."""
+    import torch
+    xt = _dtype_code(torch.empty(0, dtype=x_dtype if x_dtype is not None else torch.bfloat16))
+    return lib().rsfp4_from_x_launches(_fmt(fmt), xt, M, N, K, 1 if compensated else 0)
+
+
+def fp4_linear_from_x(x, w_packed, N, fmt, compensated=True, out=None, out_dtype=None, act=None):
+    """Quantize x[M, K] (cuda, fp32/bf16) and apply the linear in one call:
+    y [M, N] (fp32, or bf16 with out_dtype=torch.bfloat16).  act: an
+    activation buffer of packed_act_bytes(fmt, M, K, compensated) bytes that
+    the call uses where the quantizer and the linear run as two launches
+    (allocated here when omitted)."""
+    import torch
+    fmt = _fmt(fmt)
+    assert x.is_cuda and x.dim() == 2 and x.is_contiguous()
+    M, K = x.shape
+    dt = out_dtype if out_dtype is not None else (out.dtype if out is not None else torch.float32)
+    assert dt in (torch.float32, torch.bfloat16)
+    if out is None:
+        out = torch.empty((M, N), dtype=dt, device=x.device)
+    assert out.is_cuda and out.dtype == dt and out.is_contiguous() and out.numel() >= M * N
+    if act is None:
+        act = torch.empty(packed_act_bytes(fmt, M, K, compensated), dtype=torch.uint8, device=x.device)
+    name = f"rsfp4_{_FMT_NAME[fmt]}_linear" + ("_compensated" if compensated else "") + "_from_x"
+    _check(getattr(lib(), name)(_ptr(x), _dtype_code(x), M, N, K, _ptr(w_packed), w_packed.numel(), _ptr(out),
+                                _dtype_code(out), _ptr(act), act.numel(), _stream(x)))
+    return out
+
+
 # ------------------------------------------- paper numerics (tensor scale) --
 
 def nvfp4_tensor_alpha(x, out=None):

@@ -46,10 +46,13 @@
 
 #include <cstdlib>
 
+#include <type_traits>
+
 #include "codec.h"
 #include "fp4_frag.h"
 #include "kernels.h"
 #include "layout.h"
+#include "quant_row.h"
 
 namespace rsfp4 {
 
@@ -58,6 +61,7 @@ namespace {
 constexpr int kMaxWaves = 16;
 constexpr int kRedBytesMax = 128 * 1024;   // LDS for partial sums per workgroup
 constexpr int kLdsPerCu = 160 * 1024;      // gfx950
+constexpr int kLdsInq = 150 * 1024;        // partials + records, quantizing in the workgroup
 
 // Scale bytes of a wave's MAXS steps, per lane: NVFP4 2 bytes per step, MXFP4
 // 1.  Up to four steps sit in one quad entry and come with one load; eight
@@ -109,6 +113,8 @@ struct GemmArgs {
     int64_t k_hi;     // K elements at or past k_hi are left to another launch
     int accum;        // add to y instead of overwriting it (fp32 output only)
     int out_bf16;     // store y as bf16 (round to nearest even)
+    const void* x;    // in-workgroup quantization: the input rows x[M, K]
+    int qrow;         // threads per quantized row (a multiple of 64)
 };
 
 // APRE: the activation fragments are dequantized to f16 once, before the
@@ -122,8 +128,20 @@ struct GemmArgs {
 // to deposit its partial (LDS counter) reduces the group at once.  RM = 1: the
 // partials of up to ngl groups wait in LDS and the waves reduce them together
 // after one barrier (one group per wave).
-template <int FMT, int MAXS, int RT, bool COMP, int PD, bool APRE, int RM>
+//
+// XT (void: the activation records come from act in global memory): every
+// workgroup quantizes the M input rows x[M, K] (dtype XT) itself, with the
+// quantizer's row routine, into records in its LDS -- the same bytes the
+// quantize kernel writes -- and reads its fragments from there.  The rows are
+// quantized in parallel, p.qrow threads per row, NCQ chunks of 8 per thread;
+// the x loads go out before the weight loads (the memory counter is in order)
+// and the quantization runs while the weights are in flight.  Every workgroup
+// repeats the same quantization, on a compute unit that would otherwise wait
+// for its weights; no workgroup depends on another.
+template <int FMT, int MAXS, int RT, bool COMP, int PD, bool APRE, int RM, typename XT = void, int NCQ = 1>
 __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmArgs p) {
+    constexpr bool kInq = !std::is_void<XT>::value;
+    using XIn = std::conditional_t<kInq, XT, float>;
     // LDS: [ngl] counters (padded to 64), then [ngl][KW][RT][4][64] partial sums
     extern __shared__ float lds[];
     constexpr bool kPre = APRE && FMT == kNV;
@@ -147,6 +165,8 @@ __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmArgs p) {
     const int ngl = p.ngl;
     int* counters = reinterpret_cast<int*>(lds);
     float* red = lds + ((ngl + 63) & ~63);
+    // in-workgroup quantization: the B activation records after the partials
+    uint8_t* act_lds = reinterpret_cast<uint8_t*>(red + ngl * KW * RT * PW * 64);
 
     float s_gw = 1.0f;
     if (FMT == kNV) s_gw = reinterpret_cast<const WHeader*>(p.blob)->s_g;
@@ -178,6 +198,21 @@ __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmArgs p) {
         load_scales<FMT, MAXS>(r, sc_off, sc);
     };
 
+    // in-workgroup quantization: this thread's row and chunks of x, loaded
+    // before any weight load
+    const int qrow = kInq ? p.qrow : 64;
+    const int mq = kInq ? (int)threadIdx.x / qrow : 0;
+    const bool qactive = kInq && mq < p.M;
+    const int qlt = qactive ? (int)threadIdx.x % qrow : lane;
+    const int qnt = qactive ? qrow : 64;
+    float xq[NCQ][8];
+    if constexpr (kInq)
+        row_load<NCQ, 8, XIn>(static_cast<const XIn*>(p.x) + (int64_t)(qactive ? mq : 0) * p.K, p.K, qlt, qnt, qactive, xq);
+    auto quantize_rows = [&](float (*qred)[kQMaxThreads / 64]) {
+        row_quantize<FMT, NCQ, 8>(xq, p.K, qlt, qnt, qactive, COMP ? 1 : 0, act_lds + (int64_t)mq * p.row_bytes,
+                                  act_lds + (int64_t)(p.M + mq) * p.row_bytes, qred);
+    };
+
     // ---- activation fragments: loaded once, kept in registers ----
     // Their loads go out first; the first groups' weight loads follow at once,
     // so both latencies overlap and the fragments can be dequantized while the
@@ -188,57 +223,84 @@ __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmArgs p) {
         (void*)p.act, (short)0, (int)act_bytes, kRsrcWord3);
     uint4 a_raw[RT][MAXS];
     uint32_t a_rsc[RT][MAXS];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-        const int ti = 16 * rt + i;               // tile row of this lane's A operand
-        int arow;
-        bool rvalid;
-        if (COMP) {
-            const int m = ti >> 1;
-            rvalid = m < p.M;
-            arow = (ti & 1) ? p.M + m : m;
-        } else {
-            rvalid = ti < p.M;
-            arow = ti;
-        }
-#pragma unroll
-        for (int t = 0; t < MAXS; ++t) {
-            const int64_t k0 = kStepK * (s0 + t) + 32 * g;
-            const bool in = rvalid && k0 < p.k_hi;   // else: out of range -> zeros
-            const uint32_t rec = in ? (uint32_t)(arow * p.row_bytes) : act_bytes;
-            a_raw[rt][t] = ld128(ra, in ? rec + (uint32_t)(kActHead + k0 / 2) : act_bytes);
-            if (FMT == kNV)
-                a_rsc[rt][t] = __builtin_amdgcn_raw_buffer_load_b16(ra, in ? rec + scale_base + (uint32_t)(k0 / 16) : act_bytes, 0, 0);
-            else
-                a_rsc[rt][t] = __builtin_amdgcn_raw_buffer_load_b8(ra, in ? rec + scale_base + (uint32_t)(k0 / 32) : act_bytes, 0, 0);
-        }
-    }
-
-    // NVFP4 tensor scales of the rows this lane folds and stores (the
-    // epilogue's only global reads), fetched with the fragments: item (rt, pr)
-    // covers tile rows ti0 = 16rt + 4g + 2pr and ti0 + 1, i.e. token row ti0/2
-    // (base and residue) when compensated, rows ti0 and ti0 + 1 otherwise.
     float row_s0[2 * RT], row_s1[2 * RT];
+    auto load_act = [&]() {
 #pragma unroll
-    for (int item = 0; item < 2 * RT; ++item) {
-        row_s0[item] = row_s1[item] = 0.0f;
-        if (FMT == kNV) {
-            const int ti0 = 16 * (item >> 1) + 4 * g + 2 * (item & 1);
-            const int r0 = COMP ? ti0 >> 1 : ti0;
-            const int r1 = COMP ? p.M + (ti0 >> 1) : ti0 + 1;
-            const bool v0 = COMP ? (ti0 >> 1) < p.M : r0 < p.M;
-            const bool v1 = COMP ? v0 : r1 < p.M;
-            row_s0[item] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                ra, v0 ? (uint32_t)(r0 * p.row_bytes) : act_bytes, 0, 0));
-            row_s1[item] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                ra, v1 ? (uint32_t)(r1 * p.row_bytes) : act_bytes, 0, 0));
+        for (int rt = 0; rt < RT; ++rt) {
+            const int ti = 16 * rt + i;               // tile row of this lane's A operand
+            int arow;
+            bool rvalid;
+            if (COMP) {
+                const int m = ti >> 1;
+                rvalid = m < p.M;
+                arow = (ti & 1) ? p.M + m : m;
+            } else {
+                rvalid = ti < p.M;
+                arow = ti;
+            }
+#pragma unroll
+            for (int t = 0; t < MAXS; ++t) {
+                const int64_t k0 = kStepK * (s0 + t) + 32 * g;
+                const bool in = rvalid && k0 < p.k_hi;   // else: out of range -> zeros
+                const uint32_t rec = in ? (uint32_t)(arow * p.row_bytes) : act_bytes;
+                if (kInq) {
+                    const uint8_t* r8 = act_lds + rec;
+                    a_raw[rt][t] = in ? *reinterpret_cast<const uint4*>(r8 + kActHead + k0 / 2) : make_uint4(0, 0, 0, 0);
+                    if (FMT == kNV)
+                        a_rsc[rt][t] = in ? *reinterpret_cast<const uint16_t*>(r8 + scale_base + k0 / 16) : 0u;
+                    else
+                        a_rsc[rt][t] = in ? r8[scale_base + k0 / 32] : 0u;
+                    continue;
+                }
+                a_raw[rt][t] = ld128(ra, in ? rec + (uint32_t)(kActHead + k0 / 2) : act_bytes);
+                if (FMT == kNV)
+                    a_rsc[rt][t] = __builtin_amdgcn_raw_buffer_load_b16(ra, in ? rec + scale_base + (uint32_t)(k0 / 16) : act_bytes, 0, 0);
+                else
+                    a_rsc[rt][t] = __builtin_amdgcn_raw_buffer_load_b8(ra, in ? rec + scale_base + (uint32_t)(k0 / 32) : act_bytes, 0, 0);
+            }
         }
-    }
+
+        // NVFP4 tensor scales of the rows this lane folds and stores (the
+        // epilogue's only global reads), fetched with the fragments: item (rt, pr)
+        // covers tile rows ti0 = 16rt + 4g + 2pr and ti0 + 1, i.e. token row ti0/2
+        // (base and residue) when compensated, rows ti0 and ti0 + 1 otherwise.
+#pragma unroll
+        for (int item = 0; item < 2 * RT; ++item) {
+            row_s0[item] = row_s1[item] = 0.0f;
+            if (FMT == kNV) {
+                const int ti0 = 16 * (item >> 1) + 4 * g + 2 * (item & 1);
+                const int r0 = COMP ? ti0 >> 1 : ti0;
+                const int r1 = COMP ? p.M + (ti0 >> 1) : ti0 + 1;
+                const bool v0 = COMP ? (ti0 >> 1) < p.M : r0 < p.M;
+                const bool v1 = COMP ? v0 : r1 < p.M;
+                if (kInq) {
+                    row_s0[item] = v0 ? *reinterpret_cast<const float*>(act_lds + r0 * p.row_bytes) : 0.0f;
+                    row_s1[item] = v1 ? *reinterpret_cast<const float*>(act_lds + r1 * p.row_bytes) : 0.0f;
+                    continue;
+                }
+                row_s0[item] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                    ra, v0 ? (uint32_t)(r0 * p.row_bytes) : act_bytes, 0, 0));
+                row_s1[item] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                    ra, v1 ? (uint32_t)(r1 * p.row_bytes) : act_bytes, 0, 0));
+            }
+        }
+    };
+    if (!kInq) load_act();
 
 #pragma unroll
     for (int q = 0; q < PD; ++q) load_w(c0 + q * grid, wb[q], wsc[q]);
 
     for (int k = threadIdx.x; k < ngl; k += blockDim.x) counters[k] = 0;
+
+    if constexpr (kInq) {
+        // row mq of x by threads lt = 0 .. qrow - 1 of its group; threads past
+        // the M groups form one-wave groups of no row (they only take part in
+        // the barriers).  The x loads were issued first (above the weights).
+        __shared__ float qred[2][kQMaxThreads / 64];
+        quantize_rows(qred);
+        __syncthreads();                           // the records are complete
+        load_act();
+    }
 
     uint4 a_codes[RT][kAC];
     uint32_t a_sc[RT][kAC];
@@ -411,15 +473,18 @@ __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmArgs p) {
     }
 }
 
-template <int FMT, int MAXS, int RT, bool COMP, int PD, bool APRE, int RM>
+template <int FMT, int MAXS, int RT, bool COMP, int PD, bool APRE, int RM, typename XT = void, int NCQ = 1>
 hipError_t launch_t(const GemmArgs& a, int KW, int64_t grid, hipStream_t s) {
-    // allow the LDS of a CU for the partial-sum slots (set once per kernel)
+    constexpr bool kInq = !std::is_void<XT>::value;
+    // allow the LDS of a CU for the partial-sum slots and, quantizing in the
+    // workgroup, the activation records (set once per kernel)
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&gemm_small_kernel<FMT, MAXS, RT, COMP, PD, APRE, RM>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, kRedBytesMax + 1024);
+        reinterpret_cast<const void*>(&gemm_small_kernel<FMT, MAXS, RT, COMP, PD, APRE, RM, XT, NCQ>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, kInq ? kLdsInq : kRedBytesMax + 1024);
     if (attr != hipSuccess) return attr;
-    const size_t lds = (size_t)((a.ngl + 63) & ~63) * 4 + (size_t)a.ngl * KW * RT * (COMP ? 512 : 1024);
-    hipLaunchKernelGGL((gemm_small_kernel<FMT, MAXS, RT, COMP, PD, APRE, RM>), dim3((unsigned)grid),
+    size_t lds = (size_t)((a.ngl + 63) & ~63) * 4 + (size_t)a.ngl * KW * RT * (COMP ? 512 : 1024);
+    if (kInq) lds += (size_t)(COMP ? 2 * a.M : a.M) * a.row_bytes;
+    hipLaunchKernelGGL((gemm_small_kernel<FMT, MAXS, RT, COMP, PD, APRE, RM, XT, NCQ>), dim3((unsigned)grid),
                        dim3(64 * KW), lds, s, a);
     return hipGetLastError();
 }
@@ -526,15 +591,79 @@ GemmPlan plan_gemm_small(int64_t M, int64_t N, int64_t S, bool comp, int num_cus
     return pl;
 }
 
+// In-workgroup quantization (bf16 x, one row tile, up to 4 steps per wave):
+// the weight prefetch and reduction as for the narrow plans, plus NCQ.
+template <int FMT, bool COMP, int MAXS, int NCQ>
+hipError_t launch_inq_v(const GemmArgs& a, int KW, int64_t grid, hipStream_t s, bool single) {
+    using XT = __hip_bfloat16;
+    if (single)
+        return launch_t<FMT, MAXS, 1, COMP, 1, apre_for(FMT, 1, MAXS, true, COMP), rm_for(FMT, 1, MAXS, true), XT,
+                        NCQ>(a, KW, grid, s);
+    return launch_t<FMT, MAXS, 1, COMP, 1, apre_for(FMT, 1, MAXS, false, COMP), rm_for(FMT, 1, MAXS, false), XT,
+                    NCQ>(a, KW, grid, s);
+}
+
+template <int FMT, bool COMP>
+hipError_t launch_inq_fmt(const GemmArgs& a, int maxs, int ncq, int KW, int64_t grid, hipStream_t s, bool single) {
+    if (ncq <= 2) {
+        switch (maxs) {
+            case 1: return launch_inq_v<FMT, COMP, 1, 2>(a, KW, grid, s, single);
+            case 2: return launch_inq_v<FMT, COMP, 2, 2>(a, KW, grid, s, single);
+            default: return launch_inq_v<FMT, COMP, 4, 2>(a, KW, grid, s, single);
+        }
+    }
+    switch (maxs) {
+        case 1: return launch_inq_v<FMT, COMP, 1, 4>(a, KW, grid, s, single);
+        case 2: return launch_inq_v<FMT, COMP, 2, 4>(a, KW, grid, s, single);
+        default: return launch_inq_v<FMT, COMP, 4, 4>(a, KW, grid, s, single);
+    }
+}
+
 hipError_t launch_gemm_small(int fmt, const GemmPlan& pl, bool comp, const void* act,
                              int64_t row_bytes, const void* blob, int M, int64_t N, int64_t K,
                              void* y, bool out_bf16, int s_lo, int s_hi, bool accum, hipStream_t s) {
     const int64_t k_hi = (int64_t)s_hi * kStepK < K ? (int64_t)s_hi * kStepK : K;
     GemmArgs a{static_cast<const uint8_t*>(act), row_bytes, static_cast<const uint8_t*>(blob), M,
-               N, K, y, pl.ngl, s_lo, k_hi, accum ? 1 : 0, out_bf16 ? 1 : 0};
+               N, K, y, pl.ngl, s_lo, k_hi, accum ? 1 : 0, out_bf16 ? 1 : 0, nullptr, 64};
     const bool single = num_groups(N) <= pl.grid;             // one group per workgroup
     if (fmt == kNV) return launch_fmt<kNV>(a, pl.rt, comp, pl.maxs, pl.kw, pl.grid, s, single);
     return launch_fmt<kMX>(a, pl.rt, comp, pl.maxs, pl.kw, pl.grid, s, single);
+}
+
+InqPlan plan_gemm_inq(int fmt, int64_t M, int64_t N, int64_t K, bool comp, int num_cus) {
+    InqPlan q;
+    if (fmt == kNV && comp) return q;                    // not instantiated (the two launches are faster)
+    const int64_t S = num_steps(K);
+    const int64_t B = comp ? 2 * M : M;
+    if (B > 16 || S > 64) return q;                      // one row tile, up to 4 steps per wave
+    q.pl = plan_gemm_small(M, N, S, comp, num_cus);
+    if (q.pl.rt != 1 || q.pl.maxs > 4) return q;
+    q.qrow = (int)((64 * q.pl.kw / M) / 64 * 64);        // threads per row, whole waves
+    if (q.qrow < 64) return q;
+    const int64_t ncq = (K + 8 * q.qrow - 1) / (8 * q.qrow);
+    if (ncq > 4) return q;
+    q.ncq = ncq <= 2 ? 2 : 4;
+    const int64_t rec = B * act_row_bytes(fmt, K);
+    const int64_t per_group = (int64_t)q.pl.kw * (comp ? 512 : 1024);
+    const int64_t fit = (kLdsInq - 256 - rec) / per_group;
+    if (fit < 1) return q;
+    if (q.pl.ngl > fit) q.pl.ngl = (int)fit;
+    if (q.pl.ngl > 64) q.pl.ngl = 64;                   // counters within their 256 bytes
+    q.ok = true;
+    return q;
+}
+
+hipError_t launch_gemm_inq(int fmt, const InqPlan& q, bool comp, const void* x, const void* blob, int M, int64_t N,
+                           int64_t K, void* y, bool out_bf16, hipStream_t s) {
+    GemmArgs a{nullptr, act_row_bytes(fmt, K), static_cast<const uint8_t*>(blob), M, N, K, y, q.pl.ngl, 0, K, 0,
+               out_bf16 ? 1 : 0, x, q.qrow};
+    const bool single = num_groups(N) <= q.pl.grid;
+    if (fmt == kNV) {   // compensated NVFP4 always takes the two-launch path
+        if (comp) return hipErrorInvalidValue;
+        return launch_inq_fmt<kNV, false>(a, q.pl.maxs, q.ncq, q.pl.kw, q.pl.grid, s, single);
+    }
+    return comp ? launch_inq_fmt<kMX, true>(a, q.pl.maxs, q.ncq, q.pl.kw, q.pl.grid, s, single)
+                : launch_inq_fmt<kMX, false>(a, q.pl.maxs, q.ncq, q.pl.kw, q.pl.grid, s, single);
 }
 
 }  // namespace rsfp4

@@ -53,6 +53,18 @@ hipError_t launch_gemm_small(int fmt, const GemmPlan& pl, bool comp, const void*
                              int64_t row_bytes, const void* blob, int M, int64_t N, int64_t K,
                              void* y, bool out_bf16, int s_lo, int s_hi, bool accum, hipStream_t s);
 
+// Narrow linear that quantizes its own activation rows (bf16 x[M, K]) in every
+// workgroup, into LDS records (the quantize kernel's bytes), in one launch.
+struct InqPlan {
+    bool ok = false;   // the shape fits this kernel
+    GemmPlan pl;
+    int qrow = 64;     // threads per quantized row
+    int ncq = 2;       // chunks of 8 elements per thread
+};
+InqPlan plan_gemm_inq(int fmt, int64_t M, int64_t N, int64_t K, bool comp, int num_cus);
+hipError_t launch_gemm_inq(int fmt, const InqPlan& q, bool comp, const void* x, const void* blob, int M, int64_t N,
+                           int64_t K, void* y, bool out_bf16, hipStream_t s);
+
 // Wide-operand linear (any number of activation rows): 2-D tiles of 128 rows x
 // 128 channels per workgroup, each wave walking all of K.
 hipError_t launch_gemm_tile(int fmt, bool comp, const void* act, int64_t row_bytes, const void* blob,

@@ -190,6 +190,44 @@ rsfp4_status rsfp4_mxfp4_linear_compensated_bf16(const void* act, size_t act_byt
                                                  size_t w_packed_bytes, int64_t M, int64_t N, int64_t K,
                                                  void* y, void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------ one call from x (quantize + linear) --
+ * y = the linear of x[M,K] (dtype xt, row-major, 16-byte aligned) in one call:
+ * the activation quantizer of rsfp4_*_quantize_act_with_residue (with the
+ * residue for the *_compensated calls) followed by the linear, y [M, N] stored
+ * as fp32 (yt = RSFP4_F32) or bf16 (yt = RSFP4_BF16).  The sums are the ones of
+ * the two calls made in turn, bit for bit.  The page fuses residue generation
+ * into the quantizer, which emits the GEMM's operand layout (ResServe Section
+ * 4.4), and counts an extra kernel launch as a cost (Section 4.1); this call
+ * goes one step further for decode: with bf16 x, K <= 8192 and few rows to
+ * quantize (MXFP4: M <= 4; NVFP4: M <= 4 plain; compensated NVFP4, whose
+ * quantization is twice as long, always takes two launches), it is
+ * ONE launch of the narrow linear in which every workgroup quantizes the M
+ * rows itself into LDS (the same record bytes the quantizer writes, with the
+ * quantizer's arithmetic) while its weight loads are in flight, and reads its
+ * fragments from there; no workgroup waits for another and nothing goes
+ * through HBM but x, the weights and y.  Other shapes and fp32 x run the
+ * quantize and linear kernels back to back through act (with more rows the
+ * quantizer, spread over M compute units, is the faster of the two).
+ * act: rsfp4_packed_act_bytes(fmt, M, K, compensated) bytes of device memory,
+ * 16-byte aligned, owned by the caller; holds the quantized rows after a
+ * two-launch call and is left untouched by a one-launch call.  Argument checks
+ * as for the two calls. */
+/* Kernel launches such a call makes on the current device: 1 or 2 (0 for
+ * arguments the calls reject). */
+int rsfp4_from_x_launches(int fmt, int xt, int64_t M, int64_t N, int64_t K, int compensated);
+rsfp4_status rsfp4_nvfp4_linear_from_x(const void* x, int xt, int64_t M, int64_t N, int64_t K,
+                                       const void* w_packed, size_t w_packed_bytes, void* y, int yt,
+                                       void* act, size_t act_bytes, void* stream);
+rsfp4_status rsfp4_nvfp4_linear_compensated_from_x(const void* x, int xt, int64_t M, int64_t N, int64_t K,
+                                                   const void* w_packed, size_t w_packed_bytes, void* y,
+                                                   int yt, void* act, size_t act_bytes, void* stream);
+rsfp4_status rsfp4_mxfp4_linear_from_x(const void* x, int xt, int64_t M, int64_t N, int64_t K,
+                                       const void* w_packed, size_t w_packed_bytes, void* y, int yt,
+                                       void* act, size_t act_bytes, void* stream);
+rsfp4_status rsfp4_mxfp4_linear_compensated_from_x(const void* x, int xt, int64_t M, int64_t N, int64_t K,
+                                                   const void* w_packed, size_t w_packed_bytes, void* y,
+                                                   int yt, void* act, size_t act_bytes, void* stream);
+
 /* ------------------------------- paper numerics: given tensor scale (NVFP4) --
  * The operator as the ResServe page's fused quantizer computes it (Appendix
  * B.2: Eq. 8 and the pack8 description; Algorithm 1), in place of the per-row
