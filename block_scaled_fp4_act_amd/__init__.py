@@ -374,6 +374,15 @@ def mxfp4_quantize_act_kext(x, masks, k, out=None):
 
 # ------------------------------------------------------------ test/debug --
 
+def validate_packed(w_packed):
+    """(fmt, N, K) from a packed weight blob's header after checking it;
+    raises RuntimeError on a bad header (synchronizes the current stream)."""
+    f, n, k = ctypes.c_int(0), ctypes.c_int64(0), ctypes.c_int64(0)
+    _check(lib().rsfp4_validate_packed(_ptr(w_packed), w_packed.numel(), ctypes.byref(f), ctypes.byref(n),
+                                       ctypes.byref(k), _stream(w_packed)))
+    return f.value, n.value, k.value
+
+
 def unpack_weights_canonical(w_packed, fmt, N, K):
     """Canonical codes [N, K/2], scales [N, K/blk] and the NVFP4 tensor scale."""
     import torch

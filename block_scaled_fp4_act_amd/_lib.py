@@ -30,6 +30,7 @@ SIGNATURES = {
     "rsfp4_mxfp4_linear": (INT, [P, SZ, P, SZ, I64, I64, I64, P, P, SZ, P]),
     "rsfp4_mxfp4_linear_compensated": (INT, [P, SZ, P, SZ, I64, I64, I64, P, P, SZ, P]),
     "rsfp4_unpack_weights_canonical": (INT, [P, SZ, INT, I64, I64, P, P, P, P]),
+    "rsfp4_validate_packed": (INT, [P, SZ, P, P, P, P]),
     "rsfp4_nvfp4_linear_bf16": (INT, [P, SZ, P, SZ, I64, I64, I64, P, P, SZ, P]),
     "rsfp4_nvfp4_linear_compensated_bf16": (INT, [P, SZ, P, SZ, I64, I64, I64, P, P, SZ, P]),
     "rsfp4_mxfp4_linear_bf16": (INT, [P, SZ, P, SZ, I64, I64, I64, P, P, SZ, P]),

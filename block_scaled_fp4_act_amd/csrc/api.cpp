@@ -432,6 +432,35 @@ rsfp4_status rsfp4_unpack_weights_canonical(const void* w_packed, size_t w_packe
     return hip_status(launch_unpack(fmt, w_packed, N, K, codes, scales, s_g, (hipStream_t)stream), "unpack launch");
 }
 
+rsfp4_status rsfp4_validate_packed(const void* w_packed, size_t w_packed_bytes, int* fmt, int64_t* N, int64_t* K,
+                                   void* stream) {
+    g_err[0] = 0;
+    if (!w_packed) return fail(RSFP4_ERR_NULL, "w_packed must be non-NULL");
+    if (!aligned(w_packed, 256)) return fail(RSFP4_ERR_ALIGN, "w_packed must be 256-byte aligned");
+    if (w_packed_bytes < (size_t)kWHeader)
+        return fail(RSFP4_ERR_BUFFER_TOO_SMALL, "w_packed holds %zu bytes, the header alone is %lld", w_packed_bytes,
+                    (long long)kWHeader);
+    WHeader h;
+    hipError_t e = hipMemcpyAsync(&h, w_packed, sizeof h, hipMemcpyDeviceToHost, (hipStream_t)stream);
+    if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e, "header copy");
+    if (h.magic != kMagic) return fail(RSFP4_ERR_FORMAT, "not a packed weight blob (magic 0x%08x)", h.magic);
+    if (h.abi_version != RSFP4_ABI_VERSION)
+        return fail(RSFP4_ERR_FORMAT, "blob of ABI version %u, this library is %d", h.abi_version, RSFP4_ABI_VERSION);
+    if (h.fmt != RSFP4_NVFP4 && h.fmt != RSFP4_MXFP4) return fail(RSFP4_ERR_FORMAT, "unknown format %u", h.fmt);
+    if (check_common((int)h.fmt, h.K) != RSFP4_OK) return fail(RSFP4_ERR_FORMAT, "header K = %lld", (long long)h.K);
+    if (h.N < 1 || h.N > (int64_t)1 << 24) return fail(RSFP4_ERR_FORMAT, "header N = %lld", (long long)h.N);
+    const bool sg_ok = h.fmt == RSFP4_NVFP4 ? (h.s_g >= 0.0f && h.s_g < __builtin_inff()) : h.s_g == 0.0f;
+    if (!sg_ok) return fail(RSFP4_ERR_FORMAT, "header tensor scale %g", (double)h.s_g);
+    const size_t need = (size_t)packed_weight_bytes((int)h.fmt, h.N, h.K);
+    if (w_packed_bytes < need)
+        return fail(RSFP4_ERR_BUFFER_TOO_SMALL, "w_packed holds %zu bytes, its header needs %zu", w_packed_bytes, need);
+    if (fmt) *fmt = (int)h.fmt;
+    if (N) *N = h.N;
+    if (K) *K = h.K;
+    return RSFP4_OK;
+}
+
 int64_t rsfp4_kext_dim(int64_t K, int k) { return kext_dim(K, k); }
 
 rsfp4_status rsfp4_channel_abs_sum(const void* x, int xt, int64_t T, int64_t K, double* sum, int accumulate,

@@ -392,6 +392,16 @@ rsfp4_status rsfp4_unpack_weights_canonical(const void* w_packed, size_t w_packe
                                             int64_t N, int64_t K, uint8_t* codes, uint8_t* scales,
                                             float* s_g, void* stream);
 
+/* Test/debug: check a packed weight blob's 256-byte header against the rules
+ * of the layout above (magic, ABI version, format, N and K in range, tensor
+ * scale finite and non-negative for NVFP4 and zero for MXFP4, w_packed_bytes
+ * at least the size query for the header's format, N, K) and report the
+ * header's format, N and K (each output may be NULL).  Copies the header to
+ * the host on `stream` and SYNCHRONIZES that stream.  A bad header returns
+ * RSFP4_ERR_FORMAT, a short buffer RSFP4_ERR_BUFFER_TOO_SMALL. */
+rsfp4_status rsfp4_validate_packed(const void* w_packed, size_t w_packed_bytes, int* fmt, int64_t* N, int64_t* K,
+                                   void* stream);
+
 #ifdef __cplusplus
 }
 #endif

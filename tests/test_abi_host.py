@@ -157,3 +157,12 @@ def test_from_x_validation():
     assert L.rsfp4_mxfp4_linear_from_x(FAKE, 1, 2, 16, 32800, FAKE, 1 << 30, FAKE, 0, FAKE, 1 << 30, None) == 2
     assert L.rsfp4_mxfp4_linear_from_x(FAKE, 1, 0, 16, 512, FAKE, 1 << 30, FAKE, 0, FAKE, 1 << 30, None) == 2
     assert L.rsfp4_mxfp4_linear_from_x(FAKE, 1, 2, 16, 100, FAKE, 1 << 30, FAKE, 0, FAKE, 1 << 30, None) == 2
+
+
+def test_validate_packed_host_checks():
+    """rsfp4_validate_packed: the checks made before the header is read."""
+    L = rs.lib()
+    assert L.rsfp4_validate_packed(None, 1 << 20, None, None, None, None) == 1
+    assert L.rsfp4_validate_packed(ctypes.c_void_p(0x100010), 1 << 20, None, None, None, None) == 3
+    assert L.rsfp4_validate_packed(FAKE, 255, None, None, None, None) == 5
+    assert "header" in _err()

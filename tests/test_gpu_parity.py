@@ -305,3 +305,24 @@ def test_linear_limits_rejected():
         rs.fp4_linear_compensated(act[:100], blob, 1, 64, 512, 0)
     with pytest.raises(RuntimeError, match="too small"):
         rs.fp4_linear_compensated(act, blob, 18, 64, 512, 0)
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_validate_packed(fmt):
+    """A prepacked blob's header reads back its format, N and K; a corrupted
+    magic, a short buffer and a wrong tensor scale are rejected."""
+    import torch
+    rs = _rs()
+    N, K = 48, 160
+    blob = rs.prepack_weights(torch.from_numpy(inputs.weights(N, K, 3)).cuda(), fmt)
+    assert rs.validate_packed(blob) == (fmt, N, K)
+    with pytest.raises(RuntimeError, match="buffer too small"):
+        rs.validate_packed(blob[: rs.packed_weight_bytes(fmt, N, K) - 16])
+    bad = blob.clone()
+    bad[0] ^= 0xFF
+    with pytest.raises(RuntimeError, match="unknown format or dtype"):
+        rs.validate_packed(bad)
+    bad = blob.clone()
+    bad[32:36] = torch.tensor([0, 0, 0x80, 0xFF], dtype=torch.uint8)   # s_g = -inf
+    with pytest.raises(RuntimeError, match="unknown format or dtype"):
+        rs.validate_packed(bad)
