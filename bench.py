@@ -16,7 +16,8 @@ roofline of the dominant kernel, the oracle timed on the host cores, a sweep
 over the other decode workloads, selective compensation (K-Ext) at
 rho = 0.125 / 0.25 / 0.5 on the prefill-sized operands beside their plain and
 full-residue steps, and compensated decode attention (ResAttn) over the paged
-NVFP4 KV cache at decode shapes of the page's Figure 10.
+NVFP4 KV cache at decode shapes of the page's Figure 10, and the grouped
+(mixture of experts) linear beside one linear launch per expert.
 """
 import argparse
 import hashlib
@@ -212,6 +213,52 @@ ATTN_CASES = [  # (name, H_q, H_kv, D, B, L): decode shapes of the page's Figure
     ("D128_GQA8", 64, 8, 128, 8, 8192), ("D128_GQA8", 64, 8, 128, 8, 32768), ("D128_GQA8", 64, 8, 128, 32, 8192),
     ("D128_GQA4", 32, 8, 128, 8, 32768), ("D256_GQA6", 24, 4, 256, 8, 32768),
 ]
+
+
+GROUPED_CASES = [  # (format, experts, rows per expert, N, K): synthetic mixture-of-experts decode
+    (0, 8, 2, 2048, 4096), (1, 8, 2, 2048, 4096), (0, 16, 1, 2048, 4096),
+]
+
+
+def run_grouped(rs, torch, case, steps, warmup):
+    """Grouped (mixture of experts) compensated linear: E experts' stacked
+    weights (N(0, 0.02^2), rotated over >= 512 MB so each step streams them
+    from HBM), rows per expert of one quantized activation buffer; one launch
+    beside E ordinary linear launches on the same data."""
+    fmt, E, rows, N, K = case
+    M_total = E * rows
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    blobs = [rs.prepack_weights(torch.randn((N, K), generator=gen, device="cuda") * 0.02, fmt) for _ in range(E)]
+    stacked = torch.cat(blobs)
+    del blobs
+    R = max(2, int(math.ceil(ROTATE_BYTES / stacked.numel())))
+    stacks = [stacked] + [stacked.clone() for _ in range(R - 1)]
+    stride = rs.packed_weight_bytes(fmt, N, K)
+    x = (torch.randn((M_total, K), generator=gen, device="cuda")).to(torch.bfloat16)
+    act = rs.quantize_act_with_residue(x, fmt, True)
+    acts_e = [rs.quantize_act_with_residue(x[e * rows:(e + 1) * rows].contiguous(), fmt, True) for e in range(E)]
+    offs = torch.arange(0, M_total + 1, rows, dtype=torch.int32, device="cuda")
+    y = torch.zeros((M_total, N), dtype=torch.float32, device="cuda")
+    ys = [y[e * rows:(e + 1) * rows] for e in range(E)]
+    f = rs.fp4_linear_compensated
+
+    def grouped(i):
+        rs.fp4_grouped_linear(act, stacks[i % R], M_total, E, offs, rows, N, K, fmt, True, out=y)
+
+    def separate(i):
+        st = stacks[i % R]
+        for e in range(E):
+            f(acts_e[e], st[e * stride:(e + 1) * stride], rows, N, K, fmt, out=ys[e])
+
+    t_g = time_graph(torch, grouped, steps, warmup)
+    t_s = time_graph(torch, separate, steps, warmup)
+    wbytes = E * (stride - 256)
+    del stacks, stacked
+    torch.cuda.empty_cache()
+    return {"format": "nvfp4" if fmt == 0 else "mxfp4", "experts": E, "rows_per_expert": rows, "N": N, "K": K,
+            "grouped_us": round(t_g * 1e3, 3), "separate_launches_us": round(t_s * 1e3, 3),
+            "weights_GBps": round(wbytes / (t_g * 1e-3) / 1e9, 1),
+            "weights_hbm_frac": round(wbytes / (t_g * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def attn_kv_bytes(B, L, H_kv, D):
@@ -450,6 +497,12 @@ def main():
                  "large_mlp": inputs.LARGE_MLP, "mx": inputs.MX, "small": inputs.SMALL}
         for item in args.cases.split(","):
             parts = item.split(":")
+            if parts[0] == "grouped":   # grouped:<index into GROUPED_CASES> or grouped:all
+                idx = range(len(GROUPED_CASES)) if parts[1] == "all" else [int(parts[1])]
+                for ci in idx:
+                    print(json.dumps(run_grouped(rs, torch, GROUPED_CASES[ci], min(args.steps, 100),
+                                                 min(args.warmup, 10))), flush=True)
+                continue
             if parts[0] == "resattn":   # resattn:<index into ATTN_CASES> or resattn:all
                 idx = range(len(ATTN_CASES)) if parts[1] == "all" else [int(parts[1])]
                 for ci in idx:
@@ -500,7 +553,7 @@ def main():
                 "kernel": "gemm_small_kernel (compensated NVFP4 linear)",
                 "algorithmic_bytes_per_launch": gb}
 
-    sweep = []
+    sweep, grouped = [], []
     if not args.no_sweep and not args.only_headline:
         cases = [(inputs.MLP_UP, 8), (inputs.MLP_DOWN, 8)]
         cases += [(inputs.LARGE_MLP, m) for m in inputs.LARGE_MLP_M]
@@ -511,6 +564,7 @@ def main():
             torch.cuda.empty_cache()
             sweep.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()})
         attn = [run_attn(rs, torch, c, min(args.steps, 50), min(args.warmup, 5)) for c in ATTN_CASES]
+        grouped = [run_grouped(rs, torch, c, min(args.steps, 100), min(args.warmup, 10)) for c in GROUPED_CASES]
         # selective compensation (prefill-sized operands): rho = 0.125, 0.25, 0.5
         kext = []
         for w, m in ((inputs.LARGE_MLP, 128), (inputs.MX, 256)):
@@ -556,6 +610,7 @@ def main():
         line["sweep"] = sweep
         line["kext"] = kext
         line["attention"] = attn
+        line["grouped"] = grouped
     print(json.dumps(line), flush=True)
 
 

@@ -188,6 +188,25 @@ def mxfp4_linear_compensated(act, w_packed, M, N, K, out=None):
     return _linear(act, w_packed, M, N, K, MXFP4, True, out)
 
 
+# ------------------------------------ grouped linear (mixture of experts) --
+
+def fp4_grouped_linear(act, w_packed, M_total, E, offsets, max_rows, N, K, fmt, compensated=True, out=None):
+    """Expert e: rows offsets[e] .. offsets[e+1]-1 of act (M_total quantized
+    rows, with residue rows when compensated) times the e-th of E stacked
+    blobs in w_packed -> the same rows of y [M_total, N] (fp32).  offsets:
+    int32 cuda tensor [E + 1]; max_rows bounds every expert's rows."""
+    import torch
+    fmt = _fmt(fmt)
+    assert offsets.is_cuda and offsets.dtype == torch.int32 and offsets.numel() >= E + 1
+    if out is None:
+        out = torch.zeros((M_total, N), dtype=torch.float32, device=act.device)
+    assert out.is_cuda and out.dtype == torch.float32 and out.is_contiguous() and out.numel() >= M_total * N
+    name = f"rsfp4_{_FMT_NAME[fmt]}_grouped_linear" + ("_compensated" if compensated else "")
+    _check(getattr(lib(), name)(_ptr(act), act.numel(), M_total, _ptr(w_packed), w_packed.numel(), E, _ptr(offsets),
+                                max_rows, N, K, _ptr(out), _stream(act)))
+    return out
+
+
 # ------------------------------------------- quantize + linear in one call --
 
 def from_x_launches(fmt, M, N, K, compensated=True, x_dtype=None):

@@ -36,6 +36,10 @@ SIGNATURES = {
     "rsfp4_mxfp4_linear_bf16": (INT, [P, SZ, P, SZ, I64, I64, I64, P, P, SZ, P]),
     "rsfp4_mxfp4_linear_compensated_bf16": (INT, [P, SZ, P, SZ, I64, I64, I64, P, P, SZ, P]),
     "rsfp4_from_x_launches": (INT, [INT, INT, I64, I64, I64, INT]),
+    "rsfp4_nvfp4_grouped_linear": (INT, [P, SZ, I64, P, SZ, I64, P, I64, I64, I64, P, P]),
+    "rsfp4_nvfp4_grouped_linear_compensated": (INT, [P, SZ, I64, P, SZ, I64, P, I64, I64, I64, P, P]),
+    "rsfp4_mxfp4_grouped_linear": (INT, [P, SZ, I64, P, SZ, I64, P, I64, I64, I64, P, P]),
+    "rsfp4_mxfp4_grouped_linear_compensated": (INT, [P, SZ, I64, P, SZ, I64, P, I64, I64, I64, P, P]),
     "rsfp4_nvfp4_linear_from_x": (INT, [P, INT, I64, I64, I64, P, SZ, P, INT, P, SZ, P]),
     "rsfp4_nvfp4_linear_compensated_from_x": (INT, [P, INT, I64, I64, I64, P, SZ, P, INT, P, SZ, P]),
     "rsfp4_mxfp4_linear_from_x": (INT, [P, INT, I64, I64, I64, P, SZ, P, INT, P, SZ, P]),

@@ -166,6 +166,47 @@ rsfp4_status linear(int fmt, bool comp, const void* act, size_t act_bytes, const
     return RSFP4_OK;
 }
 
+// ---- grouped (mixture of experts) linear ----
+rsfp4_status grouped_linear(int fmt, bool comp, const void* act, size_t act_bytes, int64_t M_total,
+                            const void* w_packed, size_t w_bytes, int64_t E, const int32_t* offsets,
+                            int64_t max_rows, int64_t N, int64_t K, float* y, void* stream) {
+    g_err[0] = 0;
+    rsfp4_status st = check_common(fmt, K);
+    if (st != RSFP4_OK) return st;
+    if (!act || !w_packed || !offsets || !y) return fail(RSFP4_ERR_NULL, "act, w_packed, offsets and y must be non-NULL");
+    if (M_total < 1 || M_total > 65535) return fail(RSFP4_ERR_SHAPE, "M_total = %lld outside [1, 65535]", (long long)M_total);
+    if (E < 1 || E > 65535) return fail(RSFP4_ERR_SHAPE, "E = %lld outside [1, 65535]", (long long)E);
+    if (max_rows < 1 || max_rows > M_total)
+        return fail(RSFP4_ERR_SHAPE, "max_rows = %lld outside [1, M_total]", (long long)max_rows);
+    if (N < 1 || N > (int64_t)1 << 24) return fail(RSFP4_ERR_SHAPE, "N = %lld outside [1, 2^24]", (long long)N);
+    const int64_t B = comp ? 2 * max_rows : max_rows;
+    if (B > kNarrowRows)
+        return fail(RSFP4_ERR_UNSUPPORTED, "grouped linear: %lld operand rows per expert, at most %lld", (long long)B,
+                    (long long)kNarrowRows);
+    if (K > kMaxNarrowK)
+        return fail(RSFP4_ERR_UNSUPPORTED, "grouped linear: K = %lld, at most %lld", (long long)K, (long long)kMaxNarrowK);
+    if (!aligned(act, 16) || !aligned(w_packed, 256) || !aligned(offsets, 4) || !aligned(y, 4))
+        return fail(RSFP4_ERR_ALIGN, "act 16-, w_packed 256-byte, offsets and y element aligned");
+    const int64_t rb = act_row_bytes(fmt, K);
+    const int64_t rows = comp ? 2 * M_total : M_total;
+    if (rb * rows >= ((int64_t)1 << 31))
+        return fail(RSFP4_ERR_UNSUPPORTED, "activation buffer of %lld bytes: needs < 2^31", (long long)(rb * rows));
+    if (act_bytes < (size_t)(rb * rows))
+        return fail(RSFP4_ERR_BUFFER_TOO_SMALL, "act holds %zu bytes, needs %zu", act_bytes, (size_t)(rb * rows));
+    const int64_t stride = packed_weight_bytes(fmt, N, K);
+    if (w_bytes / (size_t)stride < (size_t)E)
+        return fail(RSFP4_ERR_BUFFER_TOO_SMALL, "w_packed holds %zu bytes, %lld blobs need %zu", w_bytes, (long long)E,
+                    (size_t)(stride * E));
+    int cus = 0;
+    st = num_cus(&cus);
+    if (st != RSFP4_OK) return st;
+    const int per_expert_cus = cus / E > 0 ? (int)(cus / E) : 1;
+    const GemmPlan pl = plan_gemm_small(max_rows, N, num_steps(K), comp, per_expert_cus);
+    return hip_status(launch_gemm_grouped(fmt, pl, comp, act, rb, (int)M_total, w_packed, stride, (int)E, offsets,
+                                          (int)max_rows, N, K, y, (hipStream_t)stream),
+                      "grouped linear launch");
+}
+
 // ---- quantize + linear from x in one call ----
 bool from_x_one_launch(int fmt, bool comp, int64_t M) {
     return fmt == RSFP4_MXFP4 ? M <= 4 : (!comp && M <= 4);
@@ -344,6 +385,19 @@ size_t rsfp4_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, int compe
     (void)fmt; (void)M; (void)N; (void)K; (void)compensated;
     return 0;
 }
+
+#define RSFP4_GROUPED(NAME, FMT, COMP)                                                                         \
+    rsfp4_status NAME(const void* act, size_t act_bytes, int64_t M_total, const void* w_packed,              \
+                      size_t w_packed_bytes, int64_t E, const int32_t* offsets, int64_t max_rows, int64_t N,  \
+                      int64_t K, float* y, void* stream) {                                                    \
+        return grouped_linear(FMT, COMP, act, act_bytes, M_total, w_packed, w_packed_bytes, E, offsets,      \
+                              max_rows, N, K, y, stream);                                                     \
+    }
+RSFP4_GROUPED(rsfp4_nvfp4_grouped_linear, RSFP4_NVFP4, false)
+RSFP4_GROUPED(rsfp4_nvfp4_grouped_linear_compensated, RSFP4_NVFP4, true)
+RSFP4_GROUPED(rsfp4_mxfp4_grouped_linear, RSFP4_MXFP4, false)
+RSFP4_GROUPED(rsfp4_mxfp4_grouped_linear_compensated, RSFP4_MXFP4, true)
+#undef RSFP4_GROUPED
 
 int rsfp4_from_x_launches(int fmt, int xt, int64_t M, int64_t N, int64_t K, int compensated) {
     g_err[0] = 0;

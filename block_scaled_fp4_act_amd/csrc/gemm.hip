@@ -115,6 +115,14 @@ struct GemmArgs {
     int out_bf16;     // store y as bf16 (round to nearest even)
     const void* x;    // in-workgroup quantization: the input rows x[M, K]
     int qrow;         // threads per quantized row (a multiple of 64)
+    // grouped (mixture of experts), offsets non-null: blockIdx.y is the expert
+    // e, its rows offsets[e] .. offsets[e+1] of the act buffer (of M_total rows;
+    // at most M of them are computed) and its blob the e-th of the stacked
+    // blobs, blob_stride bytes apart
+    const int32_t* offsets;
+    int64_t blob_stride;
+    int M_total;
+    int E;
 };
 
 // APRE: the activation fragments are dequantized to f16 once, before the
@@ -168,8 +176,21 @@ __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmArgs p) {
     // in-workgroup quantization: the B activation records after the partials
     uint8_t* act_lds = reinterpret_cast<uint8_t*>(red + ngl * KW * RT * PW * 64);
 
+    // this workgroup's rows: mb .. mb + Mr - 1 of an act buffer of Mt rows
+    int mb = 0, Mr = p.M, Mt = p.M;
+    const uint8_t* blob = p.blob;
+    if (p.offsets) {
+        const int e = blockIdx.y;
+        Mt = p.M_total;
+        const int lo = min(max(p.offsets[e], 0), Mt);
+        const int hi = min(max(p.offsets[e + 1], lo), Mt);
+        mb = lo;
+        Mr = min(hi - lo, p.M);
+        blob += (int64_t)e * p.blob_stride;
+    }
+
     float s_gw = 1.0f;
-    if (FMT == kNV) s_gw = reinterpret_cast<const WHeader*>(p.blob)->s_g;
+    if (FMT == kNV) s_gw = reinterpret_cast<const WHeader*>(blob)->s_g;
 
     // Offsets of this wave's loads inside a group: steps past the padded end
     // of the group land past its last byte, i.e. out of range (zeros).
@@ -191,7 +212,7 @@ __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmArgs p) {
     auto load_w = [&](int64_t c, uint4 (&codes)[MAXS], SW& sc) {
         const bool live = c < G;
         const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(p.blob + kWHeader + (live ? c : 0) * GB), (short)0, live ? (int)GB : 0, kRsrcWord3);
+            (void*)(blob + kWHeader + (live ? c : 0) * GB), (short)0, live ? (int)GB : 0, kRsrcWord3);
 #pragma unroll
         for (int t = 0; t < MAXS; ++t)
             codes[t] = ld128(r, code_base + (uint32_t)((t / 4) * quad_bytes(FMT) + (t % 4) * kStepCodes));
@@ -217,7 +238,7 @@ __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmArgs p) {
     // Their loads go out first; the first groups' weight loads follow at once,
     // so both latencies overlap and the fragments can be dequantized while the
     // weights are still in flight.
-    const int B = COMP ? 2 * p.M : p.M;
+    const int B = COMP ? 2 * Mt : Mt;
     const uint32_t act_bytes = (uint32_t)(B * p.row_bytes);
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
         (void*)p.act, (short)0, (int)act_bytes, kRsrcWord3);
@@ -232,11 +253,11 @@ __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmArgs p) {
             bool rvalid;
             if (COMP) {
                 const int m = ti >> 1;
-                rvalid = m < p.M;
-                arow = (ti & 1) ? p.M + m : m;
+                rvalid = m < Mr;
+                arow = (ti & 1) ? Mt + mb + m : mb + m;
             } else {
-                rvalid = ti < p.M;
-                arow = ti;
+                rvalid = ti < Mr;
+                arow = mb + ti;
             }
 #pragma unroll
             for (int t = 0; t < MAXS; ++t) {
@@ -269,10 +290,10 @@ __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmArgs p) {
             row_s0[item] = row_s1[item] = 0.0f;
             if (FMT == kNV) {
                 const int ti0 = 16 * (item >> 1) + 4 * g + 2 * (item & 1);
-                const int r0 = COMP ? ti0 >> 1 : ti0;
-                const int r1 = COMP ? p.M + (ti0 >> 1) : ti0 + 1;
-                const bool v0 = COMP ? (ti0 >> 1) < p.M : r0 < p.M;
-                const bool v1 = COMP ? v0 : r1 < p.M;
+                const int r0 = mb + (COMP ? ti0 >> 1 : ti0);
+                const int r1 = COMP ? Mt + mb + (ti0 >> 1) : mb + ti0 + 1;
+                const bool v0 = COMP ? (ti0 >> 1) < Mr : ti0 < Mr;
+                const bool v1 = COMP ? v0 : ti0 + 1 < Mr;
                 if (kInq) {
                     row_s0[item] = v0 ? *reinterpret_cast<const float*>(act_lds + r0 * p.row_bytes) : 0.0f;
                     row_s1[item] = v1 ? *reinterpret_cast<const float*>(act_lds + r1 * p.row_bytes) : 0.0f;
@@ -334,10 +355,11 @@ __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmArgs p) {
                 float v = 0.0f;
                 for (int w = 0; w < KW; ++w) v += src[w * RT * (PW * 64)];
                 const int m = ti0 >> 1;
-                if (n < p.N && m < p.M) {
+                if (n < p.N && m < Mr) {
                     float out = FMT == kNV ? s_gw * v : v;
-                    if (p.accum) out += reinterpret_cast<const float*>(p.y)[(int64_t)m * p.N + n];
-                    store_y(p.y, (int64_t)m * p.N + n, out, p.out_bf16);
+                    const int64_t yi = (int64_t)(mb + m) * p.N + n;
+                    if (p.accum) out += reinterpret_cast<const float*>(p.y)[yi];
+                    store_y(p.y, yi, out, p.out_bf16);
                 }
                 continue;
             }
@@ -351,12 +373,13 @@ __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmArgs p) {
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int m = ti0 + h;
-                    if (m < p.M) {
+                    if (m < Mr) {
                         const float v = h ? v1 : v0;
                         float out = v;
                         if (FMT == kNV) out = s_gw * ((h ? row_s1[item] : row_s0[item]) * v);
-                        if (p.accum) out += reinterpret_cast<const float*>(p.y)[(int64_t)m * p.N + n];
-                        store_y(p.y, (int64_t)m * p.N + n, out, p.out_bf16);
+                        const int64_t yi = (int64_t)(mb + m) * p.N + n;
+                        if (p.accum) out += reinterpret_cast<const float*>(p.y)[yi];
+                        store_y(p.y, yi, out, p.out_bf16);
                     }
                 }
             }
@@ -484,8 +507,8 @@ hipError_t launch_t(const GemmArgs& a, int KW, int64_t grid, hipStream_t s) {
     if (attr != hipSuccess) return attr;
     size_t lds = (size_t)((a.ngl + 63) & ~63) * 4 + (size_t)a.ngl * KW * RT * (COMP ? 512 : 1024);
     if (kInq) lds += (size_t)(COMP ? 2 * a.M : a.M) * a.row_bytes;
-    hipLaunchKernelGGL((gemm_small_kernel<FMT, MAXS, RT, COMP, PD, APRE, RM, XT, NCQ>), dim3((unsigned)grid),
-                       dim3(64 * KW), lds, s, a);
+    hipLaunchKernelGGL((gemm_small_kernel<FMT, MAXS, RT, COMP, PD, APRE, RM, XT, NCQ>),
+                       dim3((unsigned)grid, a.offsets ? (unsigned)a.E : 1u), dim3(64 * KW), lds, s, a);
     return hipGetLastError();
 }
 
@@ -624,8 +647,18 @@ hipError_t launch_gemm_small(int fmt, const GemmPlan& pl, bool comp, const void*
                              void* y, bool out_bf16, int s_lo, int s_hi, bool accum, hipStream_t s) {
     const int64_t k_hi = (int64_t)s_hi * kStepK < K ? (int64_t)s_hi * kStepK : K;
     GemmArgs a{static_cast<const uint8_t*>(act), row_bytes, static_cast<const uint8_t*>(blob), M,
-               N, K, y, pl.ngl, s_lo, k_hi, accum ? 1 : 0, out_bf16 ? 1 : 0, nullptr, 64};
+               N, K, y, pl.ngl, s_lo, k_hi, accum ? 1 : 0, out_bf16 ? 1 : 0, nullptr, 64, nullptr, 0, M, 1};
     const bool single = num_groups(N) <= pl.grid;             // one group per workgroup
+    if (fmt == kNV) return launch_fmt<kNV>(a, pl.rt, comp, pl.maxs, pl.kw, pl.grid, s, single);
+    return launch_fmt<kMX>(a, pl.rt, comp, pl.maxs, pl.kw, pl.grid, s, single);
+}
+
+hipError_t launch_gemm_grouped(int fmt, const GemmPlan& pl, bool comp, const void* act, int64_t row_bytes,
+                               int M_total, const void* blobs, int64_t blob_stride, int E, const int32_t* offsets,
+                               int max_rows, int64_t N, int64_t K, float* y, hipStream_t s) {
+    GemmArgs a{static_cast<const uint8_t*>(act), row_bytes, static_cast<const uint8_t*>(blobs), max_rows, N, K, y,
+               pl.ngl, 0, K, 0, 0, nullptr, 64, offsets, blob_stride, M_total, E};
+    const bool single = num_groups(N) <= pl.grid;
     if (fmt == kNV) return launch_fmt<kNV>(a, pl.rt, comp, pl.maxs, pl.kw, pl.grid, s, single);
     return launch_fmt<kMX>(a, pl.rt, comp, pl.maxs, pl.kw, pl.grid, s, single);
 }
@@ -656,7 +689,7 @@ InqPlan plan_gemm_inq(int fmt, int64_t M, int64_t N, int64_t K, bool comp, int n
 hipError_t launch_gemm_inq(int fmt, const InqPlan& q, bool comp, const void* x, const void* blob, int M, int64_t N,
                            int64_t K, void* y, bool out_bf16, hipStream_t s) {
     GemmArgs a{nullptr, act_row_bytes(fmt, K), static_cast<const uint8_t*>(blob), M, N, K, y, q.pl.ngl, 0, K, 0,
-               out_bf16 ? 1 : 0, x, q.qrow};
+               out_bf16 ? 1 : 0, x, q.qrow, nullptr, 0, M, 1};
     const bool single = num_groups(N) <= q.pl.grid;
     if (fmt == kNV) {   // compensated NVFP4 always takes the two-launch path
         if (comp) return hipErrorInvalidValue;

@@ -53,6 +53,15 @@ hipError_t launch_gemm_small(int fmt, const GemmPlan& pl, bool comp, const void*
                              int64_t row_bytes, const void* blob, int M, int64_t N, int64_t K,
                              void* y, bool out_bf16, int s_lo, int s_hi, bool accum, hipStream_t s);
 
+// Grouped (mixture of experts) narrow linear, one launch: expert e multiplies
+// rows offsets[e] .. offsets[e+1] (at most max_rows) of an act buffer of M_total
+// rows by the e-th of E stacked blobs (blob_stride bytes apart) into the same
+// rows of y (fp32).  Plan with plan_gemm_small(max_rows, N, steps, comp,
+// num_cus / E) so the E x grid workgroups fit the device.
+hipError_t launch_gemm_grouped(int fmt, const GemmPlan& pl, bool comp, const void* act, int64_t row_bytes,
+                               int M_total, const void* blobs, int64_t blob_stride, int E, const int32_t* offsets,
+                               int max_rows, int64_t N, int64_t K, float* y, hipStream_t s);
+
 // Narrow linear that quantizes its own activation rows (bf16 x[M, K]) in every
 // workgroup, into LDS records (the quantize kernel's bytes), in one launch.
 struct InqPlan {

@@ -190,6 +190,41 @@ rsfp4_status rsfp4_mxfp4_linear_compensated_bf16(const void* act, size_t act_byt
                                                  size_t w_packed_bytes, int64_t M, int64_t N, int64_t K,
                                                  void* y, void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------- grouped linear (mixture of experts) --
+ * E experts in one launch, the grouped GEMM the ResServe page names as future
+ * work for mixture-of-experts models (its conclusion): expert e multiplies
+ * the token rows offsets[e] .. offsets[e+1] - 1 of one activation buffer (all
+ * tokens quantized together, rows sorted by expert, as the quantize call
+ * writes them for M_total rows) by its own packed weights and writes the same
+ * rows of y [M_total, N] (fp32); each expert's result is that of the
+ * (compensated) linear on its rows alone.
+ *   w_packed: E blobs of rsfp4_packed_weight_bytes(fmt, N, K) bytes each, back
+ *             to back (each with its own header and tensor scale).
+ *   offsets:  DEVICE int32[E + 1], non-decreasing, within [0, M_total] (values
+ *             outside are clamped); read by the kernel, so a router on the GPU
+ *             can write them without a host round trip.
+ *   max_rows: a bound on every expert's row count that the caller guarantees
+ *             (it selects the kernel's row tiles): 1 <= max_rows, at most 32
+ *             operand rows (max_rows <= 32 plain, <= 16 compensated).  Rows of
+ *             an expert past max_rows, and rows of y no expert covers, are left
+ *             as they were.
+ * K <= 16384 (one narrow launch).  Each expert's channel groups take about
+ * num_CUs / E compute units. */
+rsfp4_status rsfp4_nvfp4_grouped_linear(const void* act, size_t act_bytes, int64_t M_total, const void* w_packed,
+                                        size_t w_packed_bytes, int64_t E, const int32_t* offsets, int64_t max_rows,
+                                        int64_t N, int64_t K, float* y, void* stream);
+rsfp4_status rsfp4_nvfp4_grouped_linear_compensated(const void* act, size_t act_bytes, int64_t M_total,
+                                                    const void* w_packed, size_t w_packed_bytes, int64_t E,
+                                                    const int32_t* offsets, int64_t max_rows, int64_t N, int64_t K,
+                                                    float* y, void* stream);
+rsfp4_status rsfp4_mxfp4_grouped_linear(const void* act, size_t act_bytes, int64_t M_total, const void* w_packed,
+                                        size_t w_packed_bytes, int64_t E, const int32_t* offsets, int64_t max_rows,
+                                        int64_t N, int64_t K, float* y, void* stream);
+rsfp4_status rsfp4_mxfp4_grouped_linear_compensated(const void* act, size_t act_bytes, int64_t M_total,
+                                                    const void* w_packed, size_t w_packed_bytes, int64_t E,
+                                                    const int32_t* offsets, int64_t max_rows, int64_t N, int64_t K,
+                                                    float* y, void* stream);
+
 /* ------------------------------------ one call from x (quantize + linear) --
  * y = the linear of x[M,K] (dtype xt, row-major, 16-byte aligned) in one call:
  * the activation quantizer of rsfp4_*_quantize_act_with_residue (with the

@@ -166,3 +166,20 @@ def test_validate_packed_host_checks():
     assert L.rsfp4_validate_packed(ctypes.c_void_p(0x100010), 1 << 20, None, None, None, None) == 3
     assert L.rsfp4_validate_packed(FAKE, 255, None, None, None, None) == 5
     assert "header" in _err()
+
+
+def test_grouped_validation():
+    """The grouped linear's host-side checks."""
+    L = rs.lib()
+    f = L.rsfp4_nvfp4_grouped_linear_compensated
+    big = 1 << 30
+    assert f(None, big, 8, FAKE, big, 4, FAKE, 2, 64, 512, FAKE, None) == 1
+    assert f(FAKE, big, 0, FAKE, big, 4, FAKE, 2, 64, 512, FAKE, None) == 2       # M_total
+    assert f(FAKE, big, 8, FAKE, big, 0, FAKE, 2, 64, 512, FAKE, None) == 2       # E
+    assert f(FAKE, big, 8, FAKE, big, 4, FAKE, 9, 64, 512, FAKE, None) == 2       # max_rows > M_total
+    assert f(FAKE, big, 40, FAKE, big, 4, FAKE, 17, 64, 512, FAKE, None) == 6     # 34 operand rows
+    assert f(FAKE, big, 8, FAKE, big, 4, FAKE, 2, 64, 20480, FAKE, None) == 6     # K past one launch
+    assert f(FAKE, 100, 8, FAKE, big, 4, FAKE, 2, 64, 512, FAKE, None) == 5       # act too small
+    need = rs.packed_weight_bytes(0, 64, 512)
+    assert f(FAKE, big, 8, FAKE, 4 * need - 1, 4, FAKE, 2, 64, 512, FAKE, None) == 5
+    assert "blobs need" in _err()
