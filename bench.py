@@ -44,11 +44,11 @@ METRIC = "compensated FP4 linear µs/call + HBM GB/s (% of peak) at M=1–8, K,N
 # calibration factors (FETCH_SIZE x2.0, WRITE_SIZE x1.0).  Valid only for the
 # kernel sources whose hash is recorded; reported as null otherwise.
 TRAFFIC = {
-    "sources_sha256": "cf0fa1731979a6a153ed9529fb9d447e9fcf6a0fb701d50b8f47aeabebedac9e",
-    "fetch_bytes": 2.0 * 4726 * 1024,   # FETCH_SIZE 4726 KiB per launch
+    "sources_sha256": "59e61721b845559d69e239fd2b32e7bdbb272e527af162fee3d5a7b8f507f99e",
+    "fetch_bytes": 2.0 * 4725 * 1024,   # FETCH_SIZE 4725 KiB per launch
     "write_bytes": 1.0 * 64 * 1024,     # WRITE_SIZE 64 KiB per launch
 }
-KERNEL_SOURCES = ["gemm.hip", "layout.h", "codec.h", "fp4_frag.h"]
+KERNEL_SOURCES = ["gemm.hip", "layout.h", "codec.h", "fp4_frag.h", "quant_row.h"]
 
 
 def kernel_sources_sha256():
@@ -371,6 +371,13 @@ def run_workload(rs, torch, wl, M, steps, warmup, want_plain=True, want_kernels=
         t_plain = time_graph(torch, lambda i: S.step(i, False), steps, warmup)
         out["plain_us_per_call"] = t_plain * 1e3
         out["comp_overhead"] = t_comp / t_plain - 1.0
+        out["plain_launches"] = rs.from_x_launches(fmt, M, wl.N, wl.K, False)
+        if out["plain_launches"] != out["launches"]:
+            # the same two-launch form on both sides (quantizer + linear)
+            t_c2 = out.get("two_launch_us_per_call", t_comp * 1e3) * 1e-3
+            t_p2 = time_graph(torch, lambda i: S.two_launch(i, False), steps, warmup)
+            out["plain_two_launch_us_per_call"] = t_p2 * 1e3
+            out["comp_overhead_two_launch"] = t_c2 / t_p2 - 1.0
         if want_kernels:
             t_gp = time_graph(torch, lambda i: S.gemm(i, False), steps, warmup)
             out["plain_gemm_us"] = t_gp * 1e3
@@ -601,8 +608,9 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
     }
-    for k in ("plain_us_per_call", "comp_overhead", "gemm_us", "plain_gemm_us", "quant_us",
-              "gemm_GBps", "nmse_comp", "nmse_plain", "paper_numerics"):
+    for k in ("launches", "plain_launches", "plain_us_per_call", "comp_overhead", "plain_two_launch_us_per_call",
+              "comp_overhead_two_launch",
+              "gemm_us", "plain_gemm_us", "quant_us", "gemm_GBps", "nmse_comp", "nmse_plain", "paper_numerics"):
         if k in head:
             line[k] = round(head[k], 6) if isinstance(head[k], float) else head[k]
     line["step_hbm_frac"] = round(head["GBps"] / HBM_PEAK_GBS, 4)
