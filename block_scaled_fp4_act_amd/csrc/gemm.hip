@@ -525,8 +525,8 @@ constexpr int pd_for(int fmt, int rt, int maxs, bool single) {
 }
 constexpr bool apre_for(int fmt, int rt, int maxs, bool single, bool comp) {
     // two row tiles: 2 steps per wave fit the f16 fragments without spills
-    // (the compensated kernels; the plain ones spill)
-    return fmt == kNV && (rt == 1 ? maxs <= (single ? 4 : 2) : (comp && maxs <= 2));
+    // (the compensated kernels; the plain ones spill); four never do
+    return fmt == kNV && (rt == 1 ? maxs <= (single ? 4 : 2) : (rt == 2 && comp && maxs <= 2));
 }
 constexpr int rm_for(int fmt, int rt, int maxs, bool single) { return single ? 0 : 1; }
 
@@ -588,8 +588,12 @@ hipError_t launch_fmt(const GemmArgs& a, int rt, bool comp, int maxs, int KW, in
     if (rt == 1)
         return comp ? launch_maxs<FMT, 1, true>(a, maxs, KW, grid, s, single)
                     : launch_maxs<FMT, 1, false>(a, maxs, KW, grid, s, single);
-    return comp ? launch_maxs<FMT, 2, true>(a, maxs, KW, grid, s, single)
-                : launch_maxs<FMT, 2, false>(a, maxs, KW, grid, s, single);
+    if (rt == 2)
+        return comp ? launch_maxs<FMT, 2, true>(a, maxs, KW, grid, s, single)
+                    : launch_maxs<FMT, 2, false>(a, maxs, KW, grid, s, single);
+    // four row tiles: compensated NVFP4 only (the host's dispatch)
+    if (FMT != kNV || !comp) return hipErrorInvalidValue;
+    return launch_maxs<kNV, 4, true>(a, maxs, KW, grid, s, single);
 }
 
 }  // namespace
@@ -597,7 +601,7 @@ hipError_t launch_fmt(const GemmArgs& a, int rt, bool comp, int maxs, int KW, in
 GemmPlan plan_gemm_small(int64_t M, int64_t N, int64_t S, bool comp, int num_cus) {
     GemmPlan pl;
     const int64_t B = comp ? 2 * M : M;
-    pl.rt = B <= 16 ? 1 : 2;
+    pl.rt = B <= 16 ? 1 : (B <= 32 ? 2 : 4);
     // the fewest steps per wave (a power of two) that covers K with <= 16 waves
     pl.maxs = S <= 16 ? 1 : (S <= 32 ? 2 : (S <= 64 ? 4 : 8));
     pl.kw = (int)((S + pl.maxs - 1) / pl.maxs);

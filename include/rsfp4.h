@@ -148,10 +148,11 @@ rsfp4_status rsfp4_mxfp4_quantize_act_with_residue(const void* x, int xt, int64_
  *   *_linear_compensated:  y = deq(q(x)) W^T + deq(q(r)) W^T (B = 2M rows; the
  *                          buffer must have been quantized with_residue)
  * B = M (plain) or 2M (compensated) activation rows enter the product.  Up to
- * 32 rows, each packed weight step is loaded from HBM once and multiplied with
- * all B rows (the narrow-M, memory-bound regime); above 32 rows a 2-D tiled
- * kernel covers 128 rows x 128 channels per workgroup (each weight tile is then
- * read once per 128 rows).  Either way base and residue products of one token
+ * 32 rows (compensated NVFP4 with N <= 16384 and K <= 16384: up to 64), each
+ * packed weight step is loaded from HBM once and multiplied with all B rows
+ * (the narrow-M, memory-bound regime); above that a 2-D tiled kernel covers
+ * 128 rows x 128 channels per workgroup (each weight tile is then read once
+ * per 128 rows).  Either way base and residue products of one token
  * land in the same lane's accumulators and are added there before the single
  * store (ResServe Section 4.3, Eq. 2 and Section 5.1, Eq. 4).  With up to 32
  * rows and K above 16384 the narrow kernel runs twice, over the two halves of
