@@ -44,7 +44,7 @@ METRIC = "compensated FP4 linear µs/call + HBM GB/s (% of peak) at M=1–8, K,N
 # calibration factors (FETCH_SIZE x2.0, WRITE_SIZE x1.0).  Valid only for the
 # kernel sources whose hash is recorded; reported as null otherwise.
 TRAFFIC = {
-    "sources_sha256": "59e61721b845559d69e239fd2b32e7bdbb272e527af162fee3d5a7b8f507f99e",
+    "sources_sha256": "2ee059d85b11e086f18c71df46933a5ab8ad6d23b3ca878f469f251214aa5340",
     "fetch_bytes": 2.0 * 4725 * 1024,   # FETCH_SIZE 4725 KiB per launch
     "write_bytes": 1.0 * 64 * 1024,     # WRITE_SIZE 64 KiB per launch
 }
