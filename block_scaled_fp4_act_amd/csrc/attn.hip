@@ -20,12 +20,17 @@
 //     one lane swap and an add.  NVFP4 values enter as exact f16 (e * S_b).
 //   * online softmax in the base-2 domain (scores pre-multiplied by log2 e),
 //     row maxima and sums over the four lanes that share a query row.
-//   * PV: the page cannot feed the MFMA's token dimension directly (the scale
-//     blocks run along d, the reduction along tokens -- the page converts V to
-//     FP8 on chip for this).  Here each lane loads 4 bytes (8 d-elements) of 8
-//     tokens, dequantizes them to exact f16 and transposes the 8 x 8 block in
-//     its own registers, so P (already in the A-operand layout the QK output
-//     leaves) times V runs on the same f16 MFMA with fp32 accumulation.
+//   * PV: the reduction runs along tokens while the scale blocks run along d
+//     (the page converts V to FP8 on chip for this).  Here the cache keeps V
+//     in the order the MFMA's B operand wants: one 32-bit word holds the codes
+//     of the 8 tokens a lane's k-slots stand for (the order the QK output
+//     leaves P in) at one column d, and a lane's 8 columns sit in 32 adjacent
+//     bytes; their 8 scale bytes (one per token, same block of d) sit in 8
+//     adjacent bytes.  A lane's V of one 128-column chunk is then two 16-byte
+//     loads and one 8-byte load, dequantized to exact f16 with a per-token
+//     scale pair per packed multiply, and P V runs on the f16 MFMA with fp32
+//     accumulation.  Few, wide loads matter: a wave can have at most 63 loads
+//     outstanding, and a page is 7 (D = 128) or 12 (D = 256) of them.
 //   * KV splits: a split writes unnormalized partial outputs with its row
 //     maxima and sums; a second kernel combines them (Section 5.2: splits
 //     expose parallelism when batch x KV heads give too few work items).
@@ -78,11 +83,35 @@ struct AttnArgs {
     float* ws_ml;              // [B*H_q][splits][2] row maximum (base 2) and sum
 };
 
-// Page layout, per KV head (36 * D bytes, KV heads consecutive in a page):
+// Page layout, per KV head (36 * D bytes, KV heads consecutive in a page);
+// NC = D / 128 chunks of 128 columns, pi(t) = the k-slot of token t:
 //   [0, 16D)    K codes, token-major: token t at t * D/2 (element 2k low nibble)
-//   [16D, 18D)  K scales: token t at 16D + t * D/16
-//   [18D, 34D)  V codes, token-major
-//   [34D, 36D)  V scales
+//   [16D, 18D)  K scales: token t at 16D + t * D/16, the byte of block
+//               8c + 2q + s (q = 0..3, s = 0..1) at 2 NC q + 2c + s
+//   [18D, 34D)  V codes: column d = 128c + 8a + e (a = 0..15, e = 0..7) of the
+//               tokens in slots 8q .. 8q + 7 is the word at
+//               2048c + 1024 (e / 4) + 16 (a + 16q) + 4 (e % 4), slot 8q + u
+//               in bits 4u .. 4u + 3
+//   [34D, 36D)  V scales: block k (16 columns) of token t at 34D + 32k + pi(t)
+// pi(t) = 8q + u with t = 4q + u (u < 4) or t = 16 + 4q + (u - 4) (u >= 4).
+__device__ __forceinline__ int kv_slot(int t) {
+    return t < 16 ? 8 * (t >> 2) + (t & 3) : 8 * ((t - 16) >> 2) + 4 + (t & 3);
+}
+
+// Eight E2M1 codes times eight per-element E4M3 scales (pairs in s[k] for
+// elements 2k, 2k + 1) -> exact f16, as dequant8 with one scale per element
+// pair.
+__device__ __forceinline__ half8 dequant8_pairs(uint32_t w, const half2v (&s)[4]) {
+    const half2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 0) * s[0];
+    const half2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 1) * s[1];
+    const half2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 2) * s[2];
+    const half2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 3) * s[3];
+    half8 r;
+    r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+    r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+    return r;
+}
+
 template <int D>
 __global__ __launch_bounds__(64) void resattn_kernel(AttnArgs p) {
     constexpr int NC = D / 128;          // 16-byte chunks of a row per lane
@@ -117,11 +146,6 @@ __global__ __launch_bounds__(64) void resattn_kernel(AttnArgs p) {
         if (qvalid) qs = *reinterpret_cast<const float*>(rec);
     }
 
-    // V tokens of this lane's k-slots: the order the QK output leaves P in
-    int vtok[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) vtok[u] = u < 4 ? 4 * j + u : 16 + 4 * j + (u - 4);
-
     floatx4 o[NC][8];
 #pragma unroll
     for (int c = 0; c < NC; ++c)
@@ -131,9 +155,9 @@ __global__ __launch_bounds__(64) void resattn_kernel(AttnArgs p) {
 
     struct Raw {
         uint4 kc[2][NC];
-        uint32_t ks[2][NC];
-        uint32_t vc[8][NC];
-        uint32_t vs[8][NC];
+        uint32_t ks[2];        // 2 NC scale bytes of token 16 tt + i
+        uint4 vc[NC][2];       // 8 columns x 8 tokens
+        u32x2 vs[NC];          // 8 tokens' scales of the lane's block
     };
     const int64_t hb = (int64_t)h * 36 * D;
     auto load_page = [&](int pg, Raw& R) {
@@ -145,18 +169,16 @@ __global__ __launch_bounds__(64) void resattn_kernel(AttnArgs p) {
         for (int tt = 0; tt < 2; ++tt) {
             const int t = 16 * tt + i;
 #pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                R.kc[tt][c] = ld128(r, (uint32_t)(t * (D / 2) + 64 * c + 16 * j));
-                R.ks[tt][c] = __builtin_amdgcn_raw_buffer_load_b16(r, (uint32_t)(16 * D + t * (D / 16) + 8 * c + 2 * j), 0, 0);
-            }
+            for (int c = 0; c < NC; ++c) R.kc[tt][c] = ld128(r, (uint32_t)(t * (D / 2) + 64 * c + 16 * j));
+            const uint32_t so = (uint32_t)(16 * D + t * (D / 16) + 2 * NC * j);
+            R.ks[tt] = NC == 1 ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, so, 0, 0)
+                               : __builtin_amdgcn_raw_buffer_load_b32(r, so, 0, 0);
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int c = 0; c < NC; ++c) {
 #pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                R.vc[u][c] = __builtin_amdgcn_raw_buffer_load_b32(r, (uint32_t)(18 * D + vtok[u] * (D / 2) + 64 * c + 4 * i), 0, 0);
-                R.vs[u][c] = __builtin_amdgcn_raw_buffer_load_b8(r, (uint32_t)(34 * D + vtok[u] * (D / 16) + 8 * c + (i >> 1)), 0, 0);
-            }
+            for (int hh = 0; hh < 2; ++hh) R.vc[c][hh] = ld128(r, (uint32_t)(18 * D + 2048 * c + 1024 * hh + 16 * lane));
+            R.vs[c] = __builtin_amdgcn_raw_buffer_load_b64(r, (uint32_t)(34 * D + 32 * (8 * c + (i >> 1)) + 8 * j), 0, 0);
         }
     };
 
@@ -169,8 +191,8 @@ __global__ __launch_bounds__(64) void resattn_kernel(AttnArgs p) {
             acc[tt] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
-                const uint32_t kb = cur.ks[tt][s >> 2];
-                const half8 a = dequant8(word(cur.kc[tt][s >> 2], s & 3), scale_h((s & 3) < 2 ? (kb & 0xFFu) : (kb >> 8)));
+                const uint32_t kb = cur.ks[tt] >> (16 * (s >> 2));
+                const half8 a = dequant8(word(cur.kc[tt][s >> 2], s & 3), scale_h((kb >> ((s & 3) < 2 ? 0 : 8)) & 0xFFu));
                 acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qf[s], acc[tt], 0, 0, 0);
             }
         }
@@ -218,20 +240,22 @@ __global__ __launch_bounds__(64) void resattn_kernel(AttnArgs p) {
                     for (int r = 0; r < 4; ++r) o[c][e][r] *= cr[r];
         }
 
-        // P V: 8 tokens x 8 d-elements per lane, transposed in registers.
-        // Tokens past L have p = 0; their cache bytes (whatever they hold)
-        // decode to finite f16 (FP4 codes are finite, and the scale conversion
-        // maps every byte to a finite value), so they add exact zeros.
+        // P V: per 128-column chunk, column 128c + 8i + e of the lane's 8
+        // tokens is word e of its 32 bytes.  Tokens past L have p = 0; their
+        // cache bytes (whatever they hold) decode to finite f16 (FP4 codes are
+        // finite, and the scale conversion maps every byte to a finite value),
+        // so they add exact zeros.
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-            half8 vv[8];
+            half2v sp[4];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) vv[u] = dequant8(cur.vc[u][c], scale_h(cur.vs[u][c]));
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t sw = cur.vs[c][k >> 1] >> (16 * (k & 1));
+                sp[k] = half2v{scale_h(sw & 0xFFu), scale_h((sw >> 8) & 0xFFu)};
+            }
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                half8 bv;
-#pragma unroll
-                for (int u = 0; u < 8; ++u) bv[u] = vv[u][e];
+                const half8 bv = dequant8_pairs(word(cur.vc[c][e >> 2], e & 3), sp);
                 o[c][e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, bv, o[c][e], 0, 0, 0);
             }
         }
@@ -399,9 +423,28 @@ __global__ __launch_bounds__(256) void kv_write_kernel(const TIn* __restrict__ k
     w1 = e2m1_pack2<1>(w1, x[10] / sd, x[11] / sd, 1.0f);
     w1 = e2m1_pack2<2>(w1, x[12] / sd, x[13] / sd, 1.0f);
     w1 = e2m1_pack2<3>(w1, x[14] / sd, x[15] / sd, 1.0f);
-    uint8_t* base = cache + page * page_bytes + (int64_t)hh * 36 * D + (kv ? 18 * D : 0);
-    *reinterpret_cast<uint2*>(base + off * (D / 2) + 8 * blk) = make_uint2(w0, w1);
-    base[16 * D + off * (D / 16) + blk] = (uint8_t)sbyte;
+    uint8_t* base = cache + page * page_bytes + (int64_t)hh * 36 * D;
+    const int nc = D / 128, c = blk >> 3;
+    if (!kv) {
+        *reinterpret_cast<uint2*>(base + off * (D / 2) + 8 * blk) = make_uint2(w0, w1);
+        base[16 * D + off * (D / 16) + 2 * nc * ((blk & 7) >> 1) + 2 * c + (blk & 1)] = (uint8_t)sbyte;
+        return;
+    }
+    // V: the token's nibble in the word of each of the block's 16 columns.  The
+    // other 7 nibbles of a word belong to other tokens, written by other threads
+    // or launches, so each nibble is cleared and set with atomics on its word.
+    const int ks = kv_slot(off), q = ks >> 3, u = ks & 7;
+    uint8_t* vb = base + 18 * D;
+#pragma unroll
+    for (int e16 = 0; e16 < 16; ++e16) {
+        const int d = 16 * blk + e16;
+        const int a = (d & 127) >> 3, e = d & 7;
+        const uint32_t code = ((e16 < 8 ? w0 : w1) >> (4 * (e16 & 7))) & 0xFu;
+        uint32_t* wp = reinterpret_cast<uint32_t*>(vb + 2048 * c + 1024 * (e >> 2) + 16 * (a + 16 * q) + 4 * (e & 3));
+        atomicAnd(wp, ~(0xFu << (4 * u)));
+        atomicOr(wp, code << (4 * u));
+    }
+    base[34 * D + 32 * blk + ks] = (uint8_t)sbyte;
 }
 
 }  // namespace

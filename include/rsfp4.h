@@ -371,10 +371,18 @@ rsfp4_status rsfp4_mxfp4_quantize_act_kext(const void* x, int xt, int64_t M, int
  * and s_q, s_r the query rows' tensor scales.
  *
  * KV cache: pages of 32 tokens; a page holds, for each KV head in turn,
- * 36 * D bytes: K codes [32][D/2] (token-major, element 2k in the low nibble),
- * K block scales [32][D/16] (E4M3, 16 elements along the head dimension), V
- * codes [32][D/2], V scales [32][D/16].  Token t of a sequence sits at page
- * block_table[b][t / 32], row t % 32.  k_scale / v_scale are the cache's
+ * 36 * D bytes (NC = D / 128):
+ *   [0, 16D)    K codes [32][D/2], token-major, element 2k in the low nibble;
+ *   [16D, 18D)  K block scales (E4M3, 16 elements along the head dimension),
+ *               D/16 bytes per row; block 8c + 2q + s (q < 4, s < 2) of row t
+ *               at 16D + t D/16 + 2 NC q + 2c + s (plain block order at D = 128);
+ *   [18D, 34D)  V codes in the attention kernel's operand order: row t has
+ *               slot pi(t) = 8q + u, where t = 4q + u (u < 4) or
+ *               t = 16 + 4q + u - 4 (u >= 4); column d = 128c + 8a + e of
+ *               slot 8q + u is bits 4u..4u+3 of the 32-bit little-endian word
+ *               at 18D + 2048c + 1024 (e / 4) + 16 (a + 16q) + 4 (e % 4);
+ *   [34D, 36D)  V block scales: block k of row t at 34D + 32k + pi(t).
+ * Token t of a sequence sits at page block_table[b][t / 32], row t % 32.  k_scale / v_scale are the cache's
  * global scales (the page's tests use 1.0): a stored value is k_scale * S_b * e.
  * D is 128 or 256. */
 size_t rsfp4_kv_page_bytes(int64_t H_kv, int64_t D);

@@ -119,24 +119,47 @@ def _check(out, ref, mag, vmax):
                            f"{float((err / np.maximum(bound, 1e-30)).max()):.3e}")
 
 
-def test_kv_cache_write_bitexact():
-    import torch
-    rs = _rs()
-    P = Problem([70, 33], 8, 2, 128, seed=3, k_scale=1.0, v_scale=0.5)
-    pb = rs.kv_page_bytes(2, 128)
+def _kv_slot(t):
+    """k-slot of page row t in the attention kernel's P V operand."""
+    return 8 * (t >> 2) + (t & 3) if t < 16 else 8 * ((t - 16) >> 2) + 4 + (t & 3)
+
+
+def _read_token(pg, base, row, D):
+    """One token's K codes, K scales, V codes and V scales read back from the
+    page region of one KV head, following the documented page layout; codes
+    come back token-major (element 2k in the low nibble of byte k)."""
+    nc = D // 128
+    kc = pg[base + row * D // 2: base + (row + 1) * D // 2]
+    kso = base + 16 * D + row * (D // 16)
+    ksc = np.array([pg[kso + 2 * nc * ((b & 7) >> 1) + 2 * (b >> 3) + (b & 1)] for b in range(D // 16)], np.uint8)
+    sl = _kv_slot(row)
+    q, u = sl >> 3, sl & 7
+    nib = []
+    for d in range(D):
+        c, a, e = d >> 7, (d & 127) >> 3, d & 7
+        off = base + 18 * D + 2048 * c + 1024 * (e >> 2) + 16 * (a + 16 * q) + 4 * (e & 3)
+        nib.append((int.from_bytes(bytes(pg[off:off + 4]), "little") >> (4 * u)) & 0xF)
+    vc = np.array([nib[2 * k] | (nib[2 * k + 1] << 4) for k in range(D // 2)], np.uint8)
+    vsc = np.array([pg[base + 34 * D + 32 * b + sl] for b in range(D // 16)], np.uint8)
+    return kc, ksc, vc, vsc
+
+
+def test_kv_slot_is_a_permutation():
+    assert sorted(_kv_slot(t) for t in range(32)) == list(range(32))
+
+
+@pytest.mark.parametrize("D", [128, 256])
+def test_kv_cache_write_bitexact(D):
+    P = Problem([70, 33], 8, 2, D, seed=3, k_scale=1.0, v_scale=0.5)
+    pb = _rs().kv_page_bytes(2, D)
     cache = P.cache.cpu().numpy().reshape(-1, pb)
-    D = 128
     for b in range(P.B):
         qk = oracle.kv_quantize(P.k[b], 1.0)
         qv = oracle.kv_quantize(P.v[b], 0.5)
         for t in range(P.lens[b]):
             page, row = divmod(int(P.table[b, t // 32]) * 32 + t % 32, 32)
             for h in range(2):
-                base = h * 36 * D
-                kc = cache[page, base + row * 64: base + row * 64 + 64]
-                ksc = cache[page, base + 16 * D + row * 8: base + 16 * D + row * 8 + 8]
-                vc = cache[page, base + 18 * D + row * 64: base + 18 * D + row * 64 + 64]
-                vsc = cache[page, base + 34 * D + row * 8: base + 34 * D + row * 8 + 8]
+                kc, ksc, vc, vsc = _read_token(cache[page], h * 36 * D, row, D)
                 assert np.array_equal(kc, qk["codes"][t, h]) and np.array_equal(ksc, qk["scales"][t, h])
                 assert np.array_equal(vc, qv["codes"][t, h]) and np.array_equal(vsc, qv["scales"][t, h])
 
