@@ -47,7 +47,7 @@ METRIC = "compensated FP4 linear µs/call + HBM GB/s (% of peak) at M=1–8, K,N
 # calibration factors (FETCH_SIZE x2.0, WRITE_SIZE x1.0).  Valid only for the
 # kernel sources whose hash is recorded; reported as null otherwise.
 TRAFFIC = {
-    "sources_sha256": "2ee059d85b11e086f18c71df46933a5ab8ad6d23b3ca878f469f251214aa5340",
+    "sources_sha256": "239438bc818f97541c14dac8fac552ec084bb66e9cff2edbe4fd5dfe737b7e45",
     "fetch_bytes": 2.0 * 4725 * 1024,   # FETCH_SIZE 4725 KiB per launch
     "write_bytes": 1.0 * 64 * 1024,     # WRITE_SIZE 64 KiB per launch
 }
@@ -461,6 +461,49 @@ def pmc_launches(rs, torch):
                       "linear_algorithmic_bytes": gemm_bytes(0, wl.M, wl.N, wl.K, True)}), flush=True)
 
 
+def pmc_paths(rs, torch):
+    """Eager launches for counter passes over every kernel path: the narrow
+    linear at the headline and the large-MLP shape (M = 8), the tiled linear
+    at the large-MLP shape (M = 128, NVFP4) and the MXFP4 shape (M = 256), all
+    compensated, then decode attention (D = 128, GQA 8, B = 8, 32K tokens);
+    three launches each, over distinct weight copies or cache pages."""
+    from block_scaled_fp4_act_amd import inputs
+    cases = [(inputs.ATTN, inputs.ATTN.M), (inputs.LARGE_MLP, 8), (inputs.LARGE_MLP, 128), (inputs.MX, 256)]
+    for wl, M in cases:
+        fmt = 0 if wl.fmt == "nvfp4" else 1
+        gen = torch.Generator(device="cuda").manual_seed(wl.w_seed)
+        W_dev = torch.randn((wl.N, wl.K), generator=gen, device="cuda", dtype=torch.float32) * 0.02
+        S = Setup(rs, torch, fmt, M, wl.N, wl.K, wl.with_m(M).draw_x(), W_dev)
+        del W_dev
+        for i in range(3):
+            S.quant(i, True)
+        torch.cuda.synchronize()
+        for i in range(3):
+            S.gemm(i, True)
+        torch.cuda.synchronize()
+        print(json.dumps({"pmc_paths": wl.name, "M": M, "format": wl.fmt,
+                          "linear_algorithmic_bytes": gemm_bytes(fmt, M, wl.N, wl.K, True),
+                          "linear_flops": 2 * 2 * M * wl.N * wl.K}), flush=True)
+        del S
+        torch.cuda.empty_cache()
+    name, H_q, H_kv, D, B, L = ATTN_CASES[4]
+    pb = rs.kv_page_bytes(H_kv, D)
+    npg = (L + 31) // 32
+    g = torch.Generator(device="cuda").manual_seed(7)
+    cache = torch.randint(0, 256, (3 * B * npg * pb,), dtype=torch.uint8, device="cuda", generator=g)
+    perm = torch.randperm(3 * B * npg, device="cuda", generator=g).to(torch.int32)
+    seq = torch.full((B,), L, dtype=torch.int32, device="cuda")
+    q = torch.randn((B * H_q, D), device="cuda", generator=g).to(torch.bfloat16)
+    act = rs.quantize_act_with_residue(q, 0, True)
+    out = torch.empty((B, H_q, D), dtype=torch.bfloat16, device="cuda")
+    for r in range(3):
+        table = perm[r * B * npg:(r + 1) * B * npg].view(B, npg).contiguous()
+        rs.resattn_decode(act, cache, table, seq, L, B, H_q, H_kv, D, compensated=True, out=out, out_bf16=True)
+    torch.cuda.synchronize()
+    print(json.dumps({"pmc_paths": "resattn " + name, "B": B, "L": L, "kv_bytes": attn_kv_bytes(B, L, H_kv, D)}),
+          flush=True)
+
+
 def cpu_baseline(wl, x, W, budget_s=12.0, max_calls=100000):
     """The oracle (plain single-threaded C, fp64 accumulation) timed on the
     host: quantize + compensated linear per call, weights quantized beforehand
@@ -515,6 +558,8 @@ def main():
     ap.add_argument("--only-headline", action="store_true", help="skip plain/kernels/sweep (profiling runs)")
     ap.add_argument("--pmc-launches", action="store_true",
                     help="only eager launches for counter passes (copy calibration + headline linear)")
+    ap.add_argument("--pmc-paths", action="store_true",
+                    help="only eager launches of every kernel path for counter passes")
     ap.add_argument("--processes", type=int, default=3,
                     help="also time the headline step in this many fresh processes (1: only this one)")
     ap.add_argument("--cases", default=None,
@@ -526,7 +571,7 @@ def main():
         sys.exit(2)
 
     procs = None
-    if args.processes > 1 and not (args.pmc_launches or args.cases or args.only_headline):
+    if args.processes > 1 and not (args.pmc_launches or args.pmc_paths or args.cases or args.only_headline):
         procs = cross_process(args.processes, args.steps, args.warmup)
 
     import torch
@@ -536,6 +581,9 @@ def main():
     rs.lib()
     if args.pmc_launches:
         pmc_launches(rs, torch)
+        return
+    if args.pmc_paths:
+        pmc_paths(rs, torch)
         return
     if args.cases:
         named = {"attn": inputs.ATTN, "mlp_up": inputs.MLP_UP, "mlp_down": inputs.MLP_DOWN,
