@@ -164,6 +164,36 @@ def test_kv_cache_write_bitexact(D):
                 assert np.array_equal(vc, qv["codes"][t, h]) and np.array_equal(vsc, qv["scales"][t, h])
 
 
+@pytest.mark.parametrize("D", [128, 256])
+def test_kv_cache_write_across_calls(D):
+    """Decode-style writes: tokens arrive over several calls (odd rows first,
+    then even rows, then one token per call) into pages that hold other bytes;
+    each call must clear and set only its tokens' nibbles of the shared V
+    words, so every token reads back bit-exact at the end."""
+    import torch
+    rs = _rs()
+    H_kv, T = 2, 40
+    pb = rs.kv_page_bytes(H_kv, D)
+    cache = torch.full((3 * pb,), 0xA7, dtype=torch.uint8, device="cuda")
+    k = inputs.round_to_bf16(_rand((T, H_kv, D), 31 + D))
+    v = inputs.round_to_bf16(_rand((T, H_kv, D), 32 + D))
+    slots = (np.arange(T) + 32).astype(np.int32)          # pages 1 and 2
+    order = [np.arange(1, 32, 2), np.arange(0, 32, 2)] + [np.array([t]) for t in range(32, T)]
+    for idx in order:
+        rs.kv_cache_write(_t(k[idx]).to(torch.bfloat16), _t(v[idx]).to(torch.bfloat16), _t(slots[idx]), cache,
+                          1.0, 1.0)
+    torch.cuda.synchronize()
+    pages = cache.cpu().numpy().reshape(-1, pb)
+    assert (pages[0] == 0xA7).all()                        # page 0 untouched
+    qk, qv = oracle.kv_quantize(k, 1.0), oracle.kv_quantize(v, 1.0)
+    for t in range(T):
+        page, row = divmod(int(slots[t]), 32)
+        for h in range(H_kv):
+            kc, ksc, vc, vsc = _read_token(pages[page], h * 36 * D, row, D)
+            assert np.array_equal(kc, qk["codes"][t, h]) and np.array_equal(ksc, qk["scales"][t, h])
+            assert np.array_equal(vc, qv["codes"][t, h]) and np.array_equal(vsc, qv["scales"][t, h])
+
+
 CASES = [  # (lens, H_q, H_kv, D)
     ([1, 37, 300], 16, 2, 128),      # GQA 8, one token, a partial page, several pages
     ([64, 5, 129], 8, 2, 128),       # GQA 4
