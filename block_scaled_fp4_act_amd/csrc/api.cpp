@@ -663,9 +663,9 @@ rsfp4_status rsfp4_resattn_decode(const void* q_act, size_t q_act_bytes, int com
     if (st != RSFP4_OK) return st;
     if (splits <= 0) splits = attn_auto_splits(B, H_kv, max_seq_len, cus);
     if (splits > 4096) return fail(RSFP4_ERR_SHAPE, "splits = %d above 4096", splits);
-    if (!aligned(q_act, 16) || !aligned(cache, 256) || !aligned(out, out_bf16 ? 2 : 4) || !aligned(ws, 4) ||
+    if (!aligned(q_act, 16) || !aligned(cache, 256) || !aligned(out, out_bf16 ? 2 : 4) || !aligned(ws, 16) ||
         !aligned(block_table, 4) || !aligned(seq_lens, 4))
-        return fail(RSFP4_ERR_ALIGN, "q_act 16-, cache 256-byte aligned; out, ws, tables element aligned");
+        return fail(RSFP4_ERR_ALIGN, "q_act and ws 16-, cache 256-byte aligned; out and tables element aligned");
     const int64_t rb = act_row_bytes(RSFP4_NVFP4, D);
     const size_t need_q = (size_t)rb * (size_t)(B * H_q) * (compensated ? 2 : 1);
     if (q_act_bytes < need_q) return fail(RSFP4_ERR_BUFFER_TOO_SMALL, "q_act holds %zu bytes, needs %zu", q_act_bytes, need_q);

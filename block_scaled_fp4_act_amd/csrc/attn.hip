@@ -374,12 +374,110 @@ __global__ __launch_bounds__(D) void resattn_reduce_kernel(AttnArgs p) {
     store_y(p.out, head * D + d, den > 0.0f ? num / den : 0.0f, p.out_bf16);
 }
 
+// Many splits (64 and more): sixteen waves share a head, wave w summing the
+// partials of splits w, w + 16, ... (a lane holds D / 64 adjacent columns, the
+// first eight partials loaded before the weights are known), and the sixteen
+// part sums meet in LDS.  With few splits and many heads the one-workgroup-
+// per-head kernel above is faster (its launch is 8x lighter).
+constexpr int kWideWaves = 16;
+constexpr int kWideMinSplits = 64;
+
+template <int D>
+__global__ __launch_bounds__(64 * kWideWaves) void resattn_reduce_wide_kernel(AttnArgs p) {
+    constexpr int VW = D / 64;
+    constexpr int NT = 64 * kWideWaves;
+    constexpr int PRE = 8;
+    typedef float vecw __attribute__((ext_vector_type(VW)));
+    __shared__ float wsh[kMaxSplits];
+    __shared__ float red[2][kWideWaves];
+    __shared__ vecw part[kWideWaves][64];
+    const int64_t head = blockIdx.x;
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int S = p.splits;
+    const float* ml = p.ws_ml + head * S * 2;
+    const vecw* src = reinterpret_cast<const vecw*>(p.ws_o + head * S * D) + lane;
+    constexpr int SW = D / VW;                       // vectors per split row
+    vecw pre[PRE];
+#pragma unroll
+    for (int u = 0; u < PRE; ++u) {
+        const int s = w + kWideWaves * u;
+        pre[u] = s < S ? src[(int64_t)s * SW] : vecw(0.0f);
+    }
+    // (m, l) of this thread's splits (S <= 4096: at most four per thread)
+    float ms[kMaxSplits / NT], ls[kMaxSplits / NT];
+    float mloc = -__builtin_inff();
+#pragma unroll
+    for (int u = 0; u < kMaxSplits / NT; ++u) {
+        const int s = t + NT * u;
+        ms[u] = -__builtin_inff();
+        ls[u] = 0.0f;
+        if (s < S) {
+            ms[u] = ml[2 * s];
+            ls[u] = ml[2 * s + 1];
+        }
+        mloc = fmaxf(mloc, ms[u]);
+    }
+    for (int off = 32; off > 0; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off, 64));
+    if (lane == 0) red[0][w] = mloc;
+    __syncthreads();
+    float M = red[0][0];
+#pragma unroll
+    for (int k = 1; k < kWideWaves; ++k) M = fmaxf(M, red[0][k]);
+    const bool live = M > -__builtin_inff();
+    float dl = 0.0f;
+#pragma unroll
+    for (int u = 0; u < kMaxSplits / NT; ++u) {
+        const int s = t + NT * u;
+        if (s < S) {
+            const float wt = live ? __builtin_amdgcn_exp2f(ms[u] - M) : 0.0f;
+            wsh[s] = wt;
+            dl += wt * ls[u];
+        }
+    }
+    for (int off = 32; off > 0; off >>= 1) dl += __shfl_xor(dl, off, 64);
+    if (lane == 0) red[1][w] = dl;
+    __syncthreads();
+    float den = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kWideWaves; ++k) den += red[1][k];
+    vecw num = vecw(0.0f);
+#pragma unroll
+    for (int u = 0; u < PRE; ++u) {
+        const int s = w + kWideWaves * u;
+        if (s < S) num += wsh[s] * pre[u];
+    }
+    for (int s0 = w + kWideWaves * PRE; s0 < S; s0 += kWideWaves * PRE) {
+#pragma unroll
+        for (int u = 0; u < PRE; ++u) {
+            const int s = s0 + kWideWaves * u;
+            pre[u] = s < S ? src[(int64_t)s * SW] : vecw(0.0f);
+        }
+#pragma unroll
+        for (int u = 0; u < PRE; ++u) {
+            const int s = s0 + kWideWaves * u;
+            if (s < S) num += wsh[s] * pre[u];
+        }
+    }
+    part[w][lane] = num;
+    __syncthreads();
+    if (t < D) {
+        const float* pf = reinterpret_cast<const float*>(&part[0][0]);
+        float o = 0.0f;
+#pragma unroll
+        for (int k = 0; k < kWideWaves; ++k) o += pf[k * D + t];
+        store_y(p.out, head * D + t, den > 0.0f ? o / den : 0.0f, p.out_bf16);
+    }
+}
+
 template <int D>
 hipError_t launch_attn_d(const AttnArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(resattn_kernel<D>, dim3((unsigned)a.splits, (unsigned)a.H_kv, (unsigned)a.B), dim3(64), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1) return e;
-    hipLaunchKernelGGL(resattn_reduce_kernel<D>, dim3((unsigned)(a.B * a.H_q)), dim3(D), 0, s, a);
+    if (a.splits >= kWideMinSplits)
+        hipLaunchKernelGGL(resattn_reduce_wide_kernel<D>, dim3((unsigned)(a.B * a.H_q)), dim3(64 * kWideWaves), 0, s, a);
+    else
+        hipLaunchKernelGGL(resattn_reduce_kernel<D>, dim3((unsigned)(a.B * a.H_q)), dim3(D), 0, s, a);
     return hipGetLastError();
 }
 

@@ -416,8 +416,9 @@ size_t rsfp4_resattn_workspace_bytes(int64_t B, int64_t H_q, int64_t D, int spli
  *                beyond max_seq_len are not read);
  *   sm_scale:    usually 1 / sqrt(D);
  *   splits:      KV splits (<= 0: the preset rule); with more than one, the
- *                workspace ws (device, >= rsfp4_resattn_workspace_bytes) holds
- *                the partial outputs and a second kernel combines them;
+ *                workspace ws (device, 16-byte aligned, at least
+ *                rsfp4_resattn_workspace_bytes) holds the partial outputs
+ *                and a second kernel combines them;
  *   out:         [B, H_q, D], fp32 or (out_bf16) bf16, fully overwritten
  *                (a sequence of length 0 gives zeros).
  * Page indices outside the cache read as zeros. */

@@ -212,6 +212,20 @@ def test_resattn_parity(case, splits, comp):
     _check(out, *P.reference(comp=comp))
 
 
+@pytest.mark.parametrize("splits", [64, 100, 130])
+@pytest.mark.parametrize("D", [128, 256])
+def test_resattn_many_splits(D, splits):
+    """64 and more splits take the sixteen-wave combine: a split count that is
+    not a multiple of 16, and more splits than pages (empty splits)."""
+    import torch
+    P = Problem([4000, 1500], 16, 2, D, seed=splits + D)
+    o32 = P.run(splits=splits)
+    _check(o32, *P.reference())
+    o16 = P.run(splits=splits, out_bf16=True)
+    assert torch.equal(o16, o32.to(torch.bfloat16))
+    _check(P.run(comp=False, splits=splits), *P.reference(comp=False))
+
+
 def test_resattn_global_scales_and_bf16_output():
     import torch
     P = Problem([77, 150], 16, 2, 128, seed=5, k_scale=0.75, v_scale=2.0)
