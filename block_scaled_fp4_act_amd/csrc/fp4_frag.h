@@ -15,6 +15,9 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kRsrcWord3 = 0x00020000;     // raw buffer, 32-bit dwords, range checked
+// Cache-policy operand of a buffer load that marks it non-temporal (the nt bit
+// of gfx950's sc0/nt/sc1 policy field): data read once, streamed past the caches.
+constexpr int kStreamPolicy = 2;
 
 // NVFP4 block-scale byte -> f16 holding S_b * 2^-8.  E4M3 (bias 7) and f16
 // (bias 15) line up field by field: the E4M3 exponent and mantissa bits moved to
@@ -50,9 +53,11 @@ __device__ __forceinline__ uint32_t word(const uint4& v, int u) {
     return u == 0 ? v.x : (u == 1 ? v.y : (u == 2 ? v.z : v.w));
 }
 
-// 16-byte raw buffer load (out-of-range offsets read zeros).
+// 16-byte raw buffer load (out-of-range offsets read zeros), with the given
+// cache-policy bits.
+template <int CPOL = 0>
 __device__ __forceinline__ uint4 ld128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, CPOL);
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
 

@@ -44,8 +44,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <cstdlib>
-
 #include <type_traits>
 
 #include "codec.h"
@@ -80,20 +78,22 @@ struct ScaleWord {
     }
 };
 
-template <int FMT, int MAXS>
+// CPOL: the loads' cache-policy bits (kStreamPolicy marks the weight stream
+// non-temporal).
+template <int FMT, int MAXS, int CPOL>
 __device__ __forceinline__ void load_scales(__amdgpu_buffer_rsrc_t r, const uint32_t* off,
                                             ScaleWord<FMT, MAXS>& s) {
     using SW = ScaleWord<FMT, MAXS>;
 #pragma unroll
     for (int q = 0; q < SW::kQuads; ++q) {
         if (SW::kBytesPerQuad == 1) {
-            s.w[q] = __builtin_amdgcn_raw_buffer_load_b8(r, off[q], 0, 0);
+            s.w[q] = __builtin_amdgcn_raw_buffer_load_b8(r, off[q], 0, CPOL);
         } else if (SW::kBytesPerQuad == 2) {
-            s.w[q] = __builtin_amdgcn_raw_buffer_load_b16(r, off[q], 0, 0);
+            s.w[q] = __builtin_amdgcn_raw_buffer_load_b16(r, off[q], 0, CPOL);
         } else if (SW::kBytesPerQuad == 4) {
-            s.w[q] = __builtin_amdgcn_raw_buffer_load_b32(r, off[q], 0, 0);
+            s.w[q] = __builtin_amdgcn_raw_buffer_load_b32(r, off[q], 0, CPOL);
         } else {
-            const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off[q], 0, 0);
+            const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off[q], 0, CPOL);
             s.w[2 * q] = v[0];
             s.w[2 * q + 1] = v[1];
         }
@@ -137,6 +137,18 @@ struct GemmArgs {
 // partials of up to ngl groups wait in LDS and the waves reduce them together
 // after one barrier (one group per wave).
 //
+// ST (streaming order, for plans whose workgroups stream many weight bytes):
+// the weight loads are non-temporal (each byte is read once, so it should not
+// displace the activation records from the caches), a group's block scales
+// are loaded before its codes (the first step's dequantization needs them,
+// and the memory counter returns loads in order, so the MFMAs of step t can
+// start as soon as steps 0..t have arrived instead of after the whole group),
+// the first weight loads are issued before the activation loads, and the next
+// group's loads are pinned ahead of the current group's arithmetic.  Measured
+// at K = 8192, N = 28672 (M = 8): 5-8 % from the cache policy, a further
+// 4-5 % from the ordering.  Single-group plans with few steps per wave keep
+// the plain order (their loads are all issued at once anyway).
+//
 // XT (void: the activation records come from act in global memory): every
 // workgroup quantizes the M input rows x[M, K] (dtype XT) itself, with the
 // quantizer's row routine, into records in its LDS -- the same bytes the
@@ -146,7 +158,7 @@ struct GemmArgs {
 // and the quantization runs while the weights are in flight.  Every workgroup
 // repeats the same quantization, on a compute unit that would otherwise wait
 // for its weights; no workgroup depends on another.
-template <int FMT, int MAXS, int RT, bool COMP, int PD, bool APRE, int RM, typename XT = void, int NCQ = 1>
+template <int FMT, int MAXS, int RT, bool COMP, int PD, bool APRE, int RM, bool ST, typename XT = void, int NCQ = 1>
 __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmArgs p) {
     constexpr bool kInq = !std::is_void<XT>::value;
     using XIn = std::conditional_t<kInq, XT, float>;
@@ -209,14 +221,16 @@ __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmArgs p) {
     // buffer unit returns zeros.  Without branches around the loads the
     // compiler's memory-counter waits stay exact, so prefetched groups are
     // really in flight while earlier ones are computed.
+    constexpr int WPOL = ST ? kStreamPolicy : 0;
     auto load_w = [&](int64_t c, uint4 (&codes)[MAXS], SW& sc) {
         const bool live = c < G;
         const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(blob + kWHeader + (live ? c : 0) * GB), (short)0, live ? (int)GB : 0, kRsrcWord3);
+        if (ST) load_scales<FMT, MAXS, WPOL>(r, sc_off, sc);
 #pragma unroll
         for (int t = 0; t < MAXS; ++t)
-            codes[t] = ld128(r, code_base + (uint32_t)((t / 4) * quad_bytes(FMT) + (t % 4) * kStepCodes));
-        load_scales<FMT, MAXS>(r, sc_off, sc);
+            codes[t] = ld128<WPOL>(r, code_base + (uint32_t)((t / 4) * quad_bytes(FMT) + (t % 4) * kStepCodes));
+        if (!ST) load_scales<FMT, MAXS, WPOL>(r, sc_off, sc);
     };
 
     // in-workgroup quantization: this thread's row and chunks of x, loaded
@@ -306,12 +320,19 @@ __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmArgs p) {
             }
         }
     };
-    if (!kInq) load_act();
-
+    if (ST && !kInq) {
 #pragma unroll
-    for (int q = 0; q < PD; ++q) load_w(c0 + q * grid, wb[q], wsc[q]);
+        for (int q = 0; q < PD; ++q) load_w(c0 + q * grid, wb[q], wsc[q]);
+        load_act();
+    } else {
+        if (!kInq) load_act();
+#pragma unroll
+        for (int q = 0; q < PD; ++q) load_w(c0 + q * grid, wb[q], wsc[q]);
+    }
 
-    for (int k = threadIdx.x; k < ngl; k += blockDim.x) counters[k] = 0;
+    // the deferred reduction (RM = 1) uses no counters
+    if (RM == 0)
+        for (int k = threadIdx.x; k < ngl; k += blockDim.x) counters[k] = 0;
 
     if constexpr (kInq) {
         // row mq of x by threads lt = 0 .. qrow - 1 of its group; threads past
@@ -340,7 +361,7 @@ __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmArgs p) {
             }
         }
     }
-    __syncthreads();                              // counters are zero
+    if (RM == 0) __syncthreads();                 // counters are zero
 
     // ---- fold and store the group reduced from LDS slot `slot` (one wave) ----
     auto reduce_slot = [&](int64_t c, int slot) {
@@ -478,6 +499,8 @@ __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmArgs p) {
         for (int q = 0; q < NB; ++q) {
             const int64_t j = j0 + q;
             load_w(c0 + (j + PD) * grid, wb[(q + PD) % NB], wsc[(q + PD) % NB]);
+            // keep the compiler from sinking these loads below the arithmetic
+            if (ST) __builtin_amdgcn_sched_barrier(0);
             if (j < nj) {
                 if (RM == 0 && slot == ngl) {     // wrap: every slot reduced -> reset
                     __syncthreads();
@@ -496,32 +519,37 @@ __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmArgs p) {
     }
 }
 
-template <int FMT, int MAXS, int RT, bool COMP, int PD, bool APRE, int RM, typename XT = void, int NCQ = 1>
+template <int FMT, int MAXS, int RT, bool COMP, int PD, bool APRE, int RM, bool ST, typename XT = void, int NCQ = 1>
 hipError_t launch_t(const GemmArgs& a, int KW, int64_t grid, hipStream_t s) {
     constexpr bool kInq = !std::is_void<XT>::value;
     // allow the LDS of a CU for the partial-sum slots and, quantizing in the
     // workgroup, the activation records (set once per kernel)
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&gemm_small_kernel<FMT, MAXS, RT, COMP, PD, APRE, RM, XT, NCQ>),
+        reinterpret_cast<const void*>(&gemm_small_kernel<FMT, MAXS, RT, COMP, PD, APRE, RM, ST, XT, NCQ>),
         hipFuncAttributeMaxDynamicSharedMemorySize, kInq ? kLdsInq : kRedBytesMax + 1024);
     if (attr != hipSuccess) return attr;
     size_t lds = (size_t)((a.ngl + 63) & ~63) * 4 + (size_t)a.ngl * KW * RT * (COMP ? 512 : 1024);
     if (kInq) lds += (size_t)(COMP ? 2 * a.M : a.M) * a.row_bytes;
-    hipLaunchKernelGGL((gemm_small_kernel<FMT, MAXS, RT, COMP, PD, APRE, RM, XT, NCQ>),
+    hipLaunchKernelGGL((gemm_small_kernel<FMT, MAXS, RT, COMP, PD, APRE, RM, ST, XT, NCQ>),
                        dim3((unsigned)grid, a.offsets ? (unsigned)a.E : 1u), dim3(64 * KW), lds, s, a);
     return hipGetLastError();
 }
 
-// Variant table, from a sweep of prefetch depth, pre-dequantized activations
-// and reduction mode on the decode workloads (and the compiler's register
-// counts: 128 VGPRs at 16 waves per CU).  Deep prefetch does not pay: one group
-// ahead is best when a workgroup streams several groups.  A workgroup with a
-// single group reduces it as soon as its last partial lands (RM = 0); with
-// several groups the deferred reduction (RM = 1) is faster.
+// Variant table, from sweeps of prefetch depth, pre-dequantized activations,
+// reduction mode and load order on the decode workloads (and the compiler's
+// register counts: 128 VGPRs at 16 waves per CU).  Deep prefetch does not pay
+// (depth 2 spills): one group ahead is best for NVFP4 when a workgroup streams
+// several groups; MXFP4 (one MFMA per step, no dequantization) and
+// single-group plans issue each group's loads just before it.  A workgroup
+// with a single group and few steps per wave reduces it as soon as its last
+// partial lands (RM = 0); otherwise the deferred reduction (RM = 1) is faster.
+// The streaming order (ST) pays wherever a wave streams several groups or
+// eight steps; single-group plans of one to four steps per wave keep the
+// plain order (K = N = 4096: 5.3 against 5.6-6.0 us).
 constexpr int pd_for(int fmt, int rt, int maxs, bool single) {
     if (single) return 0;
     if (fmt == kNV) return maxs <= 4 ? 1 : 0;
-    return rt == 1 ? (maxs <= 4 ? 1 : 0) : (maxs <= 2 ? 1 : 0);
+    return rt == 1 ? 0 : (maxs <= 2 ? 1 : 0);
 }
 constexpr bool apre_for(int fmt, int rt, int maxs, bool single, bool comp) {
     // one row tile: up to 4 steps per wave (compensated, or one pass over the
@@ -530,48 +558,16 @@ constexpr bool apre_for(int fmt, int rt, int maxs, bool single, bool comp) {
     // fit (the compensated kernels; the plain ones spill), four never do
     return fmt == kNV && (rt == 1 ? maxs <= (single || comp ? 4 : 2) : (rt == 2 && comp && maxs <= 2));
 }
-constexpr int rm_for(int fmt, int rt, int maxs, bool single) { return single ? 0 : 1; }
-
-#ifdef RSFP4_TUNE
-// Tuning builds only: RSFP4_TUNE_PD / _APRE / _RM override the table for one
-// row tile of compensated calls, to measure the alternatives.
-inline int tune_env(const char* n, int dflt) {
-    const char* e = std::getenv(n);
-    return e ? std::atoi(e) : dflt;
-}
-template <int FMT, bool COMP, int MAXS, int PD, bool APRE>
-hipError_t launch_rm(const GemmArgs& a, int KW, int64_t grid, hipStream_t s, int rm) {
-    return rm == 0 ? launch_t<FMT, MAXS, 1, COMP, PD, APRE, 0>(a, KW, grid, s)
-                   : launch_t<FMT, MAXS, 1, COMP, PD, APRE, 1>(a, KW, grid, s);
-}
-template <int FMT, bool COMP, int MAXS>
-hipError_t launch_tune(const GemmArgs& a, int KW, int64_t grid, hipStream_t s) {
-    const int pd = tune_env("RSFP4_TUNE_PD", pd_for(FMT, 1, MAXS, false));
-    const bool apre = tune_env("RSFP4_TUNE_APRE", apre_for(FMT, 1, MAXS, false, COMP)) != 0;
-    const int rm = tune_env("RSFP4_TUNE_RM", rm_for(FMT, 1, MAXS, false));
-    switch (pd * 2 + (apre ? 1 : 0)) {
-        case 0: return launch_rm<FMT, COMP, MAXS, 0, false>(a, KW, grid, s, rm);
-        case 1: return launch_rm<FMT, COMP, MAXS, 0, true>(a, KW, grid, s, rm);
-        case 2: return launch_rm<FMT, COMP, MAXS, 1, false>(a, KW, grid, s, rm);
-        case 3: return launch_rm<FMT, COMP, MAXS, 1, true>(a, KW, grid, s, rm);
-        case 4: return launch_rm<FMT, COMP, MAXS, 2, false>(a, KW, grid, s, rm);
-        case 5: return launch_rm<FMT, COMP, MAXS, 2, true>(a, KW, grid, s, rm);
-        case 6: return launch_rm<FMT, COMP, MAXS, 3, false>(a, KW, grid, s, rm);
-        default: return launch_rm<FMT, COMP, MAXS, 3, true>(a, KW, grid, s, rm);
-    }
-}
-#endif
+constexpr bool st_for(int maxs, bool single) { return !single || maxs == 8; }
+constexpr int rm_for(int maxs, bool single) { return single && !st_for(maxs, single) ? 0 : 1; }
 
 template <int FMT, int RT, bool COMP, int MAXS>
 hipError_t launch_v(const GemmArgs& a, int KW, int64_t grid, hipStream_t s, bool single) {
-#ifdef RSFP4_TUNE
-    if (RT == 1 && COMP) return launch_tune<FMT, COMP, MAXS>(a, KW, grid, s);
-#endif
     if (single)
         return launch_t<FMT, MAXS, RT, COMP, pd_for(FMT, RT, MAXS, true), apre_for(FMT, RT, MAXS, true, COMP),
-                        rm_for(FMT, RT, MAXS, true)>(a, KW, grid, s);
+                        rm_for(MAXS, true), st_for(MAXS, true)>(a, KW, grid, s);
     return launch_t<FMT, MAXS, RT, COMP, pd_for(FMT, RT, MAXS, false), apre_for(FMT, RT, MAXS, false, COMP),
-                    rm_for(FMT, RT, MAXS, false)>(a, KW, grid, s);
+                    rm_for(MAXS, false), st_for(MAXS, false)>(a, KW, grid, s);
 }
 
 template <int FMT, int RT, bool COMP>
@@ -604,11 +600,17 @@ GemmPlan plan_gemm_small(int64_t M, int64_t N, int64_t S, bool comp, int num_cus
     GemmPlan pl;
     const int64_t B = comp ? 2 * M : M;
     pl.rt = B <= 16 ? 1 : (B <= 32 ? 2 : 4);
-    // the fewest steps per wave (a power of two) that covers K with <= 16 waves
-    pl.maxs = S <= 16 ? 1 : (S <= 32 ? 2 : (S <= 64 ? 4 : 8));
-    pl.kw = (int)((S + pl.maxs - 1) / pl.maxs);
-    const int per_cu = kMaxWaves / pl.kw > 0 ? kMaxWaves / pl.kw : 1;
     const int64_t G = num_groups(N);
+    // the fewest steps per wave (a power of two) that covers K with <= 16 waves;
+    // compensated with one row tile and more groups than compute units, K of
+    // 17..32 steps takes four steps per wave over eight waves, one workgroup
+    // per CU (K = 4096, N = 14336, M = 8: 9.8 against 11.1 us for two steps
+    // over 16 waves)
+    pl.maxs = S <= 16 ? 1 : (S <= 32 ? 2 : (S <= 64 ? 4 : 8));
+    const bool wide4 = comp && pl.rt == 1 && S > 16 && S <= 32 && G > num_cus;
+    if (wide4) pl.maxs = 4;
+    pl.kw = (int)((S + pl.maxs - 1) / pl.maxs);
+    const int per_cu = wide4 ? 1 : (kMaxWaves / pl.kw > 0 ? kMaxWaves / pl.kw : 1);
     const int64_t cap = (int64_t)num_cus * per_cu;
     pl.grid = G < cap ? G : cap;
     const int64_t per_wg = (G + pl.grid - 1) / pl.grid;         // groups per workgroup
@@ -626,10 +628,10 @@ template <int FMT, bool COMP, int MAXS, int NCQ>
 hipError_t launch_inq_v(const GemmArgs& a, int KW, int64_t grid, hipStream_t s, bool single) {
     using XT = __hip_bfloat16;
     if (single)
-        return launch_t<FMT, MAXS, 1, COMP, 1, apre_for(FMT, 1, MAXS, true, COMP), rm_for(FMT, 1, MAXS, true), XT,
-                        NCQ>(a, KW, grid, s);
-    return launch_t<FMT, MAXS, 1, COMP, 1, apre_for(FMT, 1, MAXS, false, COMP), rm_for(FMT, 1, MAXS, false), XT,
-                    NCQ>(a, KW, grid, s);
+        return launch_t<FMT, MAXS, 1, COMP, 1, apre_for(FMT, 1, MAXS, true, COMP), rm_for(MAXS, true),
+                        st_for(MAXS, true), XT, NCQ>(a, KW, grid, s);
+    return launch_t<FMT, MAXS, 1, COMP, 1, apre_for(FMT, 1, MAXS, false, COMP), rm_for(MAXS, false),
+                    st_for(MAXS, false), XT, NCQ>(a, KW, grid, s);
 }
 
 template <int FMT, bool COMP>
