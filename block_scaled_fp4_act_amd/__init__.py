@@ -76,6 +76,29 @@ def workspace_bytes(fmt, M, N, K, compensated=True):
     return int(lib().rsfp4_workspace_bytes(_fmt(fmt), M, N, K, 1 if compensated else 0))
 
 
+_WS = {}
+
+
+def _workspace(fmt, M, N, K, comp, ws, device):
+    """The linear's workspace: `ws` when given (a uint8 cuda tensor, zero-filled
+    before its first use), else one zero-filled buffer per device kept here and
+    shared by every call that passes none (the library leaves its counters
+    zero after each call, so calls in stream order can share it; calls that
+    may run concurrently on other streams must pass their own)."""
+    import torch
+    need = workspace_bytes(fmt, M, N, K, comp)
+    if ws is not None:
+        return ws
+    if need == 0:
+        return None
+    key = torch.device(device).index if torch.device(device).index is not None else torch.cuda.current_device()
+    buf = _WS.get(key)
+    if buf is None or buf.numel() < need:
+        buf = torch.zeros(max(need, 1 << 20), dtype=torch.uint8, device=device)
+        _WS[key] = buf
+    return buf
+
+
 # ---------------------------------------------------------------- prepack --
 
 def prepack_weights(W, fmt, out=None):
@@ -139,37 +162,39 @@ def act_views(act, fmt, M, K, with_residue=True):
 
 # ----------------------------------------------------------------- linear --
 
-def _linear(act, w_packed, M, N, K, fmt, comp, out, bf16=False):
+def _linear(act, w_packed, M, N, K, fmt, comp, out, bf16=False, ws=None):
     import torch
     fmt = _fmt(fmt)
     dt = torch.bfloat16 if bf16 else torch.float32
     if out is None:
         out = torch.empty((M, N), dtype=dt, device=act.device)
     assert out.is_cuda and out.dtype == dt and out.is_contiguous() and out.numel() >= M * N
+    ws = _workspace(fmt, M, N, K, comp, ws, act.device)
     name = f"rsfp4_{_FMT_NAME[fmt]}_linear" + ("_compensated" if comp else "") + ("_bf16" if bf16 else "")
     _check(getattr(lib(), name)(_ptr(act), act.numel(), _ptr(w_packed), w_packed.numel(), M, N, K,
-                                _ptr(out), None, 0, _stream(act)))
+                                _ptr(out), _ptr(ws), ws.numel() if ws is not None else 0, _stream(act)))
     return out
 
 
-def fp4_linear(act, w_packed, M, N, K, fmt, out=None):
+def fp4_linear(act, w_packed, M, N, K, fmt, out=None, ws=None):
     """y = deq(q(x)) W^T (plain W4A4), fp32 [M, N]."""
-    return _linear(act, w_packed, M, N, K, fmt, False, out)
+    return _linear(act, w_packed, M, N, K, fmt, False, out, ws=ws)
 
 
-def fp4_linear_compensated(act, w_packed, M, N, K, fmt, out=None):
-    """y = deq(q(x)) W^T + deq(q(r)) W^T (residue-compensated), fp32 [M, N]."""
-    return _linear(act, w_packed, M, N, K, fmt, True, out)
+def fp4_linear_compensated(act, w_packed, M, N, K, fmt, out=None, ws=None):
+    """y = deq(q(x)) W^T + deq(q(r)) W^T (residue-compensated), fp32 [M, N].
+    ws: the split-K workspace (workspace_bytes; a shared one when omitted)."""
+    return _linear(act, w_packed, M, N, K, fmt, True, out, ws=ws)
 
 
-def fp4_linear_bf16(act, w_packed, M, N, K, fmt, out=None):
+def fp4_linear_bf16(act, w_packed, M, N, K, fmt, out=None, ws=None):
     """As fp4_linear, bf16 output (round to nearest even)."""
-    return _linear(act, w_packed, M, N, K, fmt, False, out, bf16=True)
+    return _linear(act, w_packed, M, N, K, fmt, False, out, bf16=True, ws=ws)
 
 
-def fp4_linear_compensated_bf16(act, w_packed, M, N, K, fmt, out=None):
+def fp4_linear_compensated_bf16(act, w_packed, M, N, K, fmt, out=None, ws=None):
     """As fp4_linear_compensated, bf16 output (round to nearest even)."""
-    return _linear(act, w_packed, M, N, K, fmt, True, out, bf16=True)
+    return _linear(act, w_packed, M, N, K, fmt, True, out, bf16=True, ws=ws)
 
 
 def nvfp4_linear(act, w_packed, M, N, K, out=None):
@@ -216,12 +241,13 @@ def from_x_launches(fmt, M, N, K, compensated=True, x_dtype=None):
     return lib().rsfp4_from_x_launches(_fmt(fmt), xt, M, N, K, 1 if compensated else 0)
 
 
-def fp4_linear_from_x(x, w_packed, N, fmt, compensated=True, out=None, out_dtype=None, act=None):
+def fp4_linear_from_x(x, w_packed, N, fmt, compensated=True, out=None, out_dtype=None, act=None, ws=None):
     """Quantize x[M, K] (cuda, fp32/bf16) and apply the linear in one call:
     y [M, N] (fp32, or bf16 with out_dtype=torch.bfloat16).  act: an
     activation buffer of packed_act_bytes(fmt, M, K, compensated) bytes that
     the call uses where the quantizer and the linear run as two launches
-    (allocated here when omitted)."""
+    (allocated here when omitted); ws: the linear's workspace, as for
+    fp4_linear_compensated."""
     import torch
     fmt = _fmt(fmt)
     assert x.is_cuda and x.dim() == 2 and x.is_contiguous()
@@ -233,9 +259,11 @@ def fp4_linear_from_x(x, w_packed, N, fmt, compensated=True, out=None, out_dtype
     assert out.is_cuda and out.dtype == dt and out.is_contiguous() and out.numel() >= M * N
     if act is None:
         act = torch.empty(packed_act_bytes(fmt, M, K, compensated), dtype=torch.uint8, device=x.device)
+    ws = _workspace(fmt, M, N, K, compensated, ws, x.device)
     name = f"rsfp4_{_FMT_NAME[fmt]}_linear" + ("_compensated" if compensated else "") + "_from_x"
     _check(getattr(lib(), name)(_ptr(x), _dtype_code(x), M, N, K, _ptr(w_packed), w_packed.numel(), _ptr(out),
-                                _dtype_code(out), _ptr(act), act.numel(), _stream(x)))
+                                _dtype_code(out), _ptr(act), act.numel(), _ptr(ws),
+                                ws.numel() if ws is not None else 0, _stream(x)))
     return out
 
 

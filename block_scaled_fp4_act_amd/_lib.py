@@ -40,10 +40,10 @@ SIGNATURES = {
     "rsfp4_nvfp4_grouped_linear_compensated": (INT, [P, SZ, I64, P, SZ, I64, P, I64, I64, I64, P, P]),
     "rsfp4_mxfp4_grouped_linear": (INT, [P, SZ, I64, P, SZ, I64, P, I64, I64, I64, P, P]),
     "rsfp4_mxfp4_grouped_linear_compensated": (INT, [P, SZ, I64, P, SZ, I64, P, I64, I64, I64, P, P]),
-    "rsfp4_nvfp4_linear_from_x": (INT, [P, INT, I64, I64, I64, P, SZ, P, INT, P, SZ, P]),
-    "rsfp4_nvfp4_linear_compensated_from_x": (INT, [P, INT, I64, I64, I64, P, SZ, P, INT, P, SZ, P]),
-    "rsfp4_mxfp4_linear_from_x": (INT, [P, INT, I64, I64, I64, P, SZ, P, INT, P, SZ, P]),
-    "rsfp4_mxfp4_linear_compensated_from_x": (INT, [P, INT, I64, I64, I64, P, SZ, P, INT, P, SZ, P]),
+    "rsfp4_nvfp4_linear_from_x": (INT, [P, INT, I64, I64, I64, P, SZ, P, INT, P, SZ, P, SZ, P]),
+    "rsfp4_nvfp4_linear_compensated_from_x": (INT, [P, INT, I64, I64, I64, P, SZ, P, INT, P, SZ, P, SZ, P]),
+    "rsfp4_mxfp4_linear_from_x": (INT, [P, INT, I64, I64, I64, P, SZ, P, INT, P, SZ, P, SZ, P]),
+    "rsfp4_mxfp4_linear_compensated_from_x": (INT, [P, INT, I64, I64, I64, P, SZ, P, INT, P, SZ, P, SZ, P]),
     "rsfp4_nvfp4_quantize_act_alpha": (INT, [P, INT, I64, I64, P, INT, P, SZ, P]),
     "rsfp4_nvfp4_tensor_alpha": (INT, [P, INT, I64, I64, P, P]),
     "rsfp4_kv_page_bytes": (SZ, [I64, I64]),

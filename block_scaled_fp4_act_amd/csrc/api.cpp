@@ -98,11 +98,23 @@ rsfp4_status quantize(int fmt, const void* x, int xt, int64_t M, int64_t K, int 
                       "quantize launch");
 }
 
+// The narrow linear's plan for one launch over `steps` (split across
+// workgroups where the shape gains from it: compensated NVFP4, see
+// plan_gemm_small), its workspace bytes, and whether the caller's workspace
+// allows the split (else the unsplit plan, the same result up to the
+// summation order of the K slices).
+GemmPlan narrow_plan(int fmt, bool comp, int64_t M, int64_t N, int64_t steps, int cus, bool single_pass,
+                     size_t ws_bytes, int64_t* need) {
+    const bool split_ok = fmt == RSFP4_NVFP4 && comp && single_pass;
+    GemmPlan pl = plan_gemm_small(M, N, steps, comp, cus, split_ok);
+    *need = split_ws_bytes(pl, comp, N);
+    if (pl.ks > 1 && (size_t)*need > ws_bytes) pl = plan_gemm_small(M, N, steps, comp, cus, false);
+    return pl;
+}
+
 rsfp4_status linear(int fmt, bool comp, const void* act, size_t act_bytes, const void* w_packed,
                     size_t w_bytes, int64_t M, int64_t N, int64_t K, void* y, bool out_bf16, void* ws,
                     size_t ws_bytes, void* stream) {
-    (void)ws;
-    (void)ws_bytes;
     g_err[0] = 0;
     rsfp4_status st = check_common(fmt, K);
     if (st != RSFP4_OK) return st;
@@ -114,6 +126,8 @@ rsfp4_status linear(int fmt, bool comp, const void* act, size_t act_bytes, const
     const int64_t B = comp ? 2 * M : M;
     if (!aligned(act, 16) || !aligned(w_packed, 256) || !aligned(y, out_bf16 ? 2 : 4))
         return fail(RSFP4_ERR_ALIGN, "act must be 16-, w_packed 256- and y element aligned");
+    if (ws == nullptr) ws_bytes = 0;
+    if (ws_bytes > 0 && !aligned(ws, 256)) return fail(RSFP4_ERR_ALIGN, "ws must be 256-byte aligned");
     const int64_t rb = act_row_bytes(fmt, K);
     const size_t need_a = (size_t)rb * (size_t)B;
     if (act_bytes < need_a) return fail(RSFP4_ERR_BUFFER_TOO_SMALL, "act holds %zu bytes, needs %zu", act_bytes, need_a);
@@ -161,13 +175,14 @@ rsfp4_status linear(int fmt, bool comp, const void* act, size_t act_bytes, const
     const int passes = (S + chunk - 1) / chunk;
     for (int pass = 0; pass < passes; ++pass) {
         const int s_lo = pass * chunk, s_hi = s_lo + chunk < S ? s_lo + chunk : S;
-        const GemmPlan pl = plan_gemm_small(M, N, s_hi - s_lo, comp, cus);
+        int64_t need = 0;
+        const GemmPlan pl = narrow_plan(fmt, comp, M, N, s_hi - s_lo, cus, passes == 1, ws_bytes, &need);
         if (std::getenv("RSFP4_LOG"))
             std::fprintf(stderr, "[rsfp4] linear fmt=%d comp=%d M=%lld N=%lld K=%lld steps=[%d,%d) rt=%d maxs=%d "
-                         "kw=%d grid=%lld ngl=%d\n", fmt, (int)comp, (long long)M, (long long)N, (long long)K,
-                         s_lo, s_hi, pl.rt, pl.maxs, pl.kw, (long long)pl.grid, pl.ngl);
+                         "kw=%d grid=%lld ngl=%d ks=%d\n", fmt, (int)comp, (long long)M, (long long)N, (long long)K,
+                         s_lo, s_hi, pl.rt, pl.maxs, pl.kw, (long long)pl.grid, pl.ngl, pl.ks);
         st = hip_status(launch_gemm_small(fmt, pl, comp, act, rb, w_packed, (int)M, N, K, y, out_bf16, s_lo,
-                                          s_hi, pass > 0, (hipStream_t)stream),
+                                          s_hi, pass > 0, pl.ks > 1 ? ws : nullptr, (hipStream_t)stream),
                         "linear launch");
         if (st != RSFP4_OK) return st;
     }
@@ -222,7 +237,7 @@ bool from_x_one_launch(int fmt, bool comp, int64_t M) {
 
 rsfp4_status linear_from_x(int fmt, bool comp, const void* x, int xt, int64_t M, int64_t N, int64_t K,
                            const void* w_packed, size_t w_bytes, void* y, int yt, void* act, size_t act_bytes,
-                           void* stream) {
+                           void* ws, size_t ws_bytes, void* stream) {
     g_err[0] = 0;
     rsfp4_status st = check_common(fmt, K);
     if (st != RSFP4_OK) return st;
@@ -263,7 +278,7 @@ rsfp4_status linear_from_x(int fmt, bool comp, const void* x, int xt, int64_t M,
     }
     st = quantize(fmt, x, xt, M, K, comp ? 1 : 0, act, act_bytes, stream);
     if (st != RSFP4_OK) return st;
-    return linear(fmt, comp, act, act_bytes, w_packed, w_bytes, M, N, K, y, out_bf16, nullptr, 0, stream);
+    return linear(fmt, comp, act, act_bytes, w_packed, w_bytes, M, N, K, y, out_bf16, ws, ws_bytes, stream);
 }
 
 // ---- selective compensation (K-Ext) ----
@@ -390,8 +405,18 @@ size_t rsfp4_packed_weight_bytes(int fmt, int64_t N, int64_t K) {
 }
 
 size_t rsfp4_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, int compensated) {
-    (void)fmt; (void)M; (void)N; (void)K; (void)compensated;
-    return 0;
+    g_err[0] = 0;
+    if (check_common(fmt, K) != RSFP4_OK || M < 1 || M > 65535 || N < 1 || N > (int64_t)1 << 24 || K > kMaxLinearK)
+        return 0;
+    const int64_t B = compensated ? 2 * M : M;
+    const int64_t S = num_steps(K);
+    // the split applies to one-pass plans of the narrow kernel's single row tile
+    if (B > 16 || K > kMaxNarrowK) return 0;
+    int cus = 0;
+    if (num_cus(&cus) != RSFP4_OK) return 0;
+    int64_t need = 0;
+    (void)narrow_plan(fmt, compensated != 0, M, N, S, cus, true, (size_t)1 << 62, &need);
+    return (size_t)need;
 }
 
 #define RSFP4_GROUPED(NAME, FMT, COMP)                                                                         \
@@ -419,24 +444,28 @@ int rsfp4_from_x_launches(int fmt, int xt, int64_t M, int64_t N, int64_t K, int 
 }
 
 rsfp4_status rsfp4_nvfp4_linear_from_x(const void* x, int xt, int64_t M, int64_t N, int64_t K, const void* w_packed,
-                                       size_t w_packed_bytes, void* y, int yt, void* act, size_t act_bytes,
-                                       void* stream) {
-    return linear_from_x(RSFP4_NVFP4, false, x, xt, M, N, K, w_packed, w_packed_bytes, y, yt, act, act_bytes, stream);
+                 size_t w_packed_bytes, void* y, int yt, void* act, size_t act_bytes, void* ws,
+                 size_t ws_bytes, void* stream) {
+    return linear_from_x(RSFP4_NVFP4, false, x, xt, M, N, K, w_packed, w_packed_bytes, y, yt, act, act_bytes, ws, ws_bytes,
+                         stream);
 }
-rsfp4_status rsfp4_nvfp4_linear_compensated_from_x(const void* x, int xt, int64_t M, int64_t N, int64_t K,
-                                                   const void* w_packed, size_t w_packed_bytes, void* y, int yt,
-                                                   void* act, size_t act_bytes, void* stream) {
-    return linear_from_x(RSFP4_NVFP4, true, x, xt, M, N, K, w_packed, w_packed_bytes, y, yt, act, act_bytes, stream);
+rsfp4_status rsfp4_nvfp4_linear_compensated_from_x(const void* x, int xt, int64_t M, int64_t N, int64_t K, const void* w_packed,
+                 size_t w_packed_bytes, void* y, int yt, void* act, size_t act_bytes, void* ws,
+                 size_t ws_bytes, void* stream) {
+    return linear_from_x(RSFP4_NVFP4, true, x, xt, M, N, K, w_packed, w_packed_bytes, y, yt, act, act_bytes, ws, ws_bytes,
+                         stream);
 }
 rsfp4_status rsfp4_mxfp4_linear_from_x(const void* x, int xt, int64_t M, int64_t N, int64_t K, const void* w_packed,
-                                       size_t w_packed_bytes, void* y, int yt, void* act, size_t act_bytes,
-                                       void* stream) {
-    return linear_from_x(RSFP4_MXFP4, false, x, xt, M, N, K, w_packed, w_packed_bytes, y, yt, act, act_bytes, stream);
+                 size_t w_packed_bytes, void* y, int yt, void* act, size_t act_bytes, void* ws,
+                 size_t ws_bytes, void* stream) {
+    return linear_from_x(RSFP4_MXFP4, false, x, xt, M, N, K, w_packed, w_packed_bytes, y, yt, act, act_bytes, ws, ws_bytes,
+                         stream);
 }
-rsfp4_status rsfp4_mxfp4_linear_compensated_from_x(const void* x, int xt, int64_t M, int64_t N, int64_t K,
-                                                   const void* w_packed, size_t w_packed_bytes, void* y, int yt,
-                                                   void* act, size_t act_bytes, void* stream) {
-    return linear_from_x(RSFP4_MXFP4, true, x, xt, M, N, K, w_packed, w_packed_bytes, y, yt, act, act_bytes, stream);
+rsfp4_status rsfp4_mxfp4_linear_compensated_from_x(const void* x, int xt, int64_t M, int64_t N, int64_t K, const void* w_packed,
+                 size_t w_packed_bytes, void* y, int yt, void* act, size_t act_bytes, void* ws,
+                 size_t ws_bytes, void* stream) {
+    return linear_from_x(RSFP4_MXFP4, true, x, xt, M, N, K, w_packed, w_packed_bytes, y, yt, act, act_bytes, ws, ws_bytes,
+                         stream);
 }
 
 rsfp4_status rsfp4_nvfp4_prepack_weights(const void* W, int wt, int64_t N, int64_t K, void* w_packed,

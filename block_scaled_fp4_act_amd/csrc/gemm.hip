@@ -123,6 +123,13 @@ struct GemmArgs {
     int64_t blob_stride;
     int M_total;
     int E;
+    // split K (ks > 1): workgroup b owns slice b % ks, steps s_lo + (b % ks) * ss
+    // .. + ss, and the groups b / ks + j * (grid / ks); the slices' partial sums
+    // meet in ws (counters cnt[G], then one record per group and slice)
+    int ks;
+    int ss;
+    int* cnt;
+    float* ws;
 };
 
 // APRE: the activation fragments are dequantized to f16 once, before the
@@ -143,8 +150,11 @@ struct GemmArgs {
 // are loaded before its codes (the first step's dequantization needs them,
 // and the memory counter returns loads in order, so the MFMAs of step t can
 // start as soon as steps 0..t have arrived instead of after the whole group),
-// the first weight loads are issued before the activation loads, and the next
-// group's loads are pinned ahead of the current group's arithmetic.  Measured
+// the first weight loads of a prefetching plan are issued before the
+// activation loads (a single pass, PD = 0, loads the activation fragments
+// first: the in-order memory counter would otherwise hold every step's
+// arithmetic until the last weight byte), and the next group's loads are
+// pinned ahead of the current group's arithmetic.  Measured
 // at K = 8192, N = 28672 (M = 8): 5-8 % from the cache policy, a further
 // 4-5 % from the ordering.  Single-group plans with few steps per wave keep
 // the plain order (their loads are all issued at once anyway).
@@ -158,7 +168,9 @@ struct GemmArgs {
 // and the quantization runs while the weights are in flight.  Every workgroup
 // repeats the same quantization, on a compute unit that would otherwise wait
 // for its weights; no workgroup depends on another.
-template <int FMT, int MAXS, int RT, bool COMP, int PD, bool APRE, int RM, bool ST, typename XT = void, int NCQ = 1>
+// XS: K split across workgroups (p.ks > 1; the partial sums meet in p.ws).
+template <int FMT, int MAXS, int RT, bool COMP, int PD, bool APRE, int RM, bool ST, bool XS = false,
+          typename XT = void, int NCQ = 1>
 __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmArgs p) {
     constexpr bool kInq = !std::is_void<XT>::value;
     using XIn = std::conditional_t<kInq, XT, float>;
@@ -176,12 +188,16 @@ __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmArgs p) {
     const int wave = threadIdx.x >> 6;
     const int KW = blockDim.x >> 6;
     const int g = lane >> 4, i = lane & 15;
-    const int s0 = p.s_lo + wave * MAXS;          // this wave's first step
+    const int ks = XS ? (int)(blockIdx.x % (unsigned)p.ks) : 0;    // K slice of this workgroup
+    const int s_base = XS ? p.s_lo + ks * p.ss : p.s_lo;
+    const int s0 = s_base + wave * MAXS;          // this wave's first step
+    // K elements at or past k_hi belong to another slice or launch
+    const int64_t k_hi = XS && (int64_t)(s_base + p.ss) * kStepK < p.k_hi ? (int64_t)(s_base + p.ss) * kStepK : p.k_hi;
     const int64_t G = num_groups(p.N);
     const int64_t GB = group_bytes(FMT, p.K);
     const uint32_t scale_base = (uint32_t)(kActHead + p.K / 2);
-    const int64_t grid = gridDim.x;
-    const int64_t c0 = blockIdx.x;
+    const int64_t grid = XS ? gridDim.x / p.ks : gridDim.x;       // the group stride
+    const int64_t c0 = XS ? blockIdx.x / p.ks : blockIdx.x;
     const int ngl = p.ngl;
     int* counters = reinterpret_cast<int*>(lds);
     float* red = lds + ((ngl + 63) & ~63);
@@ -276,7 +292,7 @@ __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmArgs p) {
 #pragma unroll
             for (int t = 0; t < MAXS; ++t) {
                 const int64_t k0 = kStepK * (s0 + t) + 32 * g;
-                const bool in = rvalid && k0 < p.k_hi;   // else: out of range -> zeros
+                const bool in = rvalid && k0 < k_hi;     // else: out of range -> zeros
                 const uint32_t rec = in ? (uint32_t)(arow * p.row_bytes) : act_bytes;
                 if (kInq) {
                     const uint8_t* r8 = act_lds + rec;
@@ -320,14 +336,19 @@ __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmArgs p) {
             }
         }
     };
-    if (ST && !kInq) {
+    // The first group's weights are requested in the prologue at any prefetch
+    // depth (with PD = 0 the loop then skips its load of group 0), so no
+    // workgroup waits for its activation fragments before its weight stream
+    // starts.
+    constexpr int PRE = PD > 0 ? PD : 1;
+    if (ST && PD > 0 && !kInq) {
 #pragma unroll
-        for (int q = 0; q < PD; ++q) load_w(c0 + q * grid, wb[q], wsc[q]);
+        for (int q = 0; q < PRE; ++q) load_w(c0 + q * grid, wb[q], wsc[q]);
         load_act();
     } else {
         if (!kInq) load_act();
 #pragma unroll
-        for (int q = 0; q < PD; ++q) load_w(c0 + q * grid, wb[q], wsc[q]);
+        for (int q = 0; q < PRE; ++q) load_w(c0 + q * grid, wb[q], wsc[q]);
     }
 
     // the deferred reduction (RM = 1) uses no counters
@@ -364,38 +385,87 @@ __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmArgs p) {
     if (RM == 0) __syncthreads();                 // counters are zero
 
     // ---- fold and store the group reduced from LDS slot `slot` (one wave) ----
+    // The workgroup's sum of its waves' partials (fixed wave order), PV values
+    // per lane: compensated, token row (16 rt + 4 g + 2 pr) / 2 of channel i
+    // per (row tile, pair); plain, tile rows ti0 and ti0 + 1.
+    constexpr int PV = COMP ? 2 * RT : 4 * RT;
     auto reduce_slot = [&](int64_t c, int slot) {
+        float pv[PV];
 #pragma unroll
         for (int item = 0; item < 2 * RT; ++item) {   // (row tile, pair) per lane
             const int rt = item >> 1, pr = item & 1;
-            const int ti0 = 16 * rt + 4 * g + 2 * pr;    // tile rows ti0, ti0 + 1
-            const int64_t n = c * kGroupN + i;
             if (COMP) {
                 // the waves' folded partials of token row ti0 / 2, in wave order
                 const float* src = red + (slot * KW * RT + rt) * (PW * 64) + pr * 64 + lane;
                 float v = 0.0f;
                 for (int w = 0; w < KW; ++w) v += src[w * RT * (PW * 64)];
+                pv[item] = v;
+            } else {
+                const float* src = red + (slot * KW * RT + rt) * (PW * 64) + (2 * pr) * 64 + lane;
+                float v0 = 0.0f, v1 = 0.0f;
+                for (int w = 0; w < KW; ++w) {
+                    v0 += src[w * RT * (PW * 64)];
+                    v1 += src[w * RT * (PW * 64) + 64];
+                }
+                pv[2 * item] = v0;
+                pv[2 * item + 1] = v1;
+            }
+        }
+        if constexpr (XS) {
+            // Split K: publish this slice's partial, count it in, and let the
+            // slice that completes the count sum all slices' partials in slice
+            // order (so the result does not depend on arrival order), clear the
+            // counter for the next call and store y.  Every access to the
+            // workspace is a device-scope atomic: the partials are stored and
+            // loaded with device-scope coherence (written through to, and read
+            // from, the memory side shared by all XCDs instead of one XCD's
+            // L2), and the wave waits for its partial stores to complete before
+            // its counter increment, so a slice that sees the count complete
+            // reads every other slice's finished partial.  A release/acquire
+            // fence pair would also write back and invalidate this XCD's whole
+            // L2 at every handoff, which measured 4-5 us per handoff.
+            float* rec = p.ws + ((c * p.ks + ks) * PV) * 64 + lane;
+#pragma unroll
+            for (int k = 0; k < PV; ++k) __hip_atomic_store(rec + k * 64, pv[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            int old = 0;
+            if (lane == 0) old = __hip_atomic_fetch_add(p.cnt + c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            old = __builtin_amdgcn_readfirstlane(old);
+            if (old != p.ks - 1) return;
+            float tot[PV];
+#pragma unroll
+            for (int k = 0; k < PV; ++k) tot[k] = 0.0f;
+            for (int q = 0; q < p.ks; ++q) {
+                const float* rq = p.ws + ((c * p.ks + q) * PV) * 64 + lane;
+#pragma unroll
+                for (int k = 0; k < PV; ++k)
+                    tot[k] += q == ks ? pv[k] : __hip_atomic_load(rq + k * 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+#pragma unroll
+            for (int k = 0; k < PV; ++k) pv[k] = tot[k];
+            if (lane == 0) __hip_atomic_store(p.cnt + c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+        for (int item = 0; item < 2 * RT; ++item) {
+            const int rt = item >> 1, pr = item & 1;
+            const int ti0 = 16 * rt + 4 * g + 2 * pr;    // tile rows ti0, ti0 + 1
+            const int64_t n = c * kGroupN + i;
+            if (COMP) {
                 const int m = ti0 >> 1;
                 if (n < p.N && m < Mr) {
-                    float out = FMT == kNV ? s_gw * v : v;
+                    float out = FMT == kNV ? s_gw * pv[item] : pv[item];
                     const int64_t yi = (int64_t)(mb + m) * p.N + n;
                     if (p.accum) out += reinterpret_cast<const float*>(p.y)[yi];
                     store_y(p.y, yi, out, p.out_bf16);
                 }
                 continue;
             }
-            const float* src = red + (slot * KW * RT + rt) * (PW * 64) + (2 * pr) * 64 + lane;
-            float v0 = 0.0f, v1 = 0.0f;
-            for (int w = 0; w < KW; ++w) {
-                v0 += src[w * RT * (PW * 64)];
-                v1 += src[w * RT * (PW * 64) + 64];
-            }
             if (n < p.N) {
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int m = ti0 + h;
                     if (m < Mr) {
-                        const float v = h ? v1 : v0;
+                        const float v = pv[2 * item + h];
                         float out = v;
                         if (FMT == kNV) out = s_gw * ((h ? row_s1[item] : row_s0[item]) * v);
                         const int64_t yi = (int64_t)(mb + m) * p.N + n;
@@ -498,7 +568,7 @@ __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmArgs p) {
 #pragma unroll
         for (int q = 0; q < NB; ++q) {
             const int64_t j = j0 + q;
-            load_w(c0 + (j + PD) * grid, wb[(q + PD) % NB], wsc[(q + PD) % NB]);
+            if (PD > 0 || j > 0) load_w(c0 + (j + PD) * grid, wb[(q + PD) % NB], wsc[(q + PD) % NB]);
             // keep the compiler from sinking these loads below the arithmetic
             if (ST) __builtin_amdgcn_sched_barrier(0);
             if (j < nj) {
@@ -519,18 +589,19 @@ __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmArgs p) {
     }
 }
 
-template <int FMT, int MAXS, int RT, bool COMP, int PD, bool APRE, int RM, bool ST, typename XT = void, int NCQ = 1>
+template <int FMT, int MAXS, int RT, bool COMP, int PD, bool APRE, int RM, bool ST, bool XS = false,
+          typename XT = void, int NCQ = 1>
 hipError_t launch_t(const GemmArgs& a, int KW, int64_t grid, hipStream_t s) {
     constexpr bool kInq = !std::is_void<XT>::value;
     // allow the LDS of a CU for the partial-sum slots and, quantizing in the
     // workgroup, the activation records (set once per kernel)
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&gemm_small_kernel<FMT, MAXS, RT, COMP, PD, APRE, RM, ST, XT, NCQ>),
+        reinterpret_cast<const void*>(&gemm_small_kernel<FMT, MAXS, RT, COMP, PD, APRE, RM, ST, XS, XT, NCQ>),
         hipFuncAttributeMaxDynamicSharedMemorySize, kInq ? kLdsInq : kRedBytesMax + 1024);
     if (attr != hipSuccess) return attr;
     size_t lds = (size_t)((a.ngl + 63) & ~63) * 4 + (size_t)a.ngl * KW * RT * (COMP ? 512 : 1024);
     if (kInq) lds += (size_t)(COMP ? 2 * a.M : a.M) * a.row_bytes;
-    hipLaunchKernelGGL((gemm_small_kernel<FMT, MAXS, RT, COMP, PD, APRE, RM, ST, XT, NCQ>),
+    hipLaunchKernelGGL((gemm_small_kernel<FMT, MAXS, RT, COMP, PD, APRE, RM, ST, XS, XT, NCQ>),
                        dim3((unsigned)grid, a.offsets ? (unsigned)a.E : 1u), dim3(64 * KW), lds, s, a);
     return hipGetLastError();
 }
@@ -563,6 +634,14 @@ constexpr int rm_for(int maxs, bool single) { return single && !st_for(maxs, sin
 
 template <int FMT, int RT, bool COMP, int MAXS>
 hipError_t launch_v(const GemmArgs& a, int KW, int64_t grid, hipStream_t s, bool single) {
+    // split K: compensated NVFP4 with one row tile and one or two steps per
+    // wave (the plans plan_gemm_small makes), streaming order, deferred reduction
+    if constexpr (FMT == kNV && RT == 1 && COMP && MAXS <= 2) {
+        if (a.ks > 1)
+            return launch_t<FMT, MAXS, RT, COMP, pd_for(FMT, RT, MAXS, false), apre_for(FMT, RT, MAXS, false, COMP),
+                            1, true, true>(a, KW, grid, s);
+    }
+    if (a.ks > 1) return hipErrorInvalidValue;
     if (single)
         return launch_t<FMT, MAXS, RT, COMP, pd_for(FMT, RT, MAXS, true), apre_for(FMT, RT, MAXS, true, COMP),
                         rm_for(MAXS, true), st_for(MAXS, true)>(a, KW, grid, s);
@@ -596,7 +675,7 @@ hipError_t launch_fmt(const GemmArgs& a, int rt, bool comp, int maxs, int KW, in
 
 }  // namespace
 
-GemmPlan plan_gemm_small(int64_t M, int64_t N, int64_t S, bool comp, int num_cus) {
+GemmPlan plan_gemm_small(int64_t M, int64_t N, int64_t S, bool comp, int num_cus, bool split_ok) {
     GemmPlan pl;
     const int64_t B = comp ? 2 * M : M;
     pl.rt = B <= 16 ? 1 : (B <= 32 ? 2 : 4);
@@ -619,7 +698,45 @@ GemmPlan plan_gemm_small(int64_t M, int64_t N, int64_t S, bool comp, int num_cus
     const int64_t fit = lds_cap / ((int64_t)pl.kw * pl.rt * (comp ? 512 : 1024));
     pl.ngl = (int)(per_wg < fit ? per_wg : fit);
     if (pl.ngl < 1) pl.ngl = 1;
-    return pl;
+    if (!split_ok || pl.rt != 1 || !comp) return pl;
+
+    // Split K across workgroups (one workgroup per CU, each owning one K slice
+    // of several channel groups), where one of two shapes makes it pay
+    // (measured on the compensated NVFP4 MLP pair, M = 8):
+    //   * few groups, long K (G <= CUs, S >= 64): four slices, so a workgroup
+    //     streams four groups' slices instead of one group's whole K and holds
+    //     a quarter of the activation operand (K = 14336, N = 4096: 12.5
+    //     against 14.8 us);
+    //   * a half round of groups (G a multiple of CUs / 2 but not of CUs): two
+    //     slices make the (group, slice) units a multiple of the CUs (K = 4096,
+    //     N = 14336: 10.7 against 12.6 us).
+    // The MXFP4 shapes and K = N = 4096 are slower split (one handoff costs
+    // about as much as a whole K = 4096 group).
+    int ks = 0;
+    if (G > kSplitGroups) return pl;
+    if (G <= num_cus && S >= 64 && S % 4 == 0) ks = 4;
+    else if (G > num_cus && G % num_cus != 0 && (2 * G) % num_cus == 0 && S % 4 == 0 && S <= 64) ks = 2;
+    if (ks == 0) return pl;
+    const int64_t ss = S / ks;
+    // two steps per wave where they fit in 16 waves (MLP down: 14 waves, up:
+    // 8), else one (four steps per wave spill with the split's reduction)
+    int maxs = 0;
+    for (int m : {2, 1})
+        if (maxs == 0 && ss % m == 0 && ss / m <= kMaxWaves) maxs = m;
+    if (maxs == 0) return pl;
+    GemmPlan sp;
+    sp.rt = 1;
+    sp.maxs = maxs;
+    sp.kw = (int)(ss / maxs);
+    sp.ks = ks;
+    sp.ss = (int)ss;
+    const int64_t per_slice = G * ks >= num_cus ? num_cus / ks : G;   // workgroups per slice
+    sp.grid = per_slice * ks;
+    const int64_t units = (G + per_slice - 1) / per_slice;           // groups per workgroup
+    const int64_t sfit = kRedBytesMax / ((int64_t)sp.kw * 512);
+    sp.ngl = (int)(units < sfit ? units : sfit);
+    if (sp.ngl < 1) sp.ngl = 1;
+    return sp;
 }
 
 // In-workgroup quantization (bf16 x, one row tile, up to 4 steps per wave):
@@ -629,9 +746,9 @@ hipError_t launch_inq_v(const GemmArgs& a, int KW, int64_t grid, hipStream_t s, 
     using XT = __hip_bfloat16;
     if (single)
         return launch_t<FMT, MAXS, 1, COMP, 1, apre_for(FMT, 1, MAXS, true, COMP), rm_for(MAXS, true),
-                        st_for(MAXS, true), XT, NCQ>(a, KW, grid, s);
+                        st_for(MAXS, true), false, XT, NCQ>(a, KW, grid, s);
     return launch_t<FMT, MAXS, 1, COMP, 1, apre_for(FMT, 1, MAXS, false, COMP), rm_for(MAXS, false),
-                    st_for(MAXS, false), XT, NCQ>(a, KW, grid, s);
+                    st_for(MAXS, false), false, XT, NCQ>(a, KW, grid, s);
 }
 
 template <int FMT, bool COMP>
@@ -650,13 +767,25 @@ hipError_t launch_inq_fmt(const GemmArgs& a, int maxs, int ncq, int KW, int64_t 
     }
 }
 
+int64_t split_ws_bytes(const GemmPlan& pl, bool comp, int64_t N) {
+    if (pl.ks <= 1) return 0;
+    const int64_t G = num_groups(N);
+    const int64_t pv = comp ? 2 * pl.rt : 4 * pl.rt;           // partial sums per lane
+    return kSplitCounterBytes + G * pl.ks * pv * 64 * 4;
+}
+
 hipError_t launch_gemm_small(int fmt, const GemmPlan& pl, bool comp, const void* act,
                              int64_t row_bytes, const void* blob, int M, int64_t N, int64_t K,
-                             void* y, bool out_bf16, int s_lo, int s_hi, bool accum, hipStream_t s) {
+                             void* y, bool out_bf16, int s_lo, int s_hi, bool accum, void* ws, hipStream_t s) {
     const int64_t k_hi = (int64_t)s_hi * kStepK < K ? (int64_t)s_hi * kStepK : K;
+    if (pl.ks > 1 && (ws == nullptr || pl.grid % pl.ks != 0 || pl.ss * pl.ks < s_hi - s_lo)) return hipErrorInvalidValue;
+    int* cnt = static_cast<int*>(ws);
+    if (pl.ks > 1 && num_groups(N) > kSplitGroups) return hipErrorInvalidValue;
+    float* part = pl.ks > 1 ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + kSplitCounterBytes) : nullptr;
     GemmArgs a{static_cast<const uint8_t*>(act), row_bytes, static_cast<const uint8_t*>(blob), M,
-               N, K, y, pl.ngl, s_lo, k_hi, accum ? 1 : 0, out_bf16 ? 1 : 0, nullptr, 64, nullptr, 0, M, 1};
-    const bool single = num_groups(N) <= pl.grid;             // one group per workgroup
+               N, K, y, pl.ngl, s_lo, k_hi, accum ? 1 : 0, out_bf16 ? 1 : 0, nullptr, 64, nullptr, 0, M, 1,
+               pl.ks, pl.ss, cnt, part};
+    const bool single = num_groups(N) <= pl.grid / pl.ks;     // one group per workgroup
     if (fmt == kNV) return launch_fmt<kNV>(a, pl.rt, comp, pl.maxs, pl.kw, pl.grid, s, single);
     return launch_fmt<kMX>(a, pl.rt, comp, pl.maxs, pl.kw, pl.grid, s, single);
 }
@@ -664,8 +793,9 @@ hipError_t launch_gemm_small(int fmt, const GemmPlan& pl, bool comp, const void*
 hipError_t launch_gemm_grouped(int fmt, const GemmPlan& pl, bool comp, const void* act, int64_t row_bytes,
                                int M_total, const void* blobs, int64_t blob_stride, int E, const int32_t* offsets,
                                int max_rows, int64_t N, int64_t K, float* y, hipStream_t s) {
+    if (pl.ks != 1) return hipErrorInvalidValue;
     GemmArgs a{static_cast<const uint8_t*>(act), row_bytes, static_cast<const uint8_t*>(blobs), max_rows, N, K, y,
-               pl.ngl, 0, K, 0, 0, nullptr, 64, offsets, blob_stride, M_total, E};
+               pl.ngl, 0, K, 0, 0, nullptr, 64, offsets, blob_stride, M_total, E, 1, 0, nullptr, nullptr};
     const bool single = num_groups(N) <= pl.grid;
     if (fmt == kNV) return launch_fmt<kNV>(a, pl.rt, comp, pl.maxs, pl.kw, pl.grid, s, single);
     return launch_fmt<kMX>(a, pl.rt, comp, pl.maxs, pl.kw, pl.grid, s, single);
@@ -696,8 +826,9 @@ InqPlan plan_gemm_inq(int fmt, int64_t M, int64_t N, int64_t K, bool comp, int n
 
 hipError_t launch_gemm_inq(int fmt, const InqPlan& q, bool comp, const void* x, const void* blob, int M, int64_t N,
                            int64_t K, void* y, bool out_bf16, hipStream_t s) {
+    if (q.pl.ks != 1) return hipErrorInvalidValue;
     GemmArgs a{nullptr, act_row_bytes(fmt, K), static_cast<const uint8_t*>(blob), M, N, K, y, q.pl.ngl, 0, K, 0,
-               out_bf16 ? 1 : 0, x, q.qrow, nullptr, 0, M, 1};
+               out_bf16 ? 1 : 0, x, q.qrow, nullptr, 0, M, 1, 1, 0, nullptr, nullptr};
     const bool single = num_groups(N) <= q.pl.grid;
     if (fmt == kNV) {   // compensated NVFP4 always takes the two-launch path
         if (comp) return hipErrorInvalidValue;

@@ -42,16 +42,31 @@ struct GemmPlan {
     int kw = 1;
     int64_t grid = 1;
     int ngl = 1;       // groups reduced together (partial sums held in LDS)
+    int ks = 1;        // K slices split across workgroups (1: each workgroup covers the launch's K)
+    int ss = 0;        // steps per slice (ks > 1: kw * maxs)
 };
 
-// Plan for a launch over `steps` K steps of 128 (at most 128 steps).
-GemmPlan plan_gemm_small(int64_t M, int64_t N, int64_t steps, bool comp, int num_cus);
+// Plan for a launch over `steps` K steps of 128 (at most 128 steps).  With
+// split_ok the plan may split K across workgroups (ks > 1), which needs a
+// workspace of split_ws_bytes(plan, ...) bytes.
+GemmPlan plan_gemm_small(int64_t M, int64_t N, int64_t steps, bool comp, int num_cus, bool split_ok = false);
+
+// Workspace of a split plan: kSplitGroups zero-initialised int counters (one
+// per channel group; a fixed area, so calls of any shape can share one
+// workspace: each call leaves the counters it used at zero), then one
+// partial-sum record per group and slice.  Plans split only N of at most
+// kSplitGroups groups.
+constexpr int64_t kSplitGroups = 4096;
+constexpr int64_t kSplitCounterBytes = kSplitGroups * 4;
+int64_t split_ws_bytes(const GemmPlan& pl, bool comp, int64_t N);
 
 // One launch over steps [s_lo, s_hi) of K (s_lo a multiple of 8); accum adds
 // the result to y (the second launch of a K longer than one launch covers).
+// ws: the split plan's workspace (unused when pl.ks == 1); its counters must be
+// zero on entry and are zero again when the launch completes.
 hipError_t launch_gemm_small(int fmt, const GemmPlan& pl, bool comp, const void* act,
                              int64_t row_bytes, const void* blob, int M, int64_t N, int64_t K,
-                             void* y, bool out_bf16, int s_lo, int s_hi, bool accum, hipStream_t s);
+                             void* y, bool out_bf16, int s_lo, int s_hi, bool accum, void* ws, hipStream_t s);
 
 // Grouped (mixture of experts) narrow linear, one launch: expert e multiplies
 // rows offsets[e] .. offsets[e+1] (at most max_rows) of an act buffer of M_total

@@ -110,8 +110,24 @@ size_t rsfp4_packed_act_bytes(int fmt, int64_t M, int64_t K, int with_residue);
  * with zero scales.  Only rsfp4_unpack_weights_canonical reads it back. */
 size_t rsfp4_packed_weight_bytes(int fmt, int64_t N, int64_t K);
 
-/* Device workspace the linear calls need; this build needs none and returns 0
- * (pass ws = NULL, ws_bytes = 0). */
+/* Device workspace (bytes) with which a linear call of this shape may split K
+ * across workgroups; 0 when its plan does not split.  The value depends on the
+ * current device's compute-unit count.  Shapes that split (compensated NVFP4,
+ * one pass of the narrow kernel, at most 16 operand rows, where one of two
+ * patterns makes the split faster -- few 16-channel groups with K of 64 and
+ * more steps of 128, or a number of groups that leaves the last round of
+ * workgroups half empty; the ResServe page's tile-count model, Section 5.1
+ * Eq. 5, names the second) sum their K slices' partial outputs through the
+ * workspace: 4096 int counters, one per 16-channel group (the first 16384
+ * bytes; only N of at most 4096 groups splits), then one partial-sum record
+ * per group and slice.  The counters must be zero before the workspace's
+ * first use (e.g. allocate it zero-filled); every call leaves them zero
+ * again, so one workspace serves any number of calls of any shapes in stream
+ * order (calls that may run concurrently need workspaces of their own).  The slices' partials are
+ * summed in slice order, so the result does not depend on timing.  A linear
+ * call given a NULL or smaller workspace runs the plan without the split
+ * (same result up to the summation order of the slices).  ws must be 256-byte
+ * aligned. */
 size_t rsfp4_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, int compensated);
 
 /* ------------------------------------------------------------- prepack ----
@@ -158,7 +174,10 @@ rsfp4_status rsfp4_mxfp4_quantize_act_with_residue(const void* x, int xt, int64_
  * rows and K above 16384 the narrow kernel runs twice, over the two halves of
  * the K steps, the second launch adding its part to y (so y is written, read
  * back and written again).  act_bytes and w_packed_bytes are checked against
- * the size queries. */
+ * the size queries.  ws, ws_bytes: the optional workspace of
+ * rsfp4_workspace_bytes (NULL, 0 for none; 256-byte aligned, counters zero on
+ * first use, left zero); with it, compensated NVFP4 shapes that gain from it
+ * split K across workgroups. */
 rsfp4_status rsfp4_nvfp4_linear(const void* act, size_t act_bytes, const void* w_packed,
                                 size_t w_packed_bytes, int64_t M, int64_t N, int64_t K,
                                 float* y, void* ws, size_t ws_bytes, void* stream);
@@ -246,23 +265,24 @@ rsfp4_status rsfp4_mxfp4_grouped_linear_compensated(const void* act, size_t act_
  * quantizer, spread over M compute units, is the faster of the two).
  * act: rsfp4_packed_act_bytes(fmt, M, K, compensated) bytes of device memory,
  * 16-byte aligned, owned by the caller; holds the quantized rows after a
- * two-launch call and is left untouched by a one-launch call.  Argument checks
- * as for the two calls. */
+ * two-launch call and is left untouched by a one-launch call.  ws, ws_bytes:
+ * the linear's workspace (rsfp4_workspace_bytes; NULL, 0 for none), as for the
+ * linear calls.  Argument checks as for the two calls. */
 /* Kernel launches such a call makes on the current device: 1 or 2 (0 for
  * arguments the calls reject). */
 int rsfp4_from_x_launches(int fmt, int xt, int64_t M, int64_t N, int64_t K, int compensated);
 rsfp4_status rsfp4_nvfp4_linear_from_x(const void* x, int xt, int64_t M, int64_t N, int64_t K,
                                        const void* w_packed, size_t w_packed_bytes, void* y, int yt,
-                                       void* act, size_t act_bytes, void* stream);
+                                       void* act, size_t act_bytes, void* ws, size_t ws_bytes, void* stream);
 rsfp4_status rsfp4_nvfp4_linear_compensated_from_x(const void* x, int xt, int64_t M, int64_t N, int64_t K,
                                                    const void* w_packed, size_t w_packed_bytes, void* y,
-                                                   int yt, void* act, size_t act_bytes, void* stream);
+                                                   int yt, void* act, size_t act_bytes, void* ws, size_t ws_bytes, void* stream);
 rsfp4_status rsfp4_mxfp4_linear_from_x(const void* x, int xt, int64_t M, int64_t N, int64_t K,
                                        const void* w_packed, size_t w_packed_bytes, void* y, int yt,
-                                       void* act, size_t act_bytes, void* stream);
+                                       void* act, size_t act_bytes, void* ws, size_t ws_bytes, void* stream);
 rsfp4_status rsfp4_mxfp4_linear_compensated_from_x(const void* x, int xt, int64_t M, int64_t N, int64_t K,
                                                    const void* w_packed, size_t w_packed_bytes, void* y,
-                                                   int yt, void* act, size_t act_bytes, void* stream);
+                                                   int yt, void* act, size_t act_bytes, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------- paper numerics: given tensor scale (NVFP4) --
  * The operator as the ResServe page's fused quantizer computes it (Appendix

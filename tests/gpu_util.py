@@ -51,3 +51,13 @@ def check_linear(y_gpu, y_orc, beta, tol=1e-4):
     bad = err > tol * beta
     assert not bad.any(), (f"{int(bad.sum())} of {bad.size} outside tolerance; worst ratio "
                            f"{float((err / np.maximum(beta, 1e-300)).max()):.3e}")
+
+
+def sample_channels(N, M, seed, min_outputs=4096, floor=192):
+    """Sorted output channels for a sampled full-size check: enough that the
+    sample holds at least min_outputs elements of y [M, N] (and floor
+    channels), always including the first and the last channel."""
+    n = min(N, max(floor, -(-min_outputs // M)))
+    rows = np.sort(np.random.default_rng(seed).choice(N, n, replace=False))
+    rows[0], rows[-1] = 0, N - 1
+    return rows

@@ -147,16 +147,16 @@ def test_from_x_validation():
     f = L.rsfp4_nvfp4_linear_compensated_from_x
     act_need = rs.packed_act_bytes(0, 2, 512, True)
     # null act, unknown output dtype, misaligned act, small act, small weights
-    assert f(FAKE, 1, 2, 16, 512, FAKE, 1 << 30, FAKE, 0, None, 0, None) == 1
-    assert f(FAKE, 1, 2, 16, 512, FAKE, 1 << 30, FAKE, 7, FAKE, 1 << 30, None) == 4
-    assert f(FAKE, 1, 2, 16, 512, FAKE, 1 << 30, FAKE, 0, ctypes.c_void_p(0x100008), 1 << 30, None) == 3
-    assert f(FAKE, 1, 2, 16, 512, FAKE, 1 << 30, FAKE, 0, FAKE, act_need - 1, None) == 5
+    assert f(FAKE, 1, 2, 16, 512, FAKE, 1 << 30, FAKE, 0, None, 0, None, 0, None) == 1
+    assert f(FAKE, 1, 2, 16, 512, FAKE, 1 << 30, FAKE, 7, FAKE, 1 << 30, None, 0, None) == 4
+    assert f(FAKE, 1, 2, 16, 512, FAKE, 1 << 30, FAKE, 0, ctypes.c_void_p(0x100008), 1 << 30, None, 0, None) == 3
+    assert f(FAKE, 1, 2, 16, 512, FAKE, 1 << 30, FAKE, 0, FAKE, act_need - 1, None, 0, None) == 5
     assert "act holds" in _err()
-    assert f(FAKE, 1, 2, 16, 512, FAKE, 100, FAKE, 0, FAKE, 1 << 30, None) == 5
+    assert f(FAKE, 1, 2, 16, 512, FAKE, 100, FAKE, 0, FAKE, 1 << 30, None, 0, None) == 5
     # shapes: K past the quantizer, M outside [1, 65535], bad K
-    assert L.rsfp4_mxfp4_linear_from_x(FAKE, 1, 2, 16, 32800, FAKE, 1 << 30, FAKE, 0, FAKE, 1 << 30, None) == 2
-    assert L.rsfp4_mxfp4_linear_from_x(FAKE, 1, 0, 16, 512, FAKE, 1 << 30, FAKE, 0, FAKE, 1 << 30, None) == 2
-    assert L.rsfp4_mxfp4_linear_from_x(FAKE, 1, 2, 16, 100, FAKE, 1 << 30, FAKE, 0, FAKE, 1 << 30, None) == 2
+    assert L.rsfp4_mxfp4_linear_from_x(FAKE, 1, 2, 16, 32800, FAKE, 1 << 30, FAKE, 0, FAKE, 1 << 30, None, 0, None) == 2
+    assert L.rsfp4_mxfp4_linear_from_x(FAKE, 1, 0, 16, 512, FAKE, 1 << 30, FAKE, 0, FAKE, 1 << 30, None, 0, None) == 2
+    assert L.rsfp4_mxfp4_linear_from_x(FAKE, 1, 2, 16, 100, FAKE, 1 << 30, FAKE, 0, FAKE, 1 << 30, None, 0, None) == 2
 
 
 def test_validate_packed_host_checks():

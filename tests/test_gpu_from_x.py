@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 from block_scaled_fp4_act_amd import inputs
-from gpu_util import FMT, _first_diff, check_linear, dev_x
+from gpu_util import FMT, _first_diff, check_linear, dev_x, sample_channels
 
 pytestmark = pytest.mark.gpu
 
@@ -136,8 +136,7 @@ def test_from_x_workload_sampled(wl):
     fmt = FMT[wl.fmt]
     x, W = wl.draw_x(), wl.draw_w()
     y = _run(x, W, fmt, True, x_bf16=wl.bf16)
-    rows = np.sort(np.random.default_rng(5).choice(wl.N, min(wl.N, 128), replace=False))
-    rows[0], rows[-1] = 0, wl.N - 1
+    rows = sample_channels(wl.N, wl.M, 5)
     xin = inputs.round_to_bf16(x) if wl.bf16 else x
     q = oracle.quantize_act(xin, fmt, with_residue=True)
     w = oracle.quantize_weight(W, fmt, rows=rows)

@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 from block_scaled_fp4_act_amd import inputs
-from gpu_util import FMT, check_linear, dev_x, _first_diff
+from gpu_util import FMT, check_linear, dev_x, _first_diff, sample_channels
 
 pytestmark = pytest.mark.gpu
 
@@ -276,8 +276,7 @@ def test_kext_linear_workload_sampled(wl, k):
     x, W = wl.draw_x(), _weights(wl)
     masks = oracle.kext_select(oracle.channel_abs_sum(inputs.calibration_rows(wl)), k)
     y = _kext_pipeline(x, W, fmt, masks, k, wl.bf16)
-    rows = np.sort(np.random.default_rng(9).choice(wl.N, min(wl.N, 128), replace=False))
-    rows[0], rows[-1] = 0, wl.N - 1
+    rows = sample_channels(wl.N, wl.M, 9)
     yo, beta = _oracle_kext(x, W, fmt, masks, k, wl.bf16, rows=rows)
     check_linear(y[:, rows], yo, beta)
 

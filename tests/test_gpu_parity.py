@@ -6,7 +6,7 @@ import pytest
 
 import oracle
 from block_scaled_fp4_act_amd import inputs
-from gpu_util import FMT, assert_quant_equal, check_linear, dev_x
+from gpu_util import FMT, assert_quant_equal, check_linear, dev_x, sample_channels
 
 pytestmark = pytest.mark.gpu
 
@@ -243,12 +243,12 @@ def _workload_cases():
                          ids=lambda v: f"{v.name}_M{v.M}" if hasattr(v, "name") else ("comp" if v else "plain"))
 def test_linear_workload_sampled(wl, comp):
     """Full-size workloads, launched exactly as the bench launches them; the
-    oracle computes a sample of output channels one by one."""
+    oracle computes a sample of output channels one by one (at least 4096
+    outputs of y)."""
     fmt = FMT[wl.fmt]
     x, W = wl.draw_x(), _weights(wl)
     y, _, _ = _run_linear(x, W, fmt, wl.bf16, comp)
-    rows = np.sort(np.random.default_rng(9).choice(wl.N, min(wl.N, 192), replace=False))
-    rows[0], rows[-1] = 0, wl.N - 1
+    rows = sample_channels(wl.N, wl.M, 9)
     xin = inputs.round_to_bf16(x) if wl.bf16 else x
     q = oracle.quantize_act(xin, fmt, with_residue=comp)
     w = oracle.quantize_weight(W, fmt, rows=rows)
