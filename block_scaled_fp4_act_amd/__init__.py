@@ -205,6 +205,17 @@ def nvfp4_linear_compensated(act, w_packed, M, N, K, out=None):
     return _linear(act, w_packed, M, N, K, NVFP4, True, out)
 
 
+def nvfp4_linear_compensated_noalloc(act, w_packed, M, N, K, out):
+    """rsfp4_nvfp4_linear_compensated_noalloc: the compensated NVFP4 linear
+    with the library's own scratch as workspace (no allocation in the call);
+    out: the caller's fp32 [M, N] cuda tensor."""
+    import torch
+    assert out.is_cuda and out.dtype == torch.float32 and out.is_contiguous() and out.numel() >= M * N
+    _check(lib().rsfp4_nvfp4_linear_compensated_noalloc(_ptr(act), act.numel(), _ptr(w_packed), w_packed.numel(),
+                                                        M, N, K, _ptr(out), _stream(act)))
+    return out
+
+
 def mxfp4_linear(act, w_packed, M, N, K, out=None):
     return _linear(act, w_packed, M, N, K, MXFP4, False, out)
 

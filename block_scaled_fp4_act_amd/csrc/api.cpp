@@ -498,6 +498,21 @@ rsfp4_status rsfp4_nvfp4_linear_compensated(const void* act, size_t act_bytes, c
                                             void* ws, size_t ws_bytes, void* stream) {
     return linear(RSFP4_NVFP4, true, act, act_bytes, w_packed, w_packed_bytes, M, N, K, y, false, ws, ws_bytes, stream);
 }
+rsfp4_status rsfp4_nvfp4_linear_compensated_noalloc(const void* act, size_t act_bytes, const void* w_packed,
+                                                    size_t w_packed_bytes, int64_t M, int64_t N, int64_t K,
+                                                    float* y, void* stream) {
+    const size_t need = rsfp4_workspace_bytes(RSFP4_NVFP4, M, N, K, 1);
+    if (need > (size_t)scratch_bytes())
+        return fail(RSFP4_ERR_UNSUPPORTED, "this shape's split needs %zu bytes of workspace; the library's scratch "
+                    "holds %lld (use rsfp4_nvfp4_linear_compensated with a workspace)", need,
+                    (long long)scratch_bytes());
+    void* ws = nullptr;
+    if (need > 0) {
+        const rsfp4_status st = hip_status(scratch_ptr((hipStream_t)stream, &ws), "library scratch");
+        if (st != RSFP4_OK) return st;
+    }
+    return linear(RSFP4_NVFP4, true, act, act_bytes, w_packed, w_packed_bytes, M, N, K, y, false, ws, need, stream);
+}
 rsfp4_status rsfp4_mxfp4_linear(const void* act, size_t act_bytes, const void* w_packed, size_t w_packed_bytes,
                                 int64_t M, int64_t N, int64_t K, float* y, void* ws, size_t ws_bytes,
                                 void* stream) {

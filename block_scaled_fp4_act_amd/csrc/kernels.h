@@ -60,6 +60,12 @@ constexpr int64_t kSplitGroups = 4096;
 constexpr int64_t kSplitCounterBytes = kSplitGroups * 4;
 int64_t split_ws_bytes(const GemmPlan& pl, bool comp, int64_t N);
 
+// The library's per-device scratch (scratch.hip): its size, and its device
+// address on the current device (taken on the first call per device, which
+// also clears the counter area on stream s).
+int64_t scratch_bytes();
+hipError_t scratch_ptr(hipStream_t s, void** out);
+
 // One launch over steps [s_lo, s_hi) of K (s_lo a multiple of 8); accum adds
 // the result to y (the second launch of a K longer than one launch covers).
 // ws: the split plan's workspace (unused when pl.ks == 1); its counters must be

@@ -191,6 +191,22 @@ rsfp4_status rsfp4_mxfp4_linear_compensated(const void* act, size_t act_bytes, c
                                             size_t w_packed_bytes, int64_t M, int64_t N, int64_t K,
                                             float* y, void* ws, size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under stream capture,
+ * tight serving loops, harnesses that forbid allocation): the compensated
+ * NVFP4 linear of rsfp4_nvfp4_linear_compensated, same arguments but no
+ * workspace, same plan and the same bits as that call given a workspace.
+ * Where the plan splits K it uses the library's own scratch, a device array of
+ * 16384 + 4194304 bytes on each GPU (held until the process ends; its address
+ * is taken, and its counter area cleared on `stream`, by the first call on a
+ * device).  It calls no allocator.  Shapes whose split would need more than
+ * the scratch holds are rejected with RSFP4_ERR_UNSUPPORTED (none of the
+ * plans this library makes on a 256-CU device does).  Every call on a GPU
+ * shares that GPU's scratch: calls that may overlap on one GPU (other streams,
+ * other threads) race; calls in stream order do not. */
+rsfp4_status rsfp4_nvfp4_linear_compensated_noalloc(const void* act, size_t act_bytes, const void* w_packed,
+                                                    size_t w_packed_bytes, int64_t M, int64_t N, int64_t K,
+                                                    float* y, void* stream);
+
 /* ------------------------------------------- bf16 output (the same sums) --
  * As the linears above, with y [M, N] stored as bf16 (uint16 bit patterns,
  * 2-byte aligned): the fp32 Fold result rounded to nearest even, as the
