@@ -452,3 +452,16 @@ def unpack_weights_canonical(w_packed, fmt, N, K):
     _check(lib().rsfp4_unpack_weights_canonical(_ptr(w_packed), w_packed.numel(), fmt, N, K, _ptr(codes),
                                                 _ptr(scales), _ptr(s_g), _stream(w_packed)))
     return codes, scales, s_g
+
+
+# ------------------------------------------------------------ measurement --
+
+def stream_read(src, sink=None):
+    """Read the uint8 cuda tensor src once with the library's streaming-read
+    kernel (the reference read rate); sink: a 1-element int32 cuda tensor that
+    the kernel xors the xor of all 32-bit words of src into."""
+    import torch
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=src.device)
+    _check(lib().rsfp4_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream(src)))
+    return sink

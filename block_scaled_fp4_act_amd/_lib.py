@@ -28,6 +28,7 @@ SIGNATURES = {
     "rsfp4_nvfp4_linear": (INT, [P, SZ, P, SZ, I64, I64, I64, P, P, SZ, P]),
     "rsfp4_nvfp4_linear_compensated": (INT, [P, SZ, P, SZ, I64, I64, I64, P, P, SZ, P]),
     "rsfp4_nvfp4_linear_compensated_noalloc": (INT, [P, SZ, P, SZ, I64, I64, I64, P, P]),
+    "rsfp4_stream_read": (INT, [P, SZ, P, P]),
     "rsfp4_mxfp4_linear": (INT, [P, SZ, P, SZ, I64, I64, I64, P, P, SZ, P]),
     "rsfp4_mxfp4_linear_compensated": (INT, [P, SZ, P, SZ, I64, I64, I64, P, P, SZ, P]),
     "rsfp4_unpack_weights_canonical": (INT, [P, SZ, INT, I64, I64, P, P, P, P]),

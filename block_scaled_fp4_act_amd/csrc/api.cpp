@@ -498,6 +498,20 @@ rsfp4_status rsfp4_nvfp4_linear_compensated(const void* act, size_t act_bytes, c
                                             void* ws, size_t ws_bytes, void* stream) {
     return linear(RSFP4_NVFP4, true, act, act_bytes, w_packed, w_packed_bytes, M, N, K, y, false, ws, ws_bytes, stream);
 }
+rsfp4_status rsfp4_stream_read(const void* src, size_t bytes, void* sink, void* stream) {
+    g_err[0] = 0;
+    if (!src || !sink) return fail(RSFP4_ERR_NULL, "src and sink must be non-NULL");
+    if (!aligned(src, 16) || !aligned(sink, 4)) return fail(RSFP4_ERR_ALIGN, "src must be 16- and sink 4-byte aligned");
+    if (bytes % 16 != 0) return fail(RSFP4_ERR_SHAPE, "stream read of %zu bytes: a multiple of 16 is required", bytes);
+    int cus = 0;
+    const rsfp4_status st = num_cus(&cus);
+    if (st != RSFP4_OK) return st;
+    if (bytes > (size_t)cus * ((size_t)1 << 30))
+        return fail(RSFP4_ERR_UNSUPPORTED, "stream read of %zu bytes: at most 1 GiB per compute unit", bytes);
+    return hip_status(launch_stream_read(src, (int64_t)bytes, static_cast<uint32_t*>(sink), cus, (hipStream_t)stream),
+                      "stream read launch");
+}
+
 rsfp4_status rsfp4_nvfp4_linear_compensated_noalloc(const void* act, size_t act_bytes, const void* w_packed,
                                                     size_t w_packed_bytes, int64_t M, int64_t N, int64_t K,
                                                     float* y, void* stream) {

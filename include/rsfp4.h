@@ -473,6 +473,21 @@ rsfp4_status rsfp4_unpack_weights_canonical(const void* w_packed, size_t w_packe
                                             int64_t N, int64_t K, uint8_t* codes, uint8_t* scales,
                                             float* s_g, void* stream);
 
+/* Test/measurement: read `bytes` bytes at src (device memory, 16-byte aligned)
+ * once, at the rate a kernel that only reads achieves (one workgroup of 8
+ * waves per compute unit, each sweeping a contiguous chunk with non-temporal
+ * 16-byte loads, two per wave in flight).  Timed at the byte count of a
+ * linear's weight stream it gives the measured streaming-read ceiling that
+ * the linear's HBM rate is compared with, beside the nominal peak.  The
+ * kernel folds every 32-bit word of the buffer with xor and xors the result
+ * into *sink (4 bytes of device memory, 4-byte aligned; atomically, one
+ * atomic per workgroup), so that the loads cannot be dropped and a caller
+ * that zeroes sink first reads back the xor of the whole buffer.  bytes: a
+ * multiple of 16 (else RSFP4_ERR_SHAPE), at
+ * most 1 GiB per compute unit (else RSFP4_ERR_UNSUPPORTED).  Enqueues one
+ * kernel on `stream`. */
+rsfp4_status rsfp4_stream_read(const void* src, size_t bytes, void* sink, void* stream);
+
 /* Test/debug: check a packed weight blob's 256-byte header against the rules
  * of the layout above (magic, ABI version, format, N and K in range, tensor
  * scale finite and non-negative for NVFP4 and zero for MXFP4, w_packed_bytes
