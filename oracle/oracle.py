@@ -18,6 +18,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "rsfp4_oracle.c")
 _LIB = os.path.join(_HERE, "librsfp4_oracle.so")
+_LIB_OMP = os.path.join(_HERE, "librsfp4_oracle_omp.so")    # timing build: the linear's channels over threads
+FLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
 
 NVFP4, MXFP4 = 0, 1
 BLOCK = {NVFP4: 16, MXFP4: 32}
@@ -27,7 +29,7 @@ __all__ = [
     "e2m1_value", "e2m1_encode_mag", "e4m3_value", "e4m3_encode",
     "e8m0_for_amax", "e8m0_value", "nvfp4_global_scale", "absmax",
     "quantize_act", "quantize_weight", "quantize_weight_rows", "dequant_rows",
-    "linear", "unpack_codes",
+    "linear", "threads", "unpack_codes",
     "channel_abs_sum", "kext_select", "kext_dim", "kext_extend_weight", "kext_quantize_act",
     "nvfp4_alpha", "quantize_row_alg1", "quantize_act_alg1",
     "kv_quantize", "attention_decode",
@@ -35,24 +37,39 @@ __all__ = [
 
 
 def build(force=False):
-    """Compile the oracle with gcc (-O2, no contraction, no fast-math)."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + ".tmp"
-        subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
-                               "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"])
-        os.replace(tmp, _LIB)
+    """Compile the oracle with gcc (-O2, no contraction, no fast-math), and the
+    same source with -fopenmp as the multi-threaded timing build."""
+    for path, extra in ((_LIB, []), (_LIB_OMP, ["-fopenmp"])):
+        if force or not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_SRC):
+            tmp = path + ".tmp"
+            subprocess.check_call(["gcc"] + FLAGS + extra + ["-o", tmp, _SRC, "-lm"])
+            os.replace(tmp, path)
     return _LIB
 
 
 _lib = None
+_lib_omp = None
 
 
-def lib():
-    global _lib
+def lib(threads=False):
+    """The oracle library; threads=True: the OpenMP timing build (same results)."""
+    global _lib, _lib_omp
+    if threads:
+        if _lib_omp is None:
+            if not os.path.exists(_LIB_OMP):
+                build()
+            _lib_omp = _load(_LIB_OMP)
+        return _lib_omp
     if _lib is None:
         if not os.path.exists(_LIB):
             build()
-        L = ctypes.CDLL(_LIB)
+        _lib = _load(_LIB)
+    return _lib
+
+
+def _load(path):
+    L = ctypes.CDLL(path)
+    if True:
         f32, u8, i64, i32, dbl = ctypes.c_float, ctypes.c_uint8, ctypes.c_int64, ctypes.c_int, ctypes.c_double
         P = ctypes.c_void_p
         L.oracle_e2m1_value.restype, L.oracle_e2m1_value.argtypes = f32, [u8]
@@ -88,8 +105,8 @@ def lib():
         L.oracle_quantize_act_alg1.argtypes = [P, i64, i64, f32, i32, P, P, P, P, P, P]
         L.oracle_attention_decode.restype = None
         L.oracle_attention_decode.argtypes = [P, P, P, P, i64, i64, i64, i64, dbl, P, P]
-        _lib = L
-    return _lib
+        L.oracle_threads.restype, L.oracle_threads.argtypes = i32, []
+        return L
 
 
 def _p(a):
@@ -155,20 +172,21 @@ def quantize_act(x, fmt, with_residue=True):
     return {"codes": codes, "scales": scales, "globals": globs, "deq": deq, "resid": resid}
 
 
-def quantize_weight_rows(W_rows, fmt, s_gw=0.0, want_deq=True):
-    """Quantize weight rows W_rows[n, K] with a given NVFP4 tensor scale s_gw."""
+def quantize_weight_rows(W_rows, fmt, s_gw=0.0, want_deq=True, threads=False):
+    """Quantize weight rows W_rows[n, K] with a given NVFP4 tensor scale s_gw
+    (threads=True: the OpenMP timing build, the same bits)."""
     W_rows = _f32(W_rows)
     n, K = W_rows.shape
     blk = BLOCK[fmt]
     codes = np.zeros((n, K // 2), np.uint8)
     scales = np.zeros((n, K // blk), np.uint8)
     deq = np.zeros((n, K), np.float32) if want_deq else None
-    lib().oracle_quantize_weight_rows(fmt, _p(W_rows), n, K, float(s_gw), _p(codes), _p(scales),
-                                      _p(deq) if want_deq else None)
+    lib(threads).oracle_quantize_weight_rows(fmt, _p(W_rows), n, K, float(s_gw), _p(codes), _p(scales),
+                                             _p(deq) if want_deq else None)
     return {"codes": codes, "scales": scales, "deq": deq}
 
 
-def quantize_weight(W, fmt, rows=None, want_deq=True):
+def quantize_weight(W, fmt, rows=None, want_deq=True, threads=False):
     """Quantize a weight tensor W[N, K] (NVFP4: one tensor scale from max|W|).
 
     rows: optional index array; only those rows are quantized (the tensor scale
@@ -177,7 +195,7 @@ def quantize_weight(W, fmt, rows=None, want_deq=True):
     W = _f32(W)
     s_gw = nvfp4_global_scale(absmax(W)) if fmt == NVFP4 else 0.0
     sub = W if rows is None else W[np.asarray(rows)]
-    out = quantize_weight_rows(sub, fmt, s_gw, want_deq)
+    out = quantize_weight_rows(sub, fmt, s_gw, want_deq, threads)
     out["s_g"] = np.float32(s_gw)
     return out
 
@@ -209,17 +227,23 @@ def dequant_rows(codes, scales, globals_, fmt, K):
     return (np.repeat(st, blk, axis=1) * e).astype(np.float32)
 
 
-def linear(dx, dw, M, compensated, want_beta=True):
+def linear(dx, dw, M, compensated, want_beta=True, threads=False):
     """fp64 linear over dequantized rows: dx [R, K] stacked (R = 2M when
-    compensated), dw [N, K].  Returns (y [M, N] f64, beta [M, N] f64)."""
+    compensated), dw [N, K].  Returns (y [M, N] f64, beta [M, N] f64).
+    threads=True runs the OpenMP timing build (the same bits)."""
     dx = _f32(dx)
     dw = _f32(dw)
     N, K = dw.shape
     y = np.zeros((M, N), np.float64)
     beta = np.zeros((M, N), np.float64) if want_beta else None
-    lib().oracle_linear(_p(dx), _p(dw), M, N, K, 1 if compensated else 0, _p(y),
-                        _p(beta) if want_beta else None)
+    lib(threads).oracle_linear(_p(dx), _p(dw), M, N, K, 1 if compensated else 0, _p(y),
+                               _p(beta) if want_beta else None)
     return y, beta
+
+
+def threads():
+    """Threads the OpenMP timing build uses."""
+    return int(lib(True).oracle_threads())
 
 
 # ---------------------------------------------------------------- K-Ext --

@@ -54,6 +54,9 @@
  * The encoders are written as exhaustive nearest-value searches over the code
  * tables (not as bit manipulation), so they stay independent of any fast encoder.
  */
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 #include <math.h>
 #include <stdint.h>
 #include <stddef.h>
@@ -290,6 +293,8 @@ ORACLE_API void oracle_quantize_weight_rows(int fmt, const float* W, int64_t nro
                                             float s_gw, uint8_t* codes, uint8_t* scales,
                                             float* deq) {
     int64_t blk = fmt == 0 ? 16 : 32;
+    /* rows are independent given the tensor scale (threads: timing build only) */
+#pragma omp parallel for schedule(static)
     for (int64_t n = 0; n < nrows; ++n) {
         float* drow = deq ? deq + n * K : (float*)0;
         if (fmt == 0)
@@ -311,6 +316,10 @@ ORACLE_API void oracle_linear(const float* dx, const float* dw, int64_t M, int64
     for (int64_t m = 0; m < M; ++m) {
         const float* xb = dx + m * K;
         const float* xr = compensated ? dx + (M + m) * K : (const float*)0;
+        /* Every output is its own sum, so the channels may be spread over
+         * threads (only the timing build enables OpenMP; results are the
+         * same bits either way). */
+#pragma omp parallel for schedule(static)
         for (int64_t n = 0; n < N; ++n) {
             const float* w = dw + n * K;
             double acc = 0.0, mag = 0.0;
@@ -537,4 +546,14 @@ ORACLE_API void oracle_attention_decode(const float* qb, const float* qr, const 
         }
         for (int64_t i = 0; i < d; ++i) out[h * d + i] /= den;
     }
+}
+
+/* Threads the OpenMP timing build runs its parallel loops with (1 in the
+ * plain build). */
+ORACLE_API int oracle_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
 }

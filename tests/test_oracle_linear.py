@@ -149,3 +149,21 @@ def test_tiny_grid_bruteforce_error_order(orc):
             e_plain = np.abs(x.astype(np.float64) - q["deq"][0])
             e_comp = np.abs(x.astype(np.float64) - q["deq"][0] - q["deq"][1])
             assert (e_comp <= e_plain).all()
+
+
+def test_threaded_timing_build_same_bits(orc):
+    """The OpenMP timing build of the oracle (the linear's channels and the
+    weight rows spread over threads) returns the plain build's bits."""
+    rng = np.random.default_rng(17)
+    x = inputs.activations(3, 1024, 5, 0.01, 20.0, 6, True)
+    W = inputs.weights(96, 1024, 8)
+    for fmt in (0, 1):
+        q = orc.quantize_act(x, fmt, True)
+        w1 = orc.quantize_weight(W, fmt)
+        w8 = orc.quantize_weight(W, fmt, threads=True)
+        assert np.array_equal(w1["codes"], w8["codes"]) and np.array_equal(w1["scales"], w8["scales"])
+        y1, b1 = orc.linear(q["deq"], w1["deq"], 3, True)
+        y8, b8 = orc.linear(q["deq"], w8["deq"], 3, True, threads=True)
+        assert np.array_equal(y1, y8) and np.array_equal(b1, b8)
+    assert orc.threads() >= 1
+    del rng
