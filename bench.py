@@ -5,22 +5,26 @@ quantize + residue and the compensated linear, as the library's one-call entry
 runs them (weights are prepacked once, offline, as the method prescribes):
 the quantize kernel followed by the linear, or, for few rows to quantize, one
 launch of the linear that quantizes its rows in every workgroup.  The headline
-workload is the attention projection: NVFP4, M = 4 token rows, K = N = 4096,
-x in bf16.  Steps rotate over distinct weight copies (> 2x the 256 MB Infinity
-Cache) so every step streams its weights from HBM, and are replayed from a HIP
-graph so host launch cost does not enter the timing.  Every figure is the
-median of five timed replays of its graph (the headline also gives their
-minimum and maximum); by default the headline step is also timed in three
-fresh processes before this one starts, with their median and spread.
+workload is the large-MLP projection: NVFP4, M = 8 token rows, K = 8192,
+N = 28672, x in bf16 (the HBM-bound decode shape).  Steps rotate over distinct
+weight copies (> 2x the 256 MB Infinity Cache) so every step streams its
+weights from HBM, and are replayed from a HIP graph so host launch cost does
+not enter the timing.  Every figure is the median of five timed replays of its
+graph (the headline also gives their minimum and maximum); by default the
+headline step is also timed in three fresh processes before this one starts,
+with their median and spread.
 
-Prints ONE JSON line.  Extra keys: the uncompensated (plain W4A4) pair and the
-compensation overhead, per-kernel averages, NMSE against the fp32 product, the
-roofline of the dominant kernel, the oracle timed on the host cores, a sweep
-over the other decode workloads, selective compensation (K-Ext) at
-rho = 0.125 / 0.25 / 0.5 on the prefill-sized operands beside their plain and
-full-residue steps, and compensated decode attention (ResAttn) over the paged
-NVFP4 KV cache at decode shapes of the page's Figure 10, and the grouped
-(mixture of experts) linear beside one linear launch per expert.
+Prints ONE JSON line.  Beside the headline: the roofline of its dominant
+kernel (the linear) against the nominal 8 TB/s and against the streaming-read
+rate of the same byte count measured with the library's read kernel, the
+uncompensated (plain W4A4) step and the compensation overhead, per-kernel
+averages, NMSE against the binary64 product of the bf16 activations and fp32
+weights, the oracle timed on the host cores (one thread and all threads), and
+a sweep over every workload (each with its NMSE, read ceiling and, from 64
+rows, its fraction of the matrix-core peak); then selective compensation
+(K-Ext) at rho = 0.125 / 0.25 / 0.5 on the prefill-sized operands, compensated
+decode attention (ResAttn) at decode shapes of the page's Figure 10, and the
+grouped (mixture of experts) linear.
 """
 import argparse
 import hashlib
@@ -37,8 +41,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_PEAK_TFLOPS = {0: 2500.0, 1: 10100.0}   # dense: f16 (NVFP4 runs exact f16 products), FP4 (MXFP4)
 ROTATE_BYTES = 512 << 20       # distinct weight bytes per timed loop (2x the MALL)
 
+HEADLINE_M = 8                 # token rows of the headline (large-MLP shape)
 METRIC = "compensated FP4 linear µs/call + HBM GB/s (% of peak) at M=1–8, K,N≥4096"
 
 # HBM traffic of the dominant kernel (compensated NVFP4 linear at the headline
@@ -47,11 +53,11 @@ METRIC = "compensated FP4 linear µs/call + HBM GB/s (% of peak) at M=1–8, K,N
 # calibration factors (FETCH_SIZE x2.0, WRITE_SIZE x1.0).  Valid only for the
 # kernel sources whose hash is recorded; reported as null otherwise.
 TRAFFIC = {
-    "sources_sha256": "239438bc818f97541c14dac8fac552ec084bb66e9cff2edbe4fd5dfe737b7e45",
-    "fetch_bytes": 2.0 * 4725 * 1024,   # FETCH_SIZE 4725 KiB per launch
-    "write_bytes": 1.0 * 64 * 1024,     # WRITE_SIZE 64 KiB per launch
+    "sources_sha256": None,
+    "fetch_bytes": None,
+    "write_bytes": None,
 }
-KERNEL_SOURCES = ["gemm.hip", "layout.h", "codec.h", "fp4_frag.h", "quant_row.h"]
+KERNEL_SOURCES = ["gemm.hip", "layout.h", "codec.h", "fp4_frag.h", "quant_row.h", "kernels.h"]
 
 
 def kernel_sources_sha256():
@@ -90,14 +96,16 @@ def step_bytes(fmt, M, N, K, comp, x_elem):
 class Setup:
     """Device buffers for one workload: R rotated weight copies and inputs."""
 
-    def __init__(self, rs, torch, fmt, M, N, K, x_np, W_dev, comp_rows=True):
+    def __init__(self, rs, torch, fmt, M, N, K, x_np, W_dev, bf16=True):
         self.rs, self.torch = rs, torch
         self.fmt, self.M, self.N, self.K = fmt, M, N, K
         blob = rs.prepack_weights(W_dev, fmt)
         wbytes = blob.numel()
         self.R = max(2, int(math.ceil(ROTATE_BYTES / wbytes)))
         self.blobs = [blob] + [blob.clone() for _ in range(self.R - 1)]
-        x = torch.from_numpy(x_np).cuda().to(torch.bfloat16)
+        x = torch.from_numpy(x_np).cuda()
+        if bf16:
+            x = x.to(torch.bfloat16)
         self.xs = [x.clone() for _ in range(self.R)]
         nb = rs.packed_act_bytes(fmt, M, K, True)
         self.acts = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(self.R)]
@@ -159,7 +167,8 @@ def run_kext(rs, torch, wl, M, ks, steps, warmup):
     beside the plain and full-residue steps of the same workload."""
     from block_scaled_fp4_act_amd import inputs
     fmt = 0 if wl.fmt == "nvfp4" else 1
-    base, S, x = run_workload(rs, torch, wl, M, steps, warmup, want_plain=True, want_kernels=False)
+    base, S, x = run_workload(rs, torch, wl, M, steps, warmup, want_plain=True, want_kernels=False,
+                              want_nmse=False)
     del S
     torch.cuda.empty_cache()
     gen = torch.Generator(device="cuda").manual_seed(wl.w_seed)
@@ -185,7 +194,7 @@ def run_kext(rs, torch, wl, M, ks, steps, warmup):
     return out
 
 
-def paper_numerics_step(rs, torch, S, ref, steps, warmup):
+def paper_numerics_step(rs, torch, S, steps, warmup):
     """The headline step with the page's operator numerics: the tensor scale
     alpha computed once from the batch (calibration-like, outside the timing),
     the shared-alpha multiplier-scale quantizer and the compensated linear with
@@ -205,9 +214,10 @@ def paper_numerics_step(rs, torch, S, ref, steps, warmup):
     t = time_graph(torch, step, steps, warmup)
     tq = time_graph(torch, quant, steps, warmup)
     step(0)
-    y = ys[0].float().cpu().numpy()
+    y = ys[0].double()
+    e = float(((y - S.ref) ** 2).sum()) / float((S.ref * S.ref).sum())
     return {"us_per_call": round(t * 1e3, 3), "quant_us": round(tq * 1e3, 3),
-            "nmse_comp_bf16": round(nmse(y, ref), 6), "alpha": float(alpha.item()),
+            "nmse_comp_bf16": round(e, 6), "alpha": float(alpha.item()),
             "what": "shared tensor scale alpha, multiplier-scale quantizer, bf16 output"}
 
 
@@ -344,24 +354,59 @@ def time_graph(torch, fn, steps, warmup, stats=None):
     return per[len(per) // 2]
 
 
-def nmse(y, ref):
-    return float(((y - ref) ** 2).sum() / (ref ** 2).sum())
+_READ_PEAK = {}
 
 
-def run_workload(rs, torch, wl, M, steps, warmup, want_plain=True, want_kernels=True, W_np=None):
-    from block_scaled_fp4_act_amd import inputs
+def read_peak_gbps(rs, torch, nbytes, steps=20, warmup=3):
+    """Streaming-read rate (GB/s) of the library's read kernel at a byte
+    count, over rotated buffers (>= 512 MB in all) as the linear's weights."""
+    if nbytes in _READ_PEAK:
+        return _READ_PEAK[nbytes]
+    nb = (nbytes + 255) // 256 * 256
+    nread = (nbytes + 15) // 16 * 16       # the kernel reads whole 16-byte groups
+    R = max(2, int(math.ceil(ROTATE_BYTES / nb)))
+    buf = torch.empty(R * nb, dtype=torch.uint8, device="cuda")
+    buf.fill_(0x5A)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    parts = [buf[r * nb: r * nb + nread] for r in range(R)]
+    t = time_graph(torch, lambda i: rs.stream_read(parts[i % R], sink), steps, warmup)
+    del buf, parts
+    torch.cuda.empty_cache()
+    _READ_PEAK[nbytes] = nread / (t * 1e-3) / 1e9
+    return _READ_PEAK[nbytes]
+
+
+def weight_bytes(fmt, N, K):
+    return N * K // 2 + N * K // blk(fmt) + (4 if fmt == 0 else 0)
+
+
+def run_workload(rs, torch, wl, M, steps, warmup, want_plain=True, want_kernels=True, want_nmse=True):
+    """One workload at M rows: the whole step (one call from x), the linear and
+    the quantizer alone, the plain step, NMSE against the binary64 product of
+    the (bf16) activations and the fp32 weights, the streaming-read rate at
+    the weight bytes and, from 64 rows, the linear's fraction of the matrix-
+    core peak.  W ~ N(0, 0.02^2) is drawn on the device (seeded)."""
     fmt = 0 if wl.fmt == "nvfp4" else 1
     wlm = wl.with_m(M)
     x = wlm.draw_x()
-    if W_np is not None:
-        W_dev = torch.from_numpy(W_np).cuda()
-    else:  # sweep timing only: same distribution drawn on the device
-        gen = torch.Generator(device="cuda").manual_seed(wl.w_seed)
-        W_dev = torch.randn((wl.N, wl.K), generator=gen, device="cuda", dtype=torch.float32) * 0.02
-    S = Setup(rs, torch, fmt, M, wl.N, wl.K, x, W_dev)
+    gen = torch.Generator(device="cuda").manual_seed(wl.w_seed)
+    W_dev = torch.randn((wl.N, wl.K), generator=gen, device="cuda", dtype=torch.float32) * 0.02
+    S = Setup(rs, torch, fmt, M, wl.N, wl.K, x, W_dev, bf16=wl.bf16)
+    nm = {}
+    if want_nmse:
+        xd = S.xs[0].double()
+        ref = xd @ W_dev.double().T
+        den = float((ref * ref).sum())
+        for comp in (True, False):
+            rs.quantize_act_with_residue(S.xs[0], fmt, comp, out=S.acts[0])
+            f = rs.fp4_linear_compensated if comp else rs.fp4_linear
+            y = f(S.acts[0], S.blobs[0], M, wl.N, wl.K, fmt).double()
+            nm["nmse_comp" if comp else "nmse_plain"] = float(((y - ref) ** 2).sum()) / den
+        S.ref = ref
+        del xd, y
     del W_dev
     out = {"workload": wl.name, "format": wl.fmt, "M": M, "K": wl.K, "N": wl.N, "rotation": S.R}
-    sb = step_bytes(fmt, M, wl.N, wl.K, True, 2)
+    sb = step_bytes(fmt, M, wl.N, wl.K, True, 2 if wl.bf16 else 4)
     st = {}
     t_comp = time_graph(torch, lambda i: S.step(i, True), steps, warmup, stats=st)
     out["us_per_call"] = t_comp * 1e3
@@ -394,6 +439,14 @@ def run_workload(rs, torch, wl, M, steps, warmup, want_plain=True, want_kernels=
             t_gp = time_graph(torch, lambda i: S.gemm(i, False), steps, warmup)
             out["plain_gemm_us"] = t_gp * 1e3
     out["step_GBps_frac"] = out["GBps"] / HBM_PEAK_GBS
+    out.update(nm)
+    if want_kernels:
+        rp = read_peak_gbps(rs, torch, weight_bytes(fmt, wl.N, wl.K))
+        out["read_peak_GBps"] = rp
+        out["gemm_frac_of_read_peak"] = out["gemm_GBps"] / rp
+        if M >= 64:
+            out["mfma_frac"] = out["gemm_TFLOPs"] / MFMA_PEAK_TFLOPS[fmt]
+            out["mfma_peak_TFLOPs"] = MFMA_PEAK_TFLOPS[fmt]
     return out, S, x
 
 
@@ -410,38 +463,13 @@ def host_info():
     return {"cpu": model, "nproc": os.cpu_count()}
 
 
-def read_peak_gbps(torch, nbytes=1 << 30, reps=10):
-    """Streaming-read rate of the box, for context beside the nominal peak: the
-    best of a few plain device reductions over a 1 GiB fp32 tensor (full sum,
-    row sums, row maxima).  Returns (GB/s, which)."""
-    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
-    x2 = x.view(-1, 8192)
-    ops = {"sum": lambda: x.sum(), "row_sum": lambda: x2.sum(dim=1), "row_amax": lambda: x2.amax(dim=1)}
-    best, which = 0.0, None
-    for name, op in ops.items():
-        for _ in range(3):
-            op()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            op()
-        e1.record()
-        torch.cuda.synchronize()
-        gbs = nbytes / (e0.elapsed_time(e1) * 1e-3 / reps) / 1e9
-        if gbs > best:
-            best, which = gbs, name
-    del x, x2
-    torch.cuda.empty_cache()
-    return best, which
-
-
 def pmc_launches(rs, torch):
     """Eager launches for hardware-counter passes (no graphs): a 256 MiB device
-    copy three times (calibration: known bytes read and written), then six
-    quantize and six compensated NVFP4 linear launches at the headline shape
-    over distinct weight copies."""
+    copy three times (calibration: known bytes read and written), then, for
+    each narrow workload (the attention projection, the MLP pair, the
+    large-MLP shape and the MXFP4 shape, all compensated, M = 4 or 8), three
+    quantize launches and three linear launches over distinct weight copies.
+    Each case prints its algorithmic bytes before its launches."""
     from block_scaled_fp4_act_amd import inputs
     a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
     b = torch.empty_like(a)
@@ -449,16 +477,26 @@ def pmc_launches(rs, torch):
         b.copy_(a)
     torch.cuda.synchronize()
     del a, b
-    wl = inputs.ATTN
-    S = Setup(rs, torch, 0, wl.M, wl.N, wl.K, wl.draw_x(), torch.from_numpy(wl.draw_w()).cuda())
-    for i in range(6):
-        S.quant(i, True)
-    torch.cuda.synchronize()
-    for i in range(6):
-        S.gemm(i, True)
-    torch.cuda.synchronize()
-    print(json.dumps({"pmc_launches": "done", "copy_bytes": 256 << 20,
-                      "linear_algorithmic_bytes": gemm_bytes(0, wl.M, wl.N, wl.K, True)}), flush=True)
+    print(json.dumps({"pmc_launches": "copy", "copy_bytes": 256 << 20, "launches": 3}), flush=True)
+    cases = [(inputs.ATTN, inputs.ATTN.M), (inputs.MLP_UP, 8), (inputs.MLP_DOWN, 8),
+             (inputs.LARGE_MLP, HEADLINE_M), (inputs.MX, 8)]
+    for wl, M in cases:
+        fmt = 0 if wl.fmt == "nvfp4" else 1
+        gen = torch.Generator(device="cuda").manual_seed(wl.w_seed)
+        W_dev = torch.randn((wl.N, wl.K), generator=gen, device="cuda", dtype=torch.float32) * 0.02
+        S = Setup(rs, torch, fmt, M, wl.N, wl.K, wl.with_m(M).draw_x(), W_dev, bf16=wl.bf16)
+        del W_dev
+        torch.cuda.synchronize()
+        print(json.dumps({"pmc_launches": wl.name, "M": M, "format": wl.fmt, "launches": "3 quantize, 3 linear",
+                          "linear_algorithmic_bytes": gemm_bytes(fmt, M, wl.N, wl.K, True)}), flush=True)
+        for i in range(3):
+            S.quant(i, True)
+        torch.cuda.synchronize()
+        for i in range(3):
+            S.gemm(i, True)
+        torch.cuda.synchronize()
+        del S
+        torch.cuda.empty_cache()
 
 
 def pmc_paths(rs, torch):
@@ -504,28 +542,80 @@ def pmc_paths(rs, torch):
           flush=True)
 
 
-def cpu_baseline(wl, x, W, budget_s=12.0, max_calls=100000):
-    """The oracle (plain single-threaded C, fp64 accumulation) timed on the
-    host: quantize + compensated linear per call, weights quantized beforehand
-    as on the GPU.  Bounded: calls until ~budget_s seconds."""
-    import oracle
-    fmt = 0 if wl.fmt == "nvfp4" else 1
-    w = oracle.quantize_weight(W, fmt)
-    dw = w["deq"]
-    n, t0 = 0, time.perf_counter()
+GCC_FLAGS = "gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math (-fopenmp for the all-threads build)"
+CPU_SLICE = 1024        # output channels of the one-thread sample (extrapolated to N)
+
+
+def _cpu_call_time(oracle, x, dw, fmt, M, comp, threads, min_s=0.5, max_calls=50):
+    """Median seconds of the oracle's two parts of one call -- quantize the
+    rows, then the compensated linear over the pre-quantized weights dw --
+    over repeated calls.  Returns (quantize s, linear s, calls)."""
+    tq, tl = [], []
+    t_all = time.perf_counter()
     while True:
-        q = oracle.quantize_act(x, fmt, True)
-        oracle.linear(q["deq"], dw, x.shape[0], True, want_beta=False)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or n >= max_calls:
+        t0 = time.perf_counter()
+        q = oracle.quantize_act(x, fmt, comp)
+        t1 = time.perf_counter()
+        oracle.linear(q["deq"], dw, M, comp, want_beta=False, threads=threads)
+        tq.append(t1 - t0)
+        tl.append(time.perf_counter() - t1)
+        if (time.perf_counter() - t_all >= min_s and len(tq) >= 3) or len(tq) >= max_calls:
             break
-    per_call = el / n
-    sb = step_bytes(fmt, x.shape[0], W.shape[0], W.shape[1], True, 2)
-    return {"value": sb / per_call / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "us_per_call": per_call * 1e6, "host": host_info(),
-            "sample": f"{n} full calls of the {wl.name} compensated step (quantize + linear, "
-                      f"weights pre-quantized), single thread, {el:.1f} s"}
+    tq.sort()
+    tl.sort()
+    return tq[len(tq) // 2], tl[len(tl) // 2], len(tq)
+
+
+def cpu_baseline(cases):
+    """The oracle (plain C, binary64 accumulation, -O2 without contraction)
+    timed on the host: activation quantize + compensated linear per call,
+    weights quantized beforehand as on the GPU.  Two legs per workload: all
+    threads of the OpenMP timing build (the full call where M <= 8; else the
+    quantize in full and the linear over a CPU_SLICE-channel slice, scaled to
+    N), and one thread (the quantize in full and the linear over the slice,
+    scaled to N).  cases: [(workload, [M, ...])].  Returns the per-workload
+    table and the seconds it took."""
+    import oracle
+    from block_scaled_fp4_act_amd import inputs
+    oracle.build()
+    nthr = oracle.threads()
+    rows = []
+    t_start = time.perf_counter()
+    for wl, ms in cases:
+        fmt = 0 if wl.fmt == "nvfp4" else 1
+        W = inputs.weights(wl.N, wl.K, wl.w_seed)
+        sl = np.arange(min(CPU_SLICE, wl.N))
+        full_needed = any(m <= 8 for m in ms)
+        w = oracle.quantize_weight(W, fmt, rows=None if full_needed else sl, threads=True)
+        del W
+        dw_all = w["deq"] if full_needed else None
+        dw_sl = np.ascontiguousarray(w["deq"][sl]) if full_needed else w["deq"]
+        del w
+        x_all = wl.with_m(max(ms)).draw_x()
+        for M in ms:
+            x = np.ascontiguousarray(x_all[:M])
+            if M <= 8:
+                q_all, l_all, n_all = _cpu_call_time(oracle, x, dw_all, fmt, M, True, True)
+                t_all = q_all + l_all
+                all_label = "full call"
+            else:
+                q_all, l_sl, n_all = _cpu_call_time(oracle, x, dw_sl, fmt, M, True, True)
+                t_all = q_all + l_sl * wl.N / len(sl)
+                all_label = f"quantize in full, linear over {len(sl)} channels extrapolated to N = {wl.N}"
+            q_one, l_one, n_one = _cpu_call_time(oracle, x, dw_sl, fmt, M, True, False, min_s=0.3, max_calls=10)
+            t_one = q_one + l_one * wl.N / len(sl)
+            sb = step_bytes(fmt, M, wl.N, wl.K, True, 2 if wl.bf16 else 4)
+            rows.append({"workload": wl.name, "format": wl.fmt, "M": M, "K": wl.K, "N": wl.N,
+                         "all_threads": {"us_per_call": round(t_all * 1e6, 1), "GBps": round(sb / t_all / 1e9, 4),
+                                         "threads": nthr, "sample": f"{all_label}, median of {n_all} calls"},
+                         "one_thread": {"us_per_call": round(t_one * 1e6, 1), "GBps": round(sb / t_one / 1e9, 4),
+                                        "threads": 1, "sample": f"quantize in full, linear over {len(sl)} channels "
+                                                                f"extrapolated to N = {wl.N}, median of {n_one} "
+                                                                "calls"}})
+            print(f"oracle timing {wl.name} M={M}: {t_all * 1e6:.0f} us ({nthr} threads), "
+                  f"{t_one * 1e6:.0f} us (1 thread)", file=sys.stderr, flush=True)
+        del dw_all, dw_sl
+    return rows, time.perf_counter() - t_start
 
 
 def cross_process(n, steps, warmup):
@@ -614,22 +704,13 @@ def main():
             print(json.dumps({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}), flush=True)
         return
 
-    wl = inputs.ATTN
-    W = wl.draw_w()
-    head, S, x = run_workload(rs, torch, wl, wl.M, args.steps, args.warmup,
-                              want_plain=not args.only_headline, want_kernels=not args.only_headline,
-                              W_np=W)
+    wl = inputs.LARGE_MLP.with_m(HEADLINE_M)
     fmt = 0
-    # precision against the fp32 product of the bf16 activations and fp32 weights
-    xr = inputs.round_to_bf16(x).astype(np.float64)
-    ref = xr @ W.astype(np.float64).T
-    yc = rs.fp4_linear_compensated(S.acts[0], S.blobs[0], wl.M, wl.N, wl.K, fmt).cpu().numpy()
-    rs.quantize_act_with_residue(S.xs[0], fmt, True, out=S.acts[0])
-    yp = rs.fp4_linear(S.acts[0], S.blobs[0], wl.M, wl.N, wl.K, fmt).cpu().numpy()
-    head["nmse_comp"] = nmse(yc, ref)
-    head["nmse_plain"] = nmse(yp, ref)
-    if not args.only_headline:
-        head["paper_numerics"] = paper_numerics_step(rs, torch, S, ref, args.steps, args.warmup)
+    lite = args.only_headline
+    head, S, x = run_workload(rs, torch, wl, wl.M, args.steps, args.warmup,
+                              want_plain=not lite, want_kernels=not lite, want_nmse=not lite)
+    if not lite:
+        head["paper_numerics"] = paper_numerics_step(rs, torch, S, args.steps, args.warmup)
     del S
     torch.cuda.empty_cache()
 
@@ -641,37 +722,54 @@ def main():
         traffic = None
         if TRAFFIC["sources_sha256"] is not None and TRAFFIC["sources_sha256"] == kernel_sources_sha256():
             traffic = TRAFFIC["fetch_bytes"] + TRAFFIC["write_bytes"]
+        rp = head["read_peak_GBps"]
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": "gemm_small_kernel (compensated NVFP4 linear)",
-                "algorithmic_bytes_per_launch": gb}
+                "algorithmic_bytes_per_launch": gb,
+                "measured_read_peak": round(rp, 1),
+                "measured_read_peak_by": (f"stream_read_kernel over {weight_bytes(fmt, wl.N, wl.K)} bytes "
+                                          "(the weight bytes), rotated buffers, HIP graph"),
+                "frac_of_measured_read_peak": round(ach / rp, 4)}
 
-    sweep, grouped = [], []
-    if not args.no_sweep and not args.only_headline:
-        cases = [(inputs.MLP_UP, 8), (inputs.MLP_DOWN, 8)]
+    sweep, grouped, kext, attn = [], [], [], []
+    if not args.no_sweep and not lite:
+        cases = [(inputs.SMALL, 1), (inputs.ATTN, inputs.ATTN.M), (inputs.MLP_UP, 8), (inputs.MLP_DOWN, 8)]
         cases += [(inputs.LARGE_MLP, m) for m in inputs.LARGE_MLP_M]
         cases += [(inputs.MX, m) for m in inputs.MX_M]
         for w, m in cases:
-            r, S2, _ = run_workload(rs, torch, w, m, min(args.steps, 100), min(args.warmup, 10))
-            del S2
-            torch.cuda.empty_cache()
-            sweep.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()})
+            if w is inputs.LARGE_MLP and m == HEADLINE_M:
+                r = head
+            else:
+                r, S2, _ = run_workload(rs, torch, w, m, min(args.steps, 100), min(args.warmup, 10))
+                del S2
+                torch.cuda.empty_cache()
+            sweep.append({k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()
+                          if k != "paper_numerics"})
+            print(f"sweep {w.name} M={m}: {r['us_per_call']:.2f} us", file=sys.stderr, flush=True)
         attn = [run_attn(rs, torch, c, min(args.steps, 50), min(args.warmup, 5)) for c in ATTN_CASES]
         grouped = [run_grouped(rs, torch, c, min(args.steps, 100), min(args.warmup, 10)) for c in GROUPED_CASES]
         # selective compensation (prefill-sized operands): rho = 0.125, 0.25, 0.5
-        kext = []
         for w, m in ((inputs.LARGE_MLP, 128), (inputs.MX, 256)):
             kext.append(run_kext(rs, torch, w, m, inputs.KEXT_K, min(args.steps, 100), min(args.warmup, 10)))
 
-    if roof is not None and not args.only_headline:
-        rp, which = read_peak_gbps(torch)
-        roof["measured_read_peak"] = round(rp, 1)
-        roof["measured_read_peak_by"] = f"torch {which} over 1 GiB"
-        roof["frac_of_measured_read_peak"] = round(roof["achieved"] / rp, 4)
-
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, inputs.round_to_bf16(x), W)
+        cases = [(wl, [HEADLINE_M])]
+        if not args.no_sweep and not lite:
+            cases = [(inputs.SMALL, [1]), (inputs.ATTN, [inputs.ATTN.M]), (inputs.MLP_UP, [8]),
+                     (inputs.MLP_DOWN, [8]), (inputs.LARGE_MLP, list(inputs.LARGE_MLP_M)),
+                     (inputs.MX, list(inputs.MX_M))]
+        table, secs = cpu_baseline(cases)
+        hrow = [r for r in table if r["workload"] == wl.name and r["M"] == HEADLINE_M][0]
+        cpu = {"value": hrow["all_threads"]["GBps"], "unit": "GB/s", "cores": hrow["all_threads"]["threads"],
+               "kind": "oracle",
+               "sample": (f"{wl.name} M={HEADLINE_M}: {hrow['all_threads']['sample']} (activation quantize + "
+                          "compensated linear over pre-quantized weights), OpenMP timing build"),
+               "us_per_call": hrow["all_threads"]["us_per_call"],
+               "one_thread": hrow["one_thread"],
+               "host": host_info(), "gcc": GCC_FLAGS,
+               "per_workload": table, "seconds": round(secs, 1)}
 
     line = {
         "metric": METRIC,
@@ -699,8 +797,8 @@ def main():
     if procs is not None:
         line["headline_processes"] = procs
     for k in ("launches", "plain_launches", "plain_us_per_call", "comp_overhead", "plain_two_launch_us_per_call",
-              "comp_overhead_two_launch",
-              "gemm_us", "plain_gemm_us", "quant_us", "gemm_GBps", "nmse_comp", "nmse_plain", "paper_numerics"):
+              "comp_overhead_two_launch", "gemm_us", "plain_gemm_us", "quant_us", "gemm_GBps",
+              "read_peak_GBps", "gemm_frac_of_read_peak", "nmse_comp", "nmse_plain", "paper_numerics"):
         if k in head:
             line[k] = round(head[k], 6) if isinstance(head[k], float) else head[k]
     line["step_hbm_frac"] = round(head["GBps"] / HBM_PEAK_GBS, 4)
