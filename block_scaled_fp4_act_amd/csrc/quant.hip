@@ -202,58 +202,28 @@ hipError_t launch_kext_f(const void* x, int M, int64_t K, const uint8_t* masks, 
 }
 
 // ------------------------------------------------- paper numerics (alpha) --
-// The operator of the page's fused quantizer (Appendix B.2, Eq. 8 and
-// Algorithm 1), NVFP4: one tensor scale alpha for the whole activation tensor,
-// read from device memory (static or calibrated; rsfp4_nvfp4_tensor_alpha
-// derives it from the data) and shared by x and r, so no row reduction runs.
-// Per 16-block: S_b = E4M3_RNE((Max / 6) / alpha), the multiplier scale
-// 1 / (alpha S_b) (0 when alpha S_b is 0), codes E2M1_RNE(v * scale) and the
-// residue v - e / scale (v when the scale is 0).  One thread per 8 elements,
-// two threads per block.
+// NVFP4 with one tensor scale alpha for the whole activation tensor (Appendix
+// B.2, Eqs. 8-10), read from device memory (static or calibrated;
+// rsfp4_nvfp4_tensor_alpha derives it from the data) and shared by x and r, so
+// no row reduction runs: per 16-block the scale and multiplier of
+// block_scale_alpha and the codes of encode_residue_mult.  Eight elements per
+// thread, so a block's maximum spans two adjacent lanes.
 
 template <int NC, bool RES>
-__device__ __forceinline__ void alg1_chunks(float (&v)[NC][8], int nchunks, float alpha, uint8_t* codes,
-                                            uint8_t* scales) {
-    const int tid = threadIdx.x;
+__device__ __forceinline__ void quantize_chunks_alpha(float (&v)[NC][8], int nchunks, float alpha, uint8_t* codes,
+                                                      uint8_t* scales) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-        const int j = tid + (int)blockDim.x * c;
+        const int j = (int)threadIdx.x + (int)blockDim.x * c;
         float bm = 0.0f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) bm = fmaxf(bm, fabsf(v[c][e]));
-        bm = fmaxf(bm, dpp<kDppXor1>(bm));          // the block's two lanes
-        const uint32_t sbyte = e4m3_encode((bm / 6.0f) / alpha);
-        const float st = alpha * e4m3_val(sbyte);
-        const float mult = st > 0.0f ? 1.0f / st : 0.0f;
-        float u[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) u[e] = v[c][e] * mult;
-        if (__builtin_expect(mult > 3.402823466e38f, 0)) {
-            // 1 / (alpha S_b) overflowed: a zero element gives 0 * inf; its code
-            // is the zero of its sign, as for any finite multiplier
-#pragma unroll
-            for (int e = 0; e < 8; ++e) u[e] = v[c][e] == 0.0f ? v[c][e] : u[e];
-        }
-        uint32_t packed = 0u;
-        packed = e2m1_pack2<0>(packed, u[0], u[1], 1.0f);
-        packed = e2m1_pack2<1>(packed, u[2], u[3], 1.0f);
-        packed = e2m1_pack2<2>(packed, u[4], u[5], 1.0f);
-        packed = e2m1_pack2<3>(packed, u[6], u[7], 1.0f);
-        if (RES) {
-            rsfp4_float2v d[4];
-            d[0] = e2m1_unpack2<0>(packed, 1.0f);
-            d[1] = e2m1_unpack2<1>(packed, 1.0f);
-            d[2] = e2m1_unpack2<2>(packed, 1.0f);
-            d[3] = e2m1_unpack2<3>(packed, 1.0f);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float em = mult > 0.0f ? d[e >> 1][e & 1] / mult : 0.0f;
-                v[c][e] = v[c][e] - em;
-            }
-        }
+        bm = fmaxf(bm, dpp<kDppXor1>(bm));
+        const MulScale ms = block_scale_alpha(bm, alpha);
+        const uint32_t packed = encode_residue_mult<RES>(v[c], ms.mult);
         if (j < nchunks) {
             *reinterpret_cast<uint32_t*>(codes + 4 * (int64_t)j) = packed;
-            if ((j & 1) == 0) scales[j >> 1] = (uint8_t)sbyte;
+            if ((j & 1) == 0) scales[j >> 1] = (uint8_t)ms.sbyte;
         }
     }
 }
@@ -282,13 +252,13 @@ __global__ __launch_bounds__(kQMaxThreads) void quant_alpha_kernel(const TIn* __
     uint8_t* rec = act + (int64_t)m * row_bytes;
     store_head(rec, alpha, threadIdx.x);
     if (!with_res) {
-        alg1_chunks<NC, false>(v, nchunks, alpha, rec + kActHead, rec + kActHead + K / 2);
+        quantize_chunks_alpha<NC, false>(v, nchunks, alpha, rec + kActHead, rec + kActHead + K / 2);
         return;
     }
-    alg1_chunks<NC, true>(v, nchunks, alpha, rec + kActHead, rec + kActHead + K / 2);
+    quantize_chunks_alpha<NC, true>(v, nchunks, alpha, rec + kActHead, rec + kActHead + K / 2);
     uint8_t* rrec = act + (int64_t)(M + m) * row_bytes;
     store_head(rrec, alpha, threadIdx.x);
-    alg1_chunks<NC, false>(v, nchunks, alpha, rrec + kActHead, rrec + kActHead + K / 2);
+    quantize_chunks_alpha<NC, false>(v, nchunks, alpha, rrec + kActHead, rrec + kActHead + K / 2);
 }
 
 template <int NC, typename TIn>

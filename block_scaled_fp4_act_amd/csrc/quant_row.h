@@ -213,6 +213,56 @@ __device__ __forceinline__ uint32_t encode_residue(float (&v)[EPT], float st) {
     return packed;
 }
 
+// ---- NVFP4 with a tensor scale given in advance (ResServe Appendix B.2) ----
+// Eq. 8 bounds each 16-block by s_i = Max_i / 6; Eq. 9 stores s_i / alpha
+// rounded to E4M3 and dequantizes with s~_i = alpha * S_i; Eq. 10 rounds the
+// elements to E2M1 on that effective scale.  With alpha fixed (not derived
+// from the row) the page's quantizer applies s~_i as a multiplier: codes of
+// v * (1 / s~_i), reconstruction e / (1 / s~_i).  That reading is this
+// operator's; the row-scaled quantizer above divides by s~ instead.
+struct MulScale {
+    uint32_t sbyte;   // the E4M3 byte S_i
+    float mult;       // 1 / (alpha S_i), or 0 where alpha S_i is 0
+};
+
+__device__ __forceinline__ MulScale block_scale_alpha(float bm, float alpha) {
+    MulScale m;
+    m.sbyte = e4m3_encode((bm / 6.0f) / alpha);
+    const float st = alpha * e4m3_val(m.sbyte);
+    m.mult = st > 0.0f ? 1.0f / st : 0.0f;
+    return m;
+}
+
+// E2M1 codes of the eight values v * mult, packed (element e at bits 4e);
+// with RES, v becomes the residue v - e / mult (v itself where mult is 0).
+template <bool RES>
+__device__ __forceinline__ uint32_t encode_residue_mult(float (&v)[8], float mult) {
+    float u[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) u[e] = v[e] * mult;
+    if (__builtin_expect(mult > 3.402823466e38f, 0)) {
+        // the multiplier overflowed to infinity: a zero element would give
+        // 0 * inf; its code is the zero of its sign, as for a finite multiplier
+#pragma unroll
+        for (int e = 0; e < 8; ++e) u[e] = v[e] == 0.0f ? v[e] : u[e];
+    }
+    uint32_t packed = 0u;
+    packed = e2m1_pack2<0>(packed, u[0], u[1], 1.0f);
+    packed = e2m1_pack2<1>(packed, u[2], u[3], 1.0f);
+    packed = e2m1_pack2<2>(packed, u[4], u[5], 1.0f);
+    packed = e2m1_pack2<3>(packed, u[6], u[7], 1.0f);
+    if (RES) {
+        rsfp4_float2v d[4];
+        d[0] = e2m1_unpack2<0>(packed, 1.0f);
+        d[1] = e2m1_unpack2<1>(packed, 1.0f);
+        d[2] = e2m1_unpack2<2>(packed, 1.0f);
+        d[3] = e2m1_unpack2<3>(packed, 1.0f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = v[e] - (mult > 0.0f ? d[e >> 1][e & 1] / mult : 0.0f);
+    }
+    return packed;
+}
+
 // Record header: the row's fp32 tensor scale (0 for MXFP4) and zero padding.
 __device__ __forceinline__ void store_head(uint8_t* rec, float s_g, int lt) {
     if (lt == 0) *reinterpret_cast<uint4*>(rec) = make_uint4(__float_as_uint(s_g), 0u, 0u, 0u);

@@ -429,7 +429,12 @@ size_t rsfp4_kv_page_bytes(int64_t H_kv, int64_t D);
  * S_b = E4M3_RNE(max|x| / (6 g)), codes E2M1_RNE(x / (S_b g)), g = k_scale or
  * v_scale (> 0).  The page's timings exclude cache construction; this call is
  * how the cache is built here.  cache: device, 256-byte aligned, cache_bytes /
- * rsfp4_kv_page_bytes pages. */
+ * rsfp4_kv_page_bytes pages.  The slots of one call must be distinct: the V
+ * codes of the 32 rows of a page share 32-bit words, and a token's nibbles are
+ * replaced by two atomic steps (clear, then set), so two tokens written to one
+ * slot in the same call leave the OR of their codes.  Calls that write the
+ * same pages must be ordered (one stream, or synchronised); tokens of other
+ * slots in the same words are left as they are. */
 rsfp4_status rsfp4_kv_cache_write(const void* k, const void* v, int xt, int64_t T, int64_t H_kv, int64_t D,
                                   const int32_t* slots, float k_scale, float v_scale, void* cache,
                                   size_t cache_bytes, void* stream);
