@@ -168,10 +168,15 @@ rsfp4_status linear(int fmt, bool comp, const void* act, size_t act_bytes, const
     // dequantization they save.
     const int S = (int)num_steps(K);
     int chunk = S;
-    if (K > kMaxNarrowK)
+    if (K > kMaxNarrowK) {
         chunk = 8 * ((S + 15) / 16);
-    else if (fmt == RSFP4_NVFP4 && comp && B > 16 && !out_bf16 && S > 32)
-        chunk = 32;                         // also four row tiles (B > 32): no spills at 2 steps per wave
+    } else if (fmt == RSFP4_NVFP4 && comp && B > 16 && !out_bf16 && S > 32) {
+        // two row tiles with a workspace that holds the split's partial sums:
+        // one pass with K split across workgroups in slices of 32 steps;
+        // otherwise (and four row tiles, B > 32) launches of 32 steps
+        int64_t need = 0;
+        if (narrow_plan(fmt, comp, M, N, S, cus, true, ws_bytes, &need).ks <= 1) chunk = 32;
+    }
     const int passes = (S + chunk - 1) / chunk;
     for (int pass = 0; pass < passes; ++pass) {
         const int s_lo = pass * chunk, s_hi = s_lo + chunk < S ? s_lo + chunk : S;
@@ -410,8 +415,9 @@ size_t rsfp4_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, int compe
         return 0;
     const int64_t B = compensated ? 2 * M : M;
     const int64_t S = num_steps(K);
-    // the split applies to one-pass plans of the narrow kernel's single row tile
-    if (B > 16 || K > kMaxNarrowK) return 0;
+    // the split applies to one-pass plans of the narrow kernel with one or two
+    // row tiles
+    if (B > 32 || K > kMaxNarrowK) return 0;
     int cus = 0;
     if (num_cus(&cus) != RSFP4_OK) return 0;
     int64_t need = 0;

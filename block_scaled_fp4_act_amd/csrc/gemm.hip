@@ -634,9 +634,10 @@ constexpr int rm_for(int maxs, bool single) { return single && !st_for(maxs, sin
 
 template <int FMT, int RT, bool COMP, int MAXS>
 hipError_t launch_v(const GemmArgs& a, int KW, int64_t grid, hipStream_t s, bool single) {
-    // split K: compensated NVFP4 with one row tile and one or two steps per
-    // wave (the plans plan_gemm_small makes), streaming order, deferred reduction
-    if constexpr (FMT == kNV && RT == 1 && COMP && MAXS <= 2) {
+    // split K: compensated NVFP4 with one or two row tiles and one or two steps
+    // per wave (the plans plan_gemm_small makes), streaming order, deferred
+    // reduction
+    if constexpr (FMT == kNV && RT <= 2 && COMP && MAXS <= 2) {
         if (a.ks > 1)
             return launch_t<FMT, MAXS, RT, COMP, pd_for(FMT, RT, MAXS, false), apre_for(FMT, RT, MAXS, false, COMP),
                             1, true, true>(a, KW, grid, s);
@@ -698,7 +699,7 @@ GemmPlan plan_gemm_small(int64_t M, int64_t N, int64_t S, bool comp, int num_cus
     const int64_t fit = lds_cap / ((int64_t)pl.kw * pl.rt * (comp ? 512 : 1024));
     pl.ngl = (int)(per_wg < fit ? per_wg : fit);
     if (pl.ngl < 1) pl.ngl = 1;
-    if (!split_ok || pl.rt != 1 || !comp) return pl;
+    if (!split_ok || pl.rt > 2 || !comp) return pl;
 
     // Split K across workgroups (one workgroup per CU, each owning one K slice
     // of several channel groups), where one of two shapes makes it pay
@@ -714,8 +715,19 @@ GemmPlan plan_gemm_small(int64_t M, int64_t N, int64_t S, bool comp, int num_cus
     // about as much as a whole K = 4096 group).
     int ks = 0;
     if (G > kSplitGroups) return pl;
-    if (G <= num_cus && S >= 64 && S % 4 == 0) ks = 4;
-    else if (G > num_cus && G % num_cus != 0 && (2 * G) % num_cus == 0 && S % 4 == 0 && S <= 64) ks = 2;
+    if (pl.rt == 2) {
+        // two row tiles hold their f16 fragments for two steps per wave, 32
+        // steps per workgroup: slices of up to 32 steps, one pass over K
+        // instead of launches of 32 steps that each read and rewrite y
+        // (2 to 4 equal slices, each of at most 32 steps)
+        if (S <= 32) return pl;
+        for (int k = (int)((S + 31) / 32); k <= 4 && ks == 0; ++k)
+            if (S % k == 0 && ((S / k) % 2 == 0 || S / k <= kMaxWaves)) ks = k;
+    } else if (G <= num_cus && S >= 64 && S % 4 == 0) {
+        ks = 4;
+    } else if (G > num_cus && G % num_cus != 0 && (2 * G) % num_cus == 0 && S % 4 == 0 && S <= 64) {
+        ks = 2;
+    }
     if (ks == 0) return pl;
     const int64_t ss = S / ks;
     // two steps per wave where they fit in 16 waves (MLP down: 14 waves, up:
@@ -725,7 +737,7 @@ GemmPlan plan_gemm_small(int64_t M, int64_t N, int64_t S, bool comp, int num_cus
         if (maxs == 0 && ss % m == 0 && ss / m <= kMaxWaves) maxs = m;
     if (maxs == 0) return pl;
     GemmPlan sp;
-    sp.rt = 1;
+    sp.rt = pl.rt;
     sp.maxs = maxs;
     sp.kw = (int)(ss / maxs);
     sp.ks = ks;
@@ -733,7 +745,7 @@ GemmPlan plan_gemm_small(int64_t M, int64_t N, int64_t S, bool comp, int num_cus
     const int64_t per_slice = G * ks >= num_cus ? num_cus / ks : G;   // workgroups per slice
     sp.grid = per_slice * ks;
     const int64_t units = (G + per_slice - 1) / per_slice;           // groups per workgroup
-    const int64_t sfit = kRedBytesMax / ((int64_t)sp.kw * 512);
+    const int64_t sfit = kRedBytesMax / ((int64_t)sp.kw * sp.rt * 512);
     sp.ngl = (int)(units < sfit ? units : sfit);
     if (sp.ngl < 1) sp.ngl = 1;
     return sp;

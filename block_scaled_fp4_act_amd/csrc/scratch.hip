@@ -19,10 +19,10 @@ namespace rsfp4 {
 namespace {
 
 // The split linear's counters (kSplitCounterBytes, zero between calls) and
-// partial sums: enough for every plan plan_gemm_small splits with one row
-// tile (at most kSplitGroups groups x 2 slices, or 256 groups x 4 slices,
-// 512 bytes per group and slice).
-constexpr int64_t kScratchBytes = kSplitCounterBytes + kSplitGroups * 2 * 512;
+// partial sums: enough for every plan plan_gemm_small splits (at most
+// kSplitGroups groups x 4 slices x 1 KB: two row tiles, K = 16384; one row
+// tile takes at most 2 slices of 512 bytes per group, or 4 of 256 groups).
+constexpr int64_t kScratchBytes = kSplitCounterBytes + kSplitGroups * 4 * 1024;
 
 static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 

@@ -38,7 +38,9 @@ def _cus():
 # few channel groups with K of 64+ steps (four slices, two steps per wave;
 # ragged N), and a half round of groups (two slices)
 SPLIT_CASES = [(1, 512, 8192), (8, 512, 8192), (3, 1000, 12288), (6, 16, 16384),
-               (8, 6144, 2048), (2, 6144, 4096), (7, 6136, 4096)]
+               (8, 6144, 2048), (2, 6144, 4096), (7, 6136, 4096),
+               # two row tiles (17..32 operand rows): slices of up to 32 steps
+               (16, 2048, 8192), (12, 1000, 12288), (9, 520, 16384), (16, 4096, 14336), (10, 48, 4608)]
 
 
 def _setup(M, N, K, seed):
@@ -168,4 +170,6 @@ def test_workspace_query():
     assert rs.workspace_bytes(0, 8, 28672, 8192, True) == 0       # large MLP (balanced)
     assert rs.workspace_bytes(1, 8, 4096, 14336, True) == 0       # MXFP4
     assert rs.workspace_bytes(0, 8, 4096, 14336, False) == 0      # plain
-    assert rs.workspace_bytes(0, 16, 4096, 14336, True) == 0      # two row tiles
+    assert rs.workspace_bytes(0, 16, 4096, 14336, True) > 0       # two row tiles, 4 slices of 28 steps
+    assert rs.workspace_bytes(0, 16, 4096, 4096, True) == 0       # two row tiles, 32 steps: one pass
+    assert rs.workspace_bytes(0, 17, 4096, 8192, True) == 0       # four row tiles

@@ -32,8 +32,9 @@ def test_noalloc_matches_workspace_entry():
     rs.lib()
     oracle.build()
     # the MLP down projection (K split in four on a 256-CU device), then a
-    # smaller split call, then a shape whose plan does not split
-    for i, (M, N, K) in enumerate([(8, 4096, 14336), (3, 512, 8192), (4, 1024, 4096)]):
+    # smaller split call, a shape whose plan does not split, and two row
+    # tiles split in two
+    for i, (M, N, K) in enumerate([(8, 4096, 14336), (3, 512, 8192), (4, 1024, 4096), (16, 2048, 8192)]):
         x, W, blob, act = _case(M, N, K, 40 + i)
         nb = rs.workspace_bytes(0, M, N, K, True)
         ws = torch.zeros(max(nb, 256), dtype=torch.uint8, device="cuda")
