@@ -61,8 +61,8 @@ constexpr int64_t kSplitCounterBytes = kSplitGroups * 4;
 int64_t split_ws_bytes(const GemmPlan& pl, bool comp, int64_t N);
 
 // Streaming read of bytes bytes at src (one workgroup of 8 waves per CU), the
-// reference rate for the weight stream; sink: one word that receives a value
-// only in a case that does not arise for real data.
+// reference rate for the weight stream; the xor of all its 32-bit words is
+// xor-ed into *sink.
 hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, int num_cus, hipStream_t s);
 
 // The library's per-device scratch (scratch.hip): its size, and its device
