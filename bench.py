@@ -53,8 +53,8 @@ METRIC = "compensated FP4 linear µs/call + HBM GB/s (% of peak) at M=1–8, K,N
 # calibration factors (FETCH_SIZE x2.0, WRITE_SIZE x1.0).  Valid only for the
 # kernel sources whose hash is recorded; reported as null otherwise.
 TRAFFIC = {
-    "sources_sha256": "b545fa7d3431fd012c6bd150887b85268ccd98e5521c4635e6ef68828cc26d8e",
-    "fetch_bytes": 132856832,     # 2.0 x 64,871 KiB
+    "sources_sha256": "5e81bea28f18923f7969aba7d7b90c928c4b57cbe4a7615191e42fc74b378392",
+    "fetch_bytes": 132851712,     # 2.0 x 64,869 KiB
     "write_bytes": 917504,        # 1.0 x 896 KiB
 }
 KERNEL_SOURCES = ["gemm.hip", "layout.h", "codec.h", "fp4_frag.h", "quant_row.h", "kernels.h"]
