@@ -183,3 +183,23 @@ def test_grouped_validation():
     need = rs.packed_weight_bytes(0, 64, 512)
     assert f(FAKE, big, 8, FAKE, 4 * need - 1, 4, FAKE, 2, 64, 512, FAKE, None) == 5
     assert "blobs need" in _err()
+
+
+def test_stream_read_host_checks():
+    """rsfp4_stream_read: null, alignment and size checks come before any
+    device call."""
+    L = rs.lib()
+    sink = ctypes.c_void_p(0x100000)
+    assert L.rsfp4_stream_read(None, 4096, sink, None) == 1
+    assert L.rsfp4_stream_read(FAKE, 4096, None, None) == 1
+    assert L.rsfp4_stream_read(ctypes.c_void_p(0x100008), 4096, sink, None) == 3       # src not 16-aligned
+    assert L.rsfp4_stream_read(FAKE, 4096, ctypes.c_void_p(0x100002), None) == 3       # sink not 4-aligned
+    assert L.rsfp4_stream_read(FAKE, 4088, sink, None) == 2                             # not whole 16 bytes
+    assert "multiple of 16" in _err()
+
+
+def test_noalloc_host_checks():
+    """The no-allocation linear validates like the workspace call (null and
+    shape errors before any device call)."""
+    L = rs.lib()
+    assert L.rsfp4_nvfp4_linear_compensated_noalloc(None, 0, None, 0, 1, 16, 128, None, None) == 1
