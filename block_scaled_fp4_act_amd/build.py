@@ -12,7 +12,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "librsfp4.so")
-SOURCES = ["api.cpp", "quant.hip", "prepack.hip", "calib.hip", "gemm.hip", "gemm_tile.hip", "attn.hip", "scratch.hip", "stream_read.hip"]
+SOURCES = ["api.cpp", "quant.hip", "prepack.hip", "calib.hip", "gemm.hip", "gemm_tile.hip", "gemm_tile_dma.hip", "attn.hip", "scratch.hip", "stream_read.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -152,6 +152,20 @@ rsfp4_status linear(int fmt, bool comp, const void* act, size_t act_bytes, const
         if (std::getenv("RSFP4_LOG"))
             std::fprintf(stderr, "[rsfp4] linear fmt=%d comp=%d M=%lld N=%lld K=%lld tiled\n", fmt, (int)comp,
                          (long long)M, (long long)N, (long long)K);
+        // MXFP4 with a workspace that holds the activation operand rewritten in
+        // the packed-weight layout (after the counter area, which stays zero):
+        // both operands then stream into LDS as contiguous 1 KB requests
+        if (fmt == RSFP4_MXFP4 && (int64_t)ws_bytes >= kSplitCounterBytes + act_tile_bytes(fmt, B, K)) {
+            int cus = 0;
+            st = num_cus(&cus);
+            if (st != RSFP4_OK) return st;
+            void* at = static_cast<uint8_t*>(ws) + kSplitCounterBytes;
+            st = hip_status(launch_act_tile(fmt, comp, act, rb, (int)M, K, at, (hipStream_t)stream), "linear launch");
+            if (st != RSFP4_OK) return st;
+            return hip_status(launch_gemm_tile_dma(comp, at, w_packed, (int)M, N, K, y, out_bf16, cus,
+                                                   (hipStream_t)stream),
+                              "linear launch");
+        }
         return hip_status(launch_gemm_tile(fmt, comp, act, rb, w_packed, (int)M, N, K, y, out_bf16,
                                            (hipStream_t)stream),
                           "linear launch");
@@ -415,6 +429,9 @@ size_t rsfp4_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, int compe
         return 0;
     const int64_t B = compensated ? 2 * M : M;
     const int64_t S = num_steps(K);
+    // wide MXFP4 operands: the tiled activation operand after the counter area
+    if (B > 32 && fmt == RSFP4_MXFP4)
+        return (size_t)(kSplitCounterBytes + act_tile_bytes(fmt, B, K));
     // the split applies to one-pass plans of the narrow kernel with one or two
     // row tiles
     if (B > 32 || K > kMaxNarrowK) return 0;

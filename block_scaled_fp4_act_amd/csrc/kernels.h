@@ -105,6 +105,16 @@ hipError_t launch_gemm_inq(int fmt, const InqPlan& q, bool comp, const void* x, 
 hipError_t launch_gemm_tile(int fmt, bool comp, const void* act, int64_t row_bytes, const void* blob,
                             int M, int64_t N, int64_t K, void* y, bool out_bf16, hipStream_t s);
 
+// Wide-operand MXFP4 linear over LDS-DMA streamed operands: the activation
+// records rewritten into the packed-weight layout (groups of 16 stacked rows,
+// base and residue rows interleaved; act_tile_bytes bytes), then the tiled
+// product of the two (gemm_tile_dma.hip).
+int64_t act_tile_bytes(int fmt, int64_t B, int64_t K);
+hipError_t launch_act_tile(int fmt, bool comp, const void* act, int64_t row_bytes, int M, int64_t K, void* out,
+                           hipStream_t s);
+hipError_t launch_gemm_tile_dma(bool comp, const void* act_tiled, const void* blob, int M, int64_t N, int64_t K,
+                                void* y, bool out_bf16, int num_cus, hipStream_t s);
+
 // Paper-numerics NVFP4 quantizer (tensor scale alpha from device memory, shared
 // by x and r; multiplier-scale codes and residue) and the alpha of a tensor.
 hipError_t launch_quantize_act_alpha(int xt_bf16, const void* x, int M, int64_t K, const float* alpha,

@@ -48,6 +48,12 @@ def test_size_queries():
     assert rs.packed_weight_bytes(1, 25600, 5120) == 256 + 1600 * 10 * (4096 + 256)
     assert rs.packed_weight_bytes(0, 17, 160) == 256 + 2 * 1 * (4096 + 512)   # padded quad
     assert rs.workspace_bytes(0, 4, 4096, 4096, True) == 0
+    # wide MXFP4 operands (more than 32 stacked rows): the 16 KB counter area,
+    # then the activation operand rewritten as groups of 16 rows x quads of
+    # 4 steps (4 KB codes + 256 B scale words)
+    assert rs.workspace_bytes(1, 256, 25600, 5120, True) == 16384 + 32 * 10 * (4096 + 256)
+    assert rs.workspace_bytes(1, 40, 64, 1056, False) == 16384 + 3 * 3 * (4096 + 256)
+    assert rs.workspace_bytes(1, 17, 64, 1056, True) == 16384 + 3 * 3 * (4096 + 256)
     # invalid requests size to 0
     assert rs.packed_weight_bytes(0, 16, 48) == 0
     assert rs.packed_weight_bytes(2, 16, 64) == 0
