@@ -98,6 +98,16 @@ rsfp4_status quantize(int fmt, const void* x, int xt, int64_t M, int64_t K, int 
                       "quantize launch");
 }
 
+// Workspace of the MXFP4 tiled product over rewritten activations: the
+// counter area, then the tiled operand; 0 for NVFP4 and when the operand would
+// exceed kMaxTileWs (the records path then runs without it).
+constexpr int64_t kMaxTileWs = (int64_t)1 << 30;
+int64_t tile_ws_bytes(int fmt, int64_t B, int64_t K) {
+    if (fmt != RSFP4_MXFP4) return 0;
+    const int64_t t = act_tile_bytes(B, K);
+    return t > kMaxTileWs ? 0 : kSplitCounterBytes + t;
+}
+
 // The narrow linear's plan for one launch over `steps` (split across
 // workgroups where the shape gains from it: compensated NVFP4, see
 // plan_gemm_small), its workspace bytes, and whether the caller's workspace
@@ -154,13 +164,15 @@ rsfp4_status linear(int fmt, bool comp, const void* act, size_t act_bytes, const
                          (long long)M, (long long)N, (long long)K);
         // MXFP4 with a workspace that holds the activation operand rewritten in
         // the packed-weight layout (after the counter area, which stays zero):
-        // both operands then stream into LDS as contiguous 1 KB requests
-        if (fmt == RSFP4_MXFP4 && (int64_t)ws_bytes >= kSplitCounterBytes + act_tile_bytes(fmt, B, K)) {
+        // both operands stream into LDS as contiguous 1 KB requests; same bits
+        // as the records path
+        const int64_t tws = tile_ws_bytes(fmt, B, K);
+        if (tws > 0 && (int64_t)ws_bytes >= tws) {
             int cus = 0;
             st = num_cus(&cus);
             if (st != RSFP4_OK) return st;
             void* at = static_cast<uint8_t*>(ws) + kSplitCounterBytes;
-            st = hip_status(launch_act_tile(fmt, comp, act, rb, (int)M, K, at, (hipStream_t)stream), "linear launch");
+            st = hip_status(launch_act_tile(comp, act, rb, (int)M, K, at, (hipStream_t)stream), "linear launch");
             if (st != RSFP4_OK) return st;
             return hip_status(launch_gemm_tile_dma(comp, at, w_packed, (int)M, N, K, y, out_bf16, cus,
                                                    (hipStream_t)stream),
@@ -430,8 +442,7 @@ size_t rsfp4_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, int compe
     const int64_t B = compensated ? 2 * M : M;
     const int64_t S = num_steps(K);
     // wide MXFP4 operands: the tiled activation operand after the counter area
-    if (B > 32 && fmt == RSFP4_MXFP4)
-        return (size_t)(kSplitCounterBytes + act_tile_bytes(fmt, B, K));
+    if (B > 32 && fmt == RSFP4_MXFP4) return (size_t)tile_ws_bytes(fmt, B, K);
     // the split applies to one-pass plans of the narrow kernel with one or two
     // row tiles
     if (B > 32 || K > kMaxNarrowK) return 0;

@@ -12,23 +12,12 @@
 //      rows interleaved (row 2m = q(x) row m, row 2m+1 = q(r) row m) so that
 //      every accumulator lane holds complete pairs for the Fold.  Rows past
 //      the operand and elements past K get zero codes and zero scales.  It is
-//      a byte permutation of the records: no arithmetic.
-//   2. gemm_tile_mx_dma multiplies the two tiled operands.  A row of records
-//      holds 64 bytes per step, so gathering a 16-row fragment straight from
-//      the records costs 16 partial cache lines per 1 KB; the tiled form makes
-//      every fragment one contiguous 1 KB request, for either operand.
-// A workgroup of 4 waves in a 2 x 2 grid owns TM = 32*RTW rows x TN = 32*CTW
-// channels; a wave owns RTW x CTW tiles of 16 x 16.  A stage of LDS holds one
-// step's fragments of both operands; 4 stages rotate (stage s+3 is requested
-// during step s), and a 2-slot ring holds the scale words of the current and
-// the next quad.  The requests of a stage are tracked by the vector-memory
-// counter; one barrier per step, placed halfway through the step's MFMAs and
-// fenced for LDS only (a workgroup fence would wait for every request in
-// flight, the later stages' included), publishes stage s+1 and frees the
-// buffer of stage s-1.  Each step's MFMAs are v_mfma_scale_f32_16x16x128_f8f6f4
-// (FP4 x FP4 with the E8M0 scales of both operands, the quad step selecting the
-// scale byte), summed over the steps in order, so the result is bit-identical
-// to the register-staged kernel's.
+//      a byte permutation of the records: no arithmetic.  A record row holds
+//      64 bytes per step, so gathering a 16-row fragment straight from the
+//      records costs 16 partial cache lines per 1 KB (measured: 48 against 118
+//      GB/s per compute unit for contiguous 1 KB requests); in tiles every
+//      fragment of either operand is one contiguous request.
+//   2. gemm_tile_mx_dma multiplies the two tiled operands (below).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -47,12 +36,11 @@ constexpr int kXcds = 8;
 
 // ---- 1. activation records -> tiled operand ----
 // One thread per 16-byte code chunk or per lane scale word of the output.
-template <int FMT, bool COMP>
+template <bool COMP>
 __global__ __launch_bounds__(256) void act_tile_kernel(const uint8_t* __restrict__ act, int64_t row_bytes, int M,
                                                        int64_t K, int64_t groups, uint8_t* __restrict__ out) {
-    constexpr int SB = FMT == kNV ? 2 : 1;             // scale bytes per lane and step
     const int64_t nq = num_quads(K);
-    const int64_t GB = group_bytes(FMT, K), QB = quad_bytes(FMT);
+    const int64_t GB = group_bytes(kMX, K), QB = quad_bytes(kMX);
     const int64_t per_group = nq * (4 * 64 + 64);
     const int64_t item = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (item >= groups * per_group) return;
@@ -70,47 +58,37 @@ __global__ __launch_bounds__(256) void act_tile_kernel(const uint8_t* __restrict
         rec = R * row_bytes;
     }
     uint8_t* grp_out = out + grp * GB + q * QB;
-    if (w < 256) {
+    if (w < 256) {                                     // codes: step u of the quad, lane l
         const int u = w >> 6;
         const int64_t k = (4 * q + u) * kStepK + 32 * g;
         uint4 v = make_uint4(0u, 0u, 0u, 0u);
         if (rec >= 0 && k < K) v = *reinterpret_cast<const uint4*>(act + rec + kActHead + k / 2);
         *reinterpret_cast<uint4*>(grp_out + u * kStepCodes + 16 * l) = v;
-    } else {
-        const int64_t sbase = rec + kActHead + K / 2;   // the record's block scales
-        uint32_t lo = 0u, hi = 0u;
+    } else {                                           // lane l's E8M0 bytes of block g, steps 4q..4q+3
+        const int64_t sbase = rec + kActHead + K / 2;
+        uint32_t word = 0u;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int64_t s = 4 * q + u;
-            const int64_t k = s * kStepK + 32 * g;
-            if (rec < 0 || k >= K) continue;
-            if (FMT == kMX) {
-                lo |= (uint32_t)act[sbase + 4 * s + g] << (8 * u);
-            } else {
-                const uint32_t two = (uint32_t)act[sbase + 8 * s + 2 * g] | ((uint32_t)act[sbase + 8 * s + 2 * g + 1] << 8);
-                if (u < 2) lo |= two << (16 * u);
-                else hi |= two << (16 * (u - 2));
-            }
+            if (rec >= 0 && s * kStepK + 32 * g < K) word |= (uint32_t)act[sbase + 4 * s + g] << (8 * u);
         }
-        uint8_t* dst = grp_out + kQuadSteps * kStepCodes + 4 * SB * l;
-        if (FMT == kMX) *reinterpret_cast<uint32_t*>(dst) = lo;
-        else *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+        *reinterpret_cast<uint32_t*>(grp_out + kQuadSteps * kStepCodes + 4 * l) = word;
     }
 }
 
-// ---- 2. the tiled product ----
-template <int RTW, int CTW>
-struct DmaTile {
-    static constexpr int TM = 32 * RTW, TN = 32 * CTW;
-    static constexpr int AFR = TM / 16, BFR = TN / 16;     // fragments (16-row / 16-channel groups) per step
-    static constexpr int B_OFF = AFR * 1024;
-    static constexpr int STAGE = (AFR + BFR) * 1024;
-    static constexpr int SQ = (AFR + BFR) * 256;           // scale words of one quad, both operands
-    static constexpr int DA = AFR / 4, DB = BFR / 4;       // per-wave requests of one stage
-    static constexpr int D = DA + DB;
-    static constexpr int DS = (AFR + BFR) / 4;             // per-wave scale requests of one quad
-    static_assert(AFR % 4 == 0 && BFR % 4 == 0, "fragments split evenly over the 4 waves");
-};
+// ---- 2. the tiled products ----
+// Both kernels stream the two tiled operands into a ring of LDS stages with
+// the buffer loads' LDS-DMA form (each request: 64 lanes x 16 bytes, one
+// contiguous 1 KB fragment) and track them with the vector-memory counter.
+// Every step starts with a wait for this wave's requests of its stage (what was
+// requested after it stays in flight) and a workgroup barrier fenced for LDS
+// only (a workgroup fence would also wait for the later stages' requests); the
+// barrier publishes the stage and frees the buffer the previous step read,
+// which is refilled right after it.  The matrix cores reach their rate only
+// with two waves per SIMD (one wave issuing independent MFMAs back to back
+// sustains about 60 % of it), so a workgroup runs 8 waves, or 4 waves with two
+// workgroups per compute unit, within 256 registers per wave; the other wave of
+// a SIMD hides each wave's LDS latency and barrier waits.
 
 // One request of 64 lanes: each lane's 16 (4) bytes at voffset vo of r land in
 // LDS at dst + 16 * lane (4 * lane); dst is uniform.
@@ -129,6 +107,13 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// This wave's LDS reads done, then the workgroup barrier (no memory fence).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // Buffer resource over bytes [off, bytes) of base (zeros past the end).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_at(const uint8_t* base, int64_t off, int64_t bytes) {
     const int64_t left = bytes - off;
@@ -143,6 +128,53 @@ __device__ __forceinline__ floatx4 mfma_fp4_u(const uint4& a, const uint4& b, fl
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 4, U, (int)sa, U, (int)sb);
 }
 
+// Tile of the workgroup: per XCD a contiguous range of tiles, row tiles
+// fastest, so the row tiles that share a weight tile run together on one L2.
+struct TileGrid {
+    int row_tiles;
+    int64_t tiles;
+    int64_t per_xcd;
+};
+__device__ __forceinline__ bool tile_of(const TileGrid& t, int* rtile, int64_t* ctile) {
+    const int64_t L_id = blockIdx.x;
+    const int64_t tile = (L_id % kXcds) * t.per_xcd + L_id / kXcds;
+    if (tile >= t.tiles) return false;
+    *rtile = (int)(tile % t.row_tiles);
+    *ctile = tile / t.row_tiles;
+    return true;
+}
+inline TileGrid tile_grid(int64_t B, int64_t N, int TM, int TN) {
+    TileGrid t;
+    t.row_tiles = (int)((B + TM - 1) / TM);
+    t.tiles = (int64_t)t.row_tiles * ((num_groups(N) + TN / 16 - 1) / (TN / 16));
+    t.per_xcd = (t.tiles + kXcds - 1) / kXcds;
+    return t;
+}
+
+// ---- MXFP4: both operands in the packed-weight layout ----
+// WR x WC waves; a wave owns RTW x CTW output tiles of 16 x 16, the workgroup
+// TM = 16*RTW*WR rows x TN = 16*CTW*WC channels.  A stage holds one step's
+// fragments of both operands; 4 stages rotate (stage s+3 requested in step s),
+// and a 2-slot ring holds the scale words of the current and the next quad
+// (requested in the quad's second step, read in its first).  Each step's MFMAs
+// are v_mfma_scale_f32_16x16x128_f8f6f4 (FP4 x FP4 with both operands' E8M0
+// scales, the quad step selecting the scale byte), summed over the steps in
+// order, as the register-staged kernel does: the result is bit-identical.
+template <int RTW, int CTW, int WR, int WC>
+struct MxTile {
+    static constexpr int NW = WR * WC;
+    static constexpr int TM = 16 * RTW * WR, TN = 16 * CTW * WC;
+    static constexpr int AFR = TM / 16, BFR = TN / 16;     // fragments per step
+    static constexpr int B_OFF = AFR * 1024;
+    static constexpr int STAGE = (AFR + BFR) * 1024;
+    static constexpr int SQ = (AFR + BFR) * 256;           // scale words of one quad, both operands
+    static constexpr int DA = AFR / NW, DB = BFR / NW;     // per-wave requests of one stage
+    static constexpr int D = DA + DB;
+    static constexpr int DS = DA + DB;                     // per-wave scale requests of one quad
+    static_assert(AFR % NW == 0 && BFR % NW == 0, "fragments split evenly over the waves");
+    static_assert(4 * STAGE + 2 * SQ <= 160 * 1024, "the ring fits in LDS");
+};
+
 struct DmaArgs {
     const uint8_t* at;   // tiled activation operand (act_tile_kernel)
     const uint8_t* blob; // packed weights
@@ -151,14 +183,12 @@ struct DmaArgs {
     int64_t K;
     void* y;
     int out_bf16;
-    int row_tiles;
-    int64_t tiles;
-    int64_t per_xcd;
+    TileGrid grid;
 };
 
-template <bool COMP, int RTW, int CTW>
-__global__ __launch_bounds__(256, 1) void gemm_tile_mx_dma(DmaArgs p) {
-    using T = DmaTile<RTW, CTW>;
+template <bool COMP, int RTW, int CTW, int WR, int WC, int OCC>
+__global__ __launch_bounds__(64 * WR * WC, OCC) void gemm_tile_mx_dma(DmaArgs p) {
+    using T = MxTile<RTW, CTW, WR, WC>;
     __shared__ __attribute__((aligned(16))) uint8_t st0[T::STAGE];
     __shared__ __attribute__((aligned(16))) uint8_t st1[T::STAGE];
     __shared__ __attribute__((aligned(16))) uint8_t st2[T::STAGE];
@@ -166,18 +196,14 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_mx_dma(DmaArgs p) {
     __shared__ __attribute__((aligned(16))) uint8_t sq0[T::SQ];
     __shared__ __attribute__((aligned(16))) uint8_t sq1[T::SQ];
 
-    // tile of this workgroup (per XCD a contiguous range, row tiles fastest,
-    // so the row tiles that share a weight tile run together on one L2)
-    const int64_t L_id = blockIdx.x;
-    const int64_t tile = (L_id % kXcds) * p.per_xcd + L_id / kXcds;
-    if (tile >= p.tiles) return;                        // uniform: the whole workgroup
-    const int rtile = (int)(tile % p.row_tiles);
-    const int64_t ctile = tile / p.row_tiles;
+    int rtile;
+    int64_t ctile;
+    if (!tile_of(p.grid, &rtile, &ctile)) return;       // uniform: the whole workgroup
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4, i = lane & 15;
-    const int wr = wave >> 1, wc = wave & 1;
+    const int wr = wave / WC, wc = wave % WC;
     const int64_t GB = group_bytes(kMX, p.K);
     const int64_t QB = quad_bytes(kMX);
     const int S = (int)num_steps(p.K);
@@ -193,17 +219,17 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_mx_dma(DmaArgs p) {
     const int64_t abytes = (GA - a0 < T::AFR ? GA - a0 : T::AFR) * GB;
     const int64_t bbytes = (GW - b0 < T::BFR ? GW - b0 : T::BFR) * GB;
 
-    // per-lane request offsets inside a tile: fragment j of this wave is group wave + 4j
+    // per-lane request offsets inside a tile: fragment j of this wave is group wave + NW*j
     uint32_t a_vo[T::DA], b_vo[T::DB], as_vo[T::DA], bs_vo[T::DB];
 #pragma unroll
     for (int j = 0; j < T::DA; ++j) {
-        a_vo[j] = (uint32_t)((wave + 4 * j) * GB) + 16u * lane;
-        as_vo[j] = (uint32_t)((wave + 4 * j) * GB) + kQuadSteps * kStepCodes + 4u * lane;
+        a_vo[j] = (uint32_t)((wave + T::NW * j) * GB) + 16u * lane;
+        as_vo[j] = (uint32_t)((wave + T::NW * j) * GB) + kQuadSteps * kStepCodes + 4u * lane;
     }
 #pragma unroll
     for (int j = 0; j < T::DB; ++j) {
-        b_vo[j] = (uint32_t)((wave + 4 * j) * GB) + 16u * lane;
-        bs_vo[j] = (uint32_t)((wave + 4 * j) * GB) + kQuadSteps * kStepCodes + 4u * lane;
+        b_vo[j] = (uint32_t)((wave + T::NW * j) * GB) + 16u * lane;
+        bs_vo[j] = (uint32_t)((wave + T::NW * j) * GB) + kQuadSteps * kStepCodes + 4u * lane;
     }
 
     auto stage_buf = [&](int b) -> uint8_t* { return b == 0 ? st0 : (b == 1 ? st1 : (b == 2 ? st2 : st3)); };
@@ -214,106 +240,73 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_mx_dma(DmaArgs p) {
         const __amdgpu_buffer_rsrc_t ra = rsrc_at(abase, off, abytes);
         const __amdgpu_buffer_rsrc_t rb = rsrc_at(bbase, off, bbytes);
 #pragma unroll
-        for (int j = 0; j < T::DA; ++j) dma16(ra, dst + (wave + 4 * j) * 1024, a_vo[j]);
+        for (int j = 0; j < T::DA; ++j) dma16(ra, dst + (wave + T::NW * j) * 1024, a_vo[j]);
 #pragma unroll
-        for (int j = 0; j < T::DB; ++j) dma16(rb, dst + T::B_OFF + (wave + 4 * j) * 1024, b_vo[j]);
+        for (int j = 0; j < T::DB; ++j) dma16(rb, dst + T::B_OFF + (wave + T::NW * j) * 1024, b_vo[j]);
     };
     auto dma_scales = [&](int q, int slot) {  // quad q's scale words into ring slot
         uint8_t* dst = slot ? sq1 : sq0;
         const __amdgpu_buffer_rsrc_t ra = rsrc_at(abase, (int64_t)q * QB, abytes);
         const __amdgpu_buffer_rsrc_t rb = rsrc_at(bbase, (int64_t)q * QB, bbytes);
 #pragma unroll
-        for (int j = 0; j < T::DA; ++j) dma4(ra, dst + (wave + 4 * j) * 256, as_vo[j]);
+        for (int j = 0; j < T::DA; ++j) dma4(ra, dst + (wave + T::NW * j) * 256, as_vo[j]);
 #pragma unroll
-        for (int j = 0; j < T::DB; ++j) dma4(rb, dst + (T::AFR + wave + 4 * j) * 256, bs_vo[j]);
+        for (int j = 0; j < T::DB; ++j) dma4(rb, dst + (T::AFR + wave + T::NW * j) * 256, bs_vo[j]);
     };
 
-    struct Frag {
-        uint4 a[RTW];
-        uint4 b[CTW];
-    };
-    struct Scales {
-        uint32_t a[RTW];
-        uint32_t b[CTW];
-    };
-    Frag F0, F1;
-    Scales Q0, Q1;
-
-    auto read_stage = [&](int b, Frag& F) {
-        const uint8_t* src = stage_buf(b);
-#pragma unroll
-        for (int rt = 0; rt < RTW; ++rt)
-            F.a[rt] = *reinterpret_cast<const uint4*>(src + (wr * RTW + rt) * 1024 + 16 * lane);
-#pragma unroll
-        for (int ct = 0; ct < CTW; ++ct)
-            F.b[ct] = *reinterpret_cast<const uint4*>(src + T::B_OFF + (wc * CTW + ct) * 1024 + 16 * lane);
-    };
-    auto read_scales = [&](int slot, Scales& Q) {
-        const uint8_t* src = slot ? sq1 : sq0;
-#pragma unroll
-        for (int rt = 0; rt < RTW; ++rt)
-            Q.a[rt] = *reinterpret_cast<const uint32_t*>(src + (wr * RTW + rt) * 256 + 4 * lane);
-#pragma unroll
-        for (int ct = 0; ct < CTW; ++ct)
-            Q.b[ct] = *reinterpret_cast<const uint32_t*>(src + (T::AFR + wc * CTW + ct) * 256 + 4 * lane);
-    };
-
+    uint4 fa[RTW], fb[CTW];
+    uint32_t qa[RTW], qb[CTW];
     floatx4 acc[RTW][CTW];
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
         for (int ct = 0; ct < CTW; ++ct) acc[rt][ct] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    auto mfmas = [&](const Frag& F, const Scales& Q, auto u_tag, int rt0, int rt1) {
-        constexpr int U = decltype(u_tag)::value;
-#pragma unroll
-        for (int rt = rt0; rt < rt1; ++rt)
-#pragma unroll
-            for (int ct = 0; ct < CTW; ++ct)
-                acc[rt][ct] = mfma_fp4_u<U>(F.a[rt], F.b[ct], acc[rt][ct], Q.a[rt], Q.b[ct]);
-    };
-
-    // LDS-only barrier: this wave's LDS reads done, then the workgroup barrier.
-    // (The stage's DMA requests were waited for just before, by count.)
-    auto barrier = [&]() {
-        __builtin_amdgcn_sched_barrier(0);
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        __builtin_amdgcn_sched_barrier(0);
-    };
-
-    // ---- pipeline ----
-    // Requests in program order: prologue [scales q0, stage 0, stage 1, stage 2];
-    // step s: [scales of quad q+1 if s % 4 == 1], stage s+3.  In step s the wait
-    // for stage s+1 leaves in flight what was requested after it: stages s+2 and
-    // s+3, and the next quad's scales when they were requested in step s-1 or s.
+    // Requests in program order: prologue [scales q0, stages 0, 1, 2]; step s,
+    // after its barrier: [scales of quad q+1 if s % 4 == 1], stage s+3.  The
+    // wait at the start of step s leaves in flight what steps s-2 and s-1
+    // requested (stage s was requested in step s-3, or in the prologue).
+    // Requests in program order: prologue [scales q0, stages 0, 1, 2]; step s,
+    // after its barrier: [scales of quad q+1 if s % 4 == 1], stage s+3.  The
+    // wait at the start of step s leaves in flight what steps s-2 and s-1
+    // requested (stage s was requested in step s-3, or in the prologue).
     dma_scales(0, 0);
     dma_stage(0, 0);
     dma_stage(1, 1);
     dma_stage(2, 2);
-    wait_vm<2 * T::D>();
-    barrier();
-    read_stage(0, F0);
-    read_scales(0, Q0);
     for (int q = 0; q < nq2; q += 2) {
         auto step = [&](auto v_tag) {
             constexpr int v = decltype(v_tag)::value;       // step of the two-quad body
             constexpr int u = v & 3, qp = v >> 2;
             const int s = 4 * q + v;
+            if (u == 2 || u == 3) wait_vm<2 * T::D + T::DS>();
+            else wait_vm<2 * T::D>();
+            lds_barrier();
             if (u == 1) dma_scales(q + qp + 1, qp ^ 1);
             dma_stage(s + 3, (v + 3) & 3);
-            Frag& Fc = (v & 1) ? F1 : F0;
-            Frag& Fn = (v & 1) ? F0 : F1;
-            Scales& Qc = qp ? Q1 : Q0;
-            const bool live = s < S;                       // steps past K (padding of the last quad) skip the MFMAs
-            const std::integral_constant<int, u> ut;
-            __builtin_amdgcn_sched_barrier(0);
-            if (live) mfmas(Fc, Qc, ut, 0, RTW / 2);
-            if (u == 1 || u == 2) wait_vm<2 * T::D + T::DS>();
-            else wait_vm<2 * T::D>();
-            barrier();
-            read_stage((v + 1) & 3, Fn);
-            if (u == 3) read_scales(qp ^ 1, qp ? Q0 : Q1);
-            if (live) mfmas(Fc, Qc, ut, RTW / 2, RTW);
+            const uint8_t* src = stage_buf(v & 3);
+            if (u == 0) {
+                const uint8_t* sq = qp ? sq1 : sq0;
+#pragma unroll
+                for (int rt = 0; rt < RTW; ++rt)
+                    qa[rt] = *reinterpret_cast<const uint32_t*>(sq + (wr * RTW + rt) * 256 + 4 * lane);
+#pragma unroll
+                for (int ct = 0; ct < CTW; ++ct)
+                    qb[ct] = *reinterpret_cast<const uint32_t*>(sq + (T::AFR + wc * CTW + ct) * 256 + 4 * lane);
+            }
+#pragma unroll
+            for (int rt = 0; rt < RTW; ++rt)
+                fa[rt] = *reinterpret_cast<const uint4*>(src + (wr * RTW + rt) * 1024 + 16 * lane);
+#pragma unroll
+            for (int ct = 0; ct < CTW; ++ct)
+                fb[ct] = *reinterpret_cast<const uint4*>(src + T::B_OFF + (wc * CTW + ct) * 1024 + 16 * lane);
+            if (s < S) {                                   // padding steps of the last quad: no MFMAs
+#pragma unroll
+                for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+                    for (int ct = 0; ct < CTW; ++ct)
+                        acc[rt][ct] = mfma_fp4_u<u>(fa[rt], fb[ct], acc[rt][ct], qa[rt], qb[ct]);
+            }
         };
         step(std::integral_constant<int, 0>());
         step(std::integral_constant<int, 1>());
@@ -350,42 +343,37 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_mx_dma(DmaArgs p) {
     }
 }
 
-template <bool COMP, int RTW, int CTW>
+template <bool COMP, int RTW, int CTW, int WR, int WC, int OCC>
 hipError_t launch_mx_dma(DmaArgs a, hipStream_t s) {
-    using T = DmaTile<RTW, CTW>;
-    const int B = COMP ? 2 * a.M : a.M;
-    a.row_tiles = (B + T::TM - 1) / T::TM;
-    a.tiles = (int64_t)a.row_tiles * ((num_groups(a.N) + T::BFR - 1) / T::BFR);
-    a.per_xcd = (a.tiles + kXcds - 1) / kXcds;
-    const int64_t grid = a.per_xcd * kXcds;
-    auto kern = gemm_tile_mx_dma<COMP, RTW, CTW>;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, s, a);
+    using T = MxTile<RTW, CTW, WR, WC>;
+    a.grid = tile_grid(COMP ? 2 * (int64_t)a.M : a.M, a.N, T::TM, T::TN);
+    auto kern = gemm_tile_mx_dma<COMP, RTW, CTW, WR, WC, OCC>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(a.grid.per_xcd * kXcds)), dim3(64 * T::NW), 0, s, a);
     return hipGetLastError();
 }
 
-// Tile choice (timed on the MXFP4 workload, K = 5120, N = 25600, compensated:
-// 128 x 128 tiles at M = 32 and 64, 256 x 128 at M = 128, 256 x 256 at M =
-// 256): the largest tile whose tile count still gives three quarters of the
-// compute units a tile; 256-row tiles only above 128 operand rows (below,
-// half of each tile would be empty).  128 x 128 tiles run two workgroups per
-// compute unit (72 KB of LDS each), the larger ones one.
+// Tile choice: the largest tile whose tile count still gives three quarters
+// of the compute units a tile; 256-row tiles only above 128 operand rows
+// (below, half of each tile would be empty).  256 x 256 and 256 x 128 tiles run
+// 8 waves (one workgroup per compute unit), 128 x 128 tiles 4 waves with two
+// workgroups per compute unit.
 template <bool COMP>
 hipError_t launch_mx_tiles(const DmaArgs& a, int num_cus, hipStream_t s) {
     const int64_t B = COMP ? 2 * (int64_t)a.M : a.M;
     const int64_t G = num_groups(a.N);
     const int64_t want = (3 * (int64_t)num_cus + 3) / 4;
-    if ((B + 255) / 256 * ((G + 15) / 16) >= want) return launch_mx_dma<COMP, 8, 8>(a, s);
-    if (B > 128 && (B + 255) / 256 * ((G + 7) / 8) >= want) return launch_mx_dma<COMP, 8, 4>(a, s);
-    return launch_mx_dma<COMP, 4, 4>(a, s);
+    if ((B + 255) / 256 * ((G + 15) / 16) >= want) return launch_mx_dma<COMP, 8, 4, 2, 4, 1>(a, s);
+    if (B > 128 && (B + 255) / 256 * ((G + 7) / 8) >= want) return launch_mx_dma<COMP, 8, 2, 2, 4, 1>(a, s);
+    return launch_mx_dma<COMP, 4, 4, 2, 2, 2>(a, s);
 }
 
 }  // namespace
 
-int64_t act_tile_bytes(int fmt, int64_t B, int64_t K) {
-    return (B + 15) / 16 * group_bytes(fmt, K);
+int64_t act_tile_bytes(int64_t B, int64_t K) {
+    return (B + 15) / 16 * group_bytes(kMX, K);
 }
 
-hipError_t launch_act_tile(int fmt, bool comp, const void* act, int64_t row_bytes, int M, int64_t K, void* out,
+hipError_t launch_act_tile(bool comp, const void* act, int64_t row_bytes, int M, int64_t K, void* out,
                            hipStream_t s) {
     const int64_t B = comp ? 2 * (int64_t)M : M;
     const int64_t groups = (B + 15) / 16;
@@ -393,20 +381,15 @@ hipError_t launch_act_tile(int fmt, bool comp, const void* act, int64_t row_byte
     const dim3 grid((unsigned)((items + 255) / 256));
     const uint8_t* a = static_cast<const uint8_t*>(act);
     uint8_t* o = static_cast<uint8_t*>(out);
-    if (fmt == kNV) {
-        if (comp) hipLaunchKernelGGL((act_tile_kernel<kNV, true>), grid, dim3(256), 0, s, a, row_bytes, M, K, groups, o);
-        else hipLaunchKernelGGL((act_tile_kernel<kNV, false>), grid, dim3(256), 0, s, a, row_bytes, M, K, groups, o);
-    } else {
-        if (comp) hipLaunchKernelGGL((act_tile_kernel<kMX, true>), grid, dim3(256), 0, s, a, row_bytes, M, K, groups, o);
-        else hipLaunchKernelGGL((act_tile_kernel<kMX, false>), grid, dim3(256), 0, s, a, row_bytes, M, K, groups, o);
-    }
+    if (comp) hipLaunchKernelGGL((act_tile_kernel<true>), grid, dim3(256), 0, s, a, row_bytes, M, K, groups, o);
+    else hipLaunchKernelGGL((act_tile_kernel<false>), grid, dim3(256), 0, s, a, row_bytes, M, K, groups, o);
     return hipGetLastError();
 }
 
 hipError_t launch_gemm_tile_dma(bool comp, const void* act_tiled, const void* blob, int M, int64_t N, int64_t K,
                                 void* y, bool out_bf16, int num_cus, hipStream_t s) {
     DmaArgs a{static_cast<const uint8_t*>(act_tiled), static_cast<const uint8_t*>(blob), M, N, K, y,
-              out_bf16 ? 1 : 0, 0, 0, 0};
+              out_bf16 ? 1 : 0, TileGrid{}};
     return comp ? launch_mx_tiles<true>(a, num_cus, s) : launch_mx_tiles<false>(a, num_cus, s);
 }
 

@@ -54,6 +54,8 @@ def test_size_queries():
     assert rs.workspace_bytes(1, 256, 25600, 5120, True) == 16384 + 32 * 10 * (4096 + 256)
     assert rs.workspace_bytes(1, 40, 64, 1056, False) == 16384 + 3 * 3 * (4096 + 256)
     assert rs.workspace_bytes(1, 17, 64, 1056, True) == 16384 + 3 * 3 * (4096 + 256)
+    # wide NVFP4 operands multiply the records directly: no workspace
+    assert rs.workspace_bytes(0, 128, 28672, 8192, True) == 0
     # invalid requests size to 0
     assert rs.packed_weight_bytes(0, 16, 48) == 0
     assert rs.packed_weight_bytes(2, 16, 64) == 0
