@@ -98,13 +98,12 @@ rsfp4_status quantize(int fmt, const void* x, int xt, int64_t M, int64_t K, int 
                       "quantize launch");
 }
 
-// Workspace of the MXFP4 tiled product over rewritten activations: the
-// counter area, then the tiled operand; 0 for NVFP4 and when the operand would
-// exceed kMaxTileWs (the records path then runs without it).
+// Workspace of the tiled products over rewritten activations: the counter
+// area, then the tiled operand; 0 when that would exceed kMaxTileWs (the
+// records path then runs without it).
 constexpr int64_t kMaxTileWs = (int64_t)1 << 30;
 int64_t tile_ws_bytes(int fmt, int64_t B, int64_t K) {
-    if (fmt != RSFP4_MXFP4) return 0;
-    const int64_t t = act_tile_bytes(B, K);
+    const int64_t t = act_tile_bytes(fmt, B, K);
     return t > kMaxTileWs ? 0 : kSplitCounterBytes + t;
 }
 
@@ -162,18 +161,23 @@ rsfp4_status linear(int fmt, bool comp, const void* act, size_t act_bytes, const
         if (std::getenv("RSFP4_LOG"))
             std::fprintf(stderr, "[rsfp4] linear fmt=%d comp=%d M=%lld N=%lld K=%lld tiled\n", fmt, (int)comp,
                          (long long)M, (long long)N, (long long)K);
-        // MXFP4 with a workspace that holds the activation operand rewritten in
-        // the packed-weight layout (after the counter area, which stays zero):
-        // both operands stream into LDS as contiguous 1 KB requests; same bits
-        // as the records path
+        // With a workspace that holds the activation operand rewritten in tiles
+        // (after the counter area, which stays zero; MXFP4: the packed-weight
+        // layout, both operands then streamed into LDS; NVFP4: exact f16 MFMA
+        // fragments, streamed into LDS) the activations arrive as contiguous
+        // 1 KB requests; same bits as the records path
         const int64_t tws = tile_ws_bytes(fmt, B, K);
         if (tws > 0 && (int64_t)ws_bytes >= tws) {
             int cus = 0;
             st = num_cus(&cus);
             if (st != RSFP4_OK) return st;
             void* at = static_cast<uint8_t*>(ws) + kSplitCounterBytes;
-            st = hip_status(launch_act_tile(comp, act, rb, (int)M, K, at, (hipStream_t)stream), "linear launch");
+            st = hip_status(launch_act_tile(fmt, comp, act, rb, (int)M, K, at, (hipStream_t)stream), "linear launch");
             if (st != RSFP4_OK) return st;
+            if (fmt == RSFP4_NVFP4)
+                return hip_status(launch_gemm_tile_dma_nv(comp, at, act, rb, w_packed, (int)M, N, K, y, out_bf16,
+                                                          (hipStream_t)stream),
+                                  "linear launch");
             return hip_status(launch_gemm_tile_dma(comp, at, w_packed, (int)M, N, K, y, out_bf16, cus,
                                                    (hipStream_t)stream),
                               "linear launch");
@@ -441,8 +445,10 @@ size_t rsfp4_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, int compe
         return 0;
     const int64_t B = compensated ? 2 * M : M;
     const int64_t S = num_steps(K);
-    // wide MXFP4 operands: the tiled activation operand after the counter area
-    if (B > 32 && fmt == RSFP4_MXFP4) return (size_t)tile_ws_bytes(fmt, B, K);
+    // wide operands on the tiled kernels (not the four-row-tile narrow plan of
+    // compensated NVFP4): the rewritten activation operand after the counter area
+    const bool narrow4 = fmt == RSFP4_NVFP4 && compensated && B <= 64 && K <= kMaxNarrowK && N <= 16384;
+    if (B > 32 && !narrow4) return (size_t)tile_ws_bytes(fmt, B, K);
     // the split applies to one-pass plans of the narrow kernel with one or two
     // row tiles
     if (B > 32 || K > kMaxNarrowK) return 0;

@@ -76,6 +76,46 @@ __global__ __launch_bounds__(256) void act_tile_kernel(const uint8_t* __restrict
     }
 }
 
+
+// NVFP4: one thread per (16-row group, step, lane): the lane's 32 codes and
+// their two E4M3 block scales -> four 16-byte f16 fragments e * S_b (exact, the
+// values the register-staged kernel forms in LDS; the tensor scale stays out,
+// applied in the epilogue), one per 32-element sub-step of the f16 MFMA, at
+// group * S * 4 KB + step * 4 KB + u * 1 KB.
+template <bool COMP>
+__global__ __launch_bounds__(256) void act_tile_f16_kernel(const uint8_t* __restrict__ act, int64_t row_bytes, int M,
+                                                           int64_t K, int64_t groups, uint8_t* __restrict__ out) {
+    const int64_t S = num_steps(K);
+    const int64_t item = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (item >= groups * S * 64) return;
+    const int64_t grp = item / (S * 64);
+    const int64_t r = item - grp * S * 64;
+    const int64_t s = r >> 6;
+    const int l = (int)(r & 63), g = l >> 4, i = l & 15;
+    const int64_t R = 16 * grp + i;
+    int64_t rec = -1;
+    if (COMP) {
+        const int64_t m = R >> 1;
+        if (m < M) rec = ((R & 1) ? M + m : m) * row_bytes;
+    } else if (R < M) {
+        rec = R * row_bytes;
+    }
+    const int64_t k = s * kStepK + 32 * g;
+    uint4 c = make_uint4(0u, 0u, 0u, 0u);
+    uint32_t sc = 0u;
+    if (rec >= 0 && k < K) {
+        c = *reinterpret_cast<const uint4*>(act + rec + kActHead + k / 2);
+        const uint8_t* sp = act + rec + kActHead + K / 2 + k / 16;     // blocks 2g, 2g+1 of the step
+        sc = (uint32_t)sp[0] | ((uint32_t)sp[1] << 8);
+    }
+    uint8_t* dst = out + grp * S * 4096 + s * 4096 + 16 * l;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const half8 h = dequant8(word(c, u), scale_h(u < 2 ? (sc & 0xFFu) : (sc >> 8)));
+        *reinterpret_cast<half8*>(dst + u * 1024) = h;
+    }
+}
+
 // ---- 2. the tiled products ----
 // Both kernels stream the two tiled operands into a ring of LDS stages with
 // the buffer loads' LDS-DMA form (each request: 64 lanes x 16 bytes, one
@@ -367,22 +407,223 @@ hipError_t launch_mx_tiles(const DmaArgs& a, int num_cus, hipStream_t s) {
     return launch_mx_dma<COMP, 4, 4, 2, 2, 2>(a, s);
 }
 
+
+// ---- NVFP4: f16 activation fragments (DMA) x weights from a register ring ----
+// The register-staged kernel's structure (4 waves, two workgroups per compute
+// unit; a workgroup owns 128 rows x 128 channels, each wave all 128 rows and
+// its own 2 groups of 16 channels, whose weight fragments it streams into a
+// register ring 3 steps ahead and dequantizes to f16 at use, the scale words a
+// quad ahead), with the activation staging replaced: the f16 fragments of each
+// step (32 KB) stream into one of two LDS stages by DMA instead of passing
+// through registers, a dequantization and LDS stores in every workgroup.  Same
+// f16 operands and MFMA order as that kernel: bit-identical results.
+struct NvArgs {
+    const uint8_t* at;     // f16 activation fragments (act_tile_f16_kernel)
+    const uint8_t* act;    // the activation records (per-row tensor scales)
+    int64_t row_bytes;
+    const uint8_t* blob;
+    int M;
+    int64_t N;
+    int64_t K;
+    void* y;
+    int out_bf16;
+    TileGrid grid;
+};
+
+template <bool COMP>
+__global__ __launch_bounds__(256, 2) void gemm_tile_nv_dma(NvArgs p) {
+    constexpr int RTW = 8, CTW = 2, RD = 4;           // 16-row tiles, 16-channel groups per wave; ring depth
+    constexpr int TM = 16 * RTW, GPT = 4 * CTW;       // workgroup rows, channel groups
+    constexpr int STAGE = RTW * 4096;                 // one step of TM rows as f16: [u4][rt] blocks of 1 KB
+    constexpr int DA = 4 * RTW / 4;                   // per-wave requests of one stage
+    __shared__ __attribute__((aligned(16))) uint8_t st0[STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t st1[STAGE];
+
+    int rtile;
+    int64_t ctile;
+    if (!tile_of(p.grid, &rtile, &ctile)) return;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4, i = lane & 15;
+    const int S = (int)num_steps(p.K);
+    const int nq2 = (((S + kQuadSteps - 1) / kQuadSteps) + 1) & ~1;
+    const int64_t GB = group_bytes(kNV, p.K), QB = quad_bytes(kNV);
+    const int64_t GA = (int64_t)S * 4096;             // f16 fragments of one 16-row group
+    const int B = COMP ? 2 * p.M : p.M;
+    const int64_t NGA = (B + 15) / 16, G = num_groups(p.N);
+    const int64_t a0 = (int64_t)rtile * RTW;
+    const uint8_t* abase = p.at + a0 * GA;
+    const int64_t abytes = (NGA - a0 < RTW ? NGA - a0 : RTW) * GA;
+    const int64_t cw = ctile * GPT + wave * CTW;      // this wave's weight groups
+    const int64_t live = G - cw < 0 ? 0 : (G - cw < CTW ? G - cw : CTW);
+    const uint8_t* wbase = p.blob + kWHeader + (live > 0 ? cw : 0) * GB;
+    const int64_t wbytes = live * GB;
+
+    // activation request j of this wave: block wave + 4j = (16-row tile rt, sub-step u4)
+    uint32_t a_vo[DA];
+    int a_dst[DA];
+#pragma unroll
+    for (int j = 0; j < DA; ++j) {
+        const int blk = wave + 4 * j, rt = blk >> 2, u4 = blk & 3;
+        a_vo[j] = (uint32_t)(rt * GA) + (uint32_t)(u4 * 1024) + 16u * lane;
+        a_dst[j] = (u4 * RTW + rt) * 1024;
+    }
+    uint32_t b_vo[CTW], bs_vo[CTW];
+#pragma unroll
+    for (int ct = 0; ct < CTW; ++ct) {
+        b_vo[ct] = (uint32_t)(ct * GB) + 16u * lane;
+        bs_vo[ct] = (uint32_t)(ct * GB) + kQuadSteps * kStepCodes + 8u * lane;
+    }
+    auto dma_a = [&](int s, uint8_t* dst) {
+        const __amdgpu_buffer_rsrc_t r = rsrc_at(abase, (int64_t)s * 4096, abytes);
+#pragma unroll
+        for (int j = 0; j < DA; ++j) dma16(r, dst + a_dst[j], a_vo[j]);
+    };
+    uint4 ring[RD][CTW];
+    u32x2 sw[2][CTW];
+    auto load_b = [&](int s, int slot) {
+        const __amdgpu_buffer_rsrc_t r =
+            rsrc_at(wbase, (int64_t)(s / kQuadSteps) * QB + (s % kQuadSteps) * kStepCodes, wbytes);
+#pragma unroll
+        for (int ct = 0; ct < CTW; ++ct) ring[slot][ct] = ld128(r, b_vo[ct]);
+    };
+    auto load_sw = [&](int q, int slot) {
+        const __amdgpu_buffer_rsrc_t r = rsrc_at(wbase, (int64_t)q * QB, wbytes);
+#pragma unroll
+        for (int ct = 0; ct < CTW; ++ct) sw[slot][ct] = __builtin_amdgcn_raw_buffer_load_b64(r, bs_vo[ct], 0, 0);
+    };
+
+    floatx4 acc[RTW][CTW];
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < CTW; ++ct) acc[rt][ct] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // Requests in program order: prologue [scales q0, weights of steps
+    // 0..RD-3, activations of step 0, weights of step RD-2]; step s, after its
+    // barrier: activations of step s+1, [scales of quad q+1 if s % 4 == 0],
+    // weights of step s+RD-1.  The wait at the start of step s leaves in
+    // flight the weight and scale loads requested after step s's activations.
+    load_sw(0, 0);
+#pragma unroll
+    for (int r = 0; r < RD - 2; ++r) load_b(r, r);
+    dma_a(0, st0);
+    load_b(RD - 2, RD - 2);
+    for (int q = 0; q < nq2; q += 2) {
+        auto step = [&](auto v_tag) {
+            constexpr int v = decltype(v_tag)::value;   // step of the two-quad body
+            constexpr int u = v & 3, qs = v >> 2;
+            const int s = 4 * q + v;
+            if (u == 1) wait_vm<2 * CTW>();
+            else wait_vm<CTW>();
+            lds_barrier();
+            dma_a(s + 1, (v & 1) ? st0 : st1);
+            if (u == 0) load_sw(q + qs + 1, qs ^ 1);
+            load_b(s + RD - 1, (v + RD - 1) % RD);
+            const uint8_t* cur = (v & 1) ? st1 : st0;
+            constexpr int slot = v % RD;
+            if (s < S) {
+#pragma unroll
+                for (int u4 = 0; u4 < 4; ++u4) {
+                    half8 ah[RTW], bh[CTW];
+#pragma unroll
+                    for (int rt = 0; rt < RTW; ++rt)
+                        ah[rt] = *reinterpret_cast<const half8*>(cur + (u4 * RTW + rt) * 1024 + 16 * lane);
+#pragma unroll
+                    for (int ct = 0; ct < CTW; ++ct) {
+                        const uint32_t sword = u < 2 ? sw[qs][ct][0] : sw[qs][ct][1];
+                        const uint32_t sb = (sword >> (16 * (u & 1) + (u4 < 2 ? 0 : 8))) & 0xFFu;
+                        bh[ct] = dequant8(word(ring[slot][ct], u4), scale_h(sb));
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+                        for (int ct = 0; ct < CTW; ++ct)
+                            acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[rt], bh[ct], acc[rt][ct], 0, 0, 0);
+                }
+            }
+        };
+        step(std::integral_constant<int, 0>());
+        step(std::integral_constant<int, 1>());
+        step(std::integral_constant<int, 2>());
+        step(std::integral_constant<int, 3>());
+        step(std::integral_constant<int, 4>());
+        step(std::integral_constant<int, 5>());
+        step(std::integral_constant<int, 6>());
+        step(std::integral_constant<int, 7>());
+    }
+    wait_vm<0>();
+
+    // ---- Fold + store: lane holds rows 16rt + 4g + r of channel 16(cw+ct) + i ----
+    const float s_gw = reinterpret_cast<const WHeader*>(p.blob)->s_g;
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+#pragma unroll
+        for (int ct = 0; ct < CTW; ++ct) {
+            const int64_t n = 16 * (cw + ct) + i;
+            if (n >= p.N) continue;
+#pragma unroll
+            for (int pr = 0; pr < 2; ++pr) {
+                const int R0 = TM * rtile + 16 * rt + 4 * g + 2 * pr;
+                const float v0 = acc[rt][ct][2 * pr], v1 = acc[rt][ct][2 * pr + 1];
+                if (COMP) {
+                    const int m = R0 >> 1;
+                    if (m < p.M) {
+                        const float sx = *reinterpret_cast<const float*>(p.act + (int64_t)m * p.row_bytes);
+                        const float sr = *reinterpret_cast<const float*>(p.act + (int64_t)(p.M + m) * p.row_bytes);
+                        store_y(p.y, (int64_t)m * p.N + n, s_gw * (sx * v0 + sr * v1), p.out_bf16);
+                    }
+                } else {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int m = R0 + h;
+                        if (m < p.M) {
+                            const float sx = *reinterpret_cast<const float*>(p.act + (int64_t)m * p.row_bytes);
+                            store_y(p.y, (int64_t)m * p.N + n, s_gw * (sx * (h ? v1 : v0)), p.out_bf16);
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
 }  // namespace
 
-int64_t act_tile_bytes(int64_t B, int64_t K) {
+int64_t act_tile_bytes(int fmt, int64_t B, int64_t K) {
+    if (fmt == kNV) return (B + 15) / 16 * num_steps(K) * 4096;
     return (B + 15) / 16 * group_bytes(kMX, K);
 }
 
-hipError_t launch_act_tile(bool comp, const void* act, int64_t row_bytes, int M, int64_t K, void* out,
+hipError_t launch_act_tile(int fmt, bool comp, const void* act, int64_t row_bytes, int M, int64_t K, void* out,
                            hipStream_t s) {
     const int64_t B = comp ? 2 * (int64_t)M : M;
     const int64_t groups = (B + 15) / 16;
-    const int64_t items = groups * num_quads(K) * 320;
-    const dim3 grid((unsigned)((items + 255) / 256));
     const uint8_t* a = static_cast<const uint8_t*>(act);
     uint8_t* o = static_cast<uint8_t*>(out);
-    if (comp) hipLaunchKernelGGL((act_tile_kernel<true>), grid, dim3(256), 0, s, a, row_bytes, M, K, groups, o);
-    else hipLaunchKernelGGL((act_tile_kernel<false>), grid, dim3(256), 0, s, a, row_bytes, M, K, groups, o);
+    if (fmt == kNV) {
+        const dim3 grid((unsigned)((groups * num_steps(K) * 64 + 255) / 256));
+        if (comp) hipLaunchKernelGGL((act_tile_f16_kernel<true>), grid, dim3(256), 0, s, a, row_bytes, M, K, groups, o);
+        else hipLaunchKernelGGL((act_tile_f16_kernel<false>), grid, dim3(256), 0, s, a, row_bytes, M, K, groups, o);
+    } else {
+        const dim3 grid((unsigned)((groups * num_quads(K) * 320 + 255) / 256));
+        if (comp) hipLaunchKernelGGL((act_tile_kernel<true>), grid, dim3(256), 0, s, a, row_bytes, M, K, groups, o);
+        else hipLaunchKernelGGL((act_tile_kernel<false>), grid, dim3(256), 0, s, a, row_bytes, M, K, groups, o);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_tile_dma_nv(bool comp, const void* act_tiled, const void* act, int64_t row_bytes,
+                                   const void* blob, int M, int64_t N, int64_t K, void* y, bool out_bf16,
+                                   hipStream_t s) {
+    NvArgs a{static_cast<const uint8_t*>(act_tiled), static_cast<const uint8_t*>(act), row_bytes,
+             static_cast<const uint8_t*>(blob), M, N, K, y, out_bf16 ? 1 : 0, TileGrid{}};
+    a.grid = tile_grid(comp ? 2 * (int64_t)M : M, N, 128, 128);
+    const dim3 grid((unsigned)(a.grid.per_xcd * kXcds));
+    if (comp) hipLaunchKernelGGL((gemm_tile_nv_dma<true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((gemm_tile_nv_dma<false>), grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -109,11 +109,16 @@ hipError_t launch_gemm_tile(int fmt, bool comp, const void* act, int64_t row_byt
 // records rewritten into the packed-weight layout (groups of 16 stacked rows,
 // base and residue rows interleaved; act_tile_bytes bytes), then the tiled
 // product of the two (gemm_tile_dma.hip).
-int64_t act_tile_bytes(int64_t B, int64_t K);
-hipError_t launch_act_tile(bool comp, const void* act, int64_t row_bytes, int M, int64_t K, void* out,
+int64_t act_tile_bytes(int fmt, int64_t B, int64_t K);
+hipError_t launch_act_tile(int fmt, bool comp, const void* act, int64_t row_bytes, int M, int64_t K, void* out,
                            hipStream_t s);
 hipError_t launch_gemm_tile_dma(bool comp, const void* act_tiled, const void* blob, int M, int64_t N, int64_t K,
                                 void* y, bool out_bf16, int num_cus, hipStream_t s);
+// NVFP4: the activations rewritten as exact f16 MFMA fragments (4 KB per 16
+// rows and step), streamed into LDS by DMA; weights from a register ring.
+hipError_t launch_gemm_tile_dma_nv(bool comp, const void* act_tiled, const void* act, int64_t row_bytes,
+                                   const void* blob, int M, int64_t N, int64_t K, void* y, bool out_bf16,
+                                   hipStream_t s);
 
 // Paper-numerics NVFP4 quantizer (tensor scale alpha from device memory, shared
 // by x and r; multiplier-scale codes and residue) and the alpha of a tensor.

@@ -54,8 +54,11 @@ def test_size_queries():
     assert rs.workspace_bytes(1, 256, 25600, 5120, True) == 16384 + 32 * 10 * (4096 + 256)
     assert rs.workspace_bytes(1, 40, 64, 1056, False) == 16384 + 3 * 3 * (4096 + 256)
     assert rs.workspace_bytes(1, 17, 64, 1056, True) == 16384 + 3 * 3 * (4096 + 256)
-    # wide NVFP4 operands multiply the records directly: no workspace
-    assert rs.workspace_bytes(0, 128, 28672, 8192, True) == 0
+    # NVFP4: 4 KB of f16 fragments per 16 rows and step (33..64 compensated
+    # rows with N, K <= 16384 take the narrow kernel and no such workspace)
+    assert rs.workspace_bytes(0, 128, 28672, 8192, True) == 16384 + 16 * 64 * 4096
+    assert rs.workspace_bytes(0, 40, 64, 1056, False) == 16384 + 3 * 9 * 4096
+    assert rs.workspace_bytes(0, 20, 28672, 8192, True) == 16384 + 3 * 64 * 4096
     # invalid requests size to 0
     assert rs.packed_weight_bytes(0, 16, 48) == 0
     assert rs.packed_weight_bytes(2, 16, 64) == 0

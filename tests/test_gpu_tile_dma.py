@@ -1,7 +1,7 @@
-"""GPU parity of the wide MXFP4 linear over LDS-DMA streamed operands: the
-activation records are rewritten into the packed-weight layout (in the
-workspace of rsfp4_workspace_bytes, after its counter area), then both tiled
-operands are multiplied.  Against the oracle elementwise, and bit for bit
+"""GPU parity of the wide linear over LDS-DMA streamed activations: the
+activation records are rewritten in tiles (MXFP4: the packed-weight layout,
+both operands then streamed into LDS; NVFP4: exact f16 MFMA fragments) in the
+workspace of rsfp4_workspace_bytes, after its counter area, then multiplied.  Against the oracle elementwise, and bit for bit
 against the register-staged tiled kernel that a call with a smaller workspace
 runs (both sum the same MFMAs in the same order); the workspace's counters
 stay zero, and graph replays match the eager call."""
@@ -38,11 +38,14 @@ CASES = [(17, 264, 384, True), (33, 130, 160, False), (40, 512, 1056, True), (64
          (100, 72, 2048, False), (129, 300, 512, True), (40, 64, 24576, True), (30, 16400, 256, True),
          (200, 1000, 1184, True), (48, 520, 5152, False), (300, 40, 96, True), (37, 2056, 4096, True),
          (20, 16400, 4096, True)]
-FMT_CASES = [(1,) + c for c in CASES]
+# NVFP4 compensated with 33..64 stacked rows, N <= 16384 and K <= 16384 runs
+# the narrow kernel with four row tiles instead: those shapes are left out
+NV_NARROW4 = lambda M, N, K, comp: comp and 2 * M <= 64 and N <= 16384 and K <= 16384
+FMT_CASES = [(f,) + c for f in (0, 1) for c in CASES if not (f == 0 and NV_NARROW4(*c))]
 
 
 def _cid(c):
-    return "M%dN%dK%d%s" % (c[1], c[2], c[3], "c" if c[4] else "p")
+    return "%s-M%dN%dK%d%s" % ("nv" if c[0] == 0 else "mx", c[1], c[2], c[3], "c" if c[4] else "p")
 
 
 def _setup(fmt, M, N, K, comp, seed):
@@ -78,10 +81,11 @@ def _ws(fmt, M, N, K, comp):
 
 
 def _group_bytes(fmt, K):
-    """Bytes of 16 rows of the rewritten activations: quads of 4 steps (4 KB
-    of codes + 256 B of scale words)."""
-    assert fmt == 1
-    return -(-K // 512) * (4 * 1024 + 256)
+    """Bytes of 16 rows of the rewritten activations: MXFP4 quads of 4 steps
+    (4 KB of codes + 256 B of scale words), NVFP4 4 KB of f16 per step."""
+    if fmt == 1:
+        return -(-K // 512) * (4 * 1024 + 256)
+    return -(-K // 128) * 4096
 
 
 def _small_ws():
@@ -116,10 +120,11 @@ def test_dma_path_bitwise_equals_register_staged(case, bf16):
     assert torch.equal(a, b), f"{int((a != b).sum())} of {a.numel()} outputs differ"
 
 
-@pytest.mark.parametrize("wl", [inputs.MX.with_m(m) for m in (17, 32, 64, 128, 256)], ids=lambda w: f"M{w.M}")
+@pytest.mark.parametrize("wl", [inputs.MX.with_m(m) for m in (17, 32, 64, 128, 256)]
+                         + [inputs.LARGE_MLP.with_m(m) for m in (17, 32, 64, 128)], ids=lambda w: f"{w.name}_M{w.M}")
 def test_dma_path_workload(wl):
-    """The MXFP4 workload at full size (K = 5120, N = 25600) as the bench
-    launches it: bit for bit against the register-staged kernel, and a
+    """The MXFP4 and large-MLP NVFP4 workloads at full size, as the bench
+    launches them: bit for bit against the register-staged kernel, and a
     sample of output channels against the oracle."""
     import torch
     fmt = 1 if wl.fmt == "mxfp4" else 0
@@ -142,7 +147,8 @@ def test_dma_path_workload(wl):
 # Ragged shapes large enough for the 256-row tiles on a 256-CU device:
 # 256 x 256 tiles (3 row tiles, the last with 8 rows; 65 channel tiles, the
 # last with one group) and 256 x 128 tiles (one row tile of 240 rows)
-WIDE_CASES = [(1, 260, 16400, 1184, True), (1, 120, 24600, 1056, True), (1, 250, 24600, 672, False)]
+WIDE_CASES = [(1, 260, 16400, 1184, True), (1, 120, 24600, 1056, True), (1, 250, 24600, 672, False),
+              (0, 130, 28700, 1184, True), (0, 200, 16400, 800, False)]
 
 
 @pytest.mark.parametrize("case", WIDE_CASES, ids=_cid)
@@ -162,11 +168,12 @@ def test_dma_path_large_tiles(case):
     check_linear(y_dma.cpu().numpy()[:, rows], yo, beta)
 
 
-def test_dma_path_graph_replays():
+@pytest.mark.parametrize("fmt", [0, 1], ids=["nv", "mx"])
+def test_dma_path_graph_replays(fmt):
     """Rewrite + product captured in a HIP graph: every replay (with eager
     work between them) equals the eager call bit for bit."""
     import torch
-    fmt, M, N, K = 1, 96, 2056, 2048
+    M, N, K = 96, 2056, 2048
     _, _, blob, act = _setup(fmt, M, N, K, True, 99)
     ws = _ws(fmt, M, N, K, True)
     y_eager = _call(fmt, act, blob, M, N, K, True, ws).clone()
