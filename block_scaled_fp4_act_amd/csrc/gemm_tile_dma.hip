@@ -194,9 +194,9 @@ inline TileGrid tile_grid(int64_t B, int64_t N, int TM, int TN) {
 // ---- MXFP4: both operands in the packed-weight layout ----
 // WR x WC waves; a wave owns RTW x CTW output tiles of 16 x 16, the workgroup
 // TM = 16*RTW*WR rows x TN = 16*CTW*WC channels.  A stage holds one step's
-// fragments of both operands; 4 stages rotate (stage s+3 requested in step s),
-// and a 2-slot ring holds the scale words of the current and the next quad
-// (requested in the quad's second step, read in its first).  Each step's MFMAs
+// fragments of both operands; 4 stages rotate (stage s+4 requested in step s,
+// after its barrier), and a 2-slot ring holds the scale words of the current
+// and the next quad (requested in a quad's second step, read in its last).  Each step's MFMAs
 // are v_mfma_scale_f32_16x16x128_f8f6f4 (FP4 x FP4 with both operands' E8M0
 // scales, the quad step selecting the scale byte), summed over the steps in
 // order, as the register-staged kernel does: the result is bit-identical.
@@ -294,59 +294,88 @@ __global__ __launch_bounds__(64 * WR * WC, OCC) void gemm_tile_mx_dma(DmaArgs p)
         for (int j = 0; j < T::DB; ++j) dma4(rb, dst + (T::AFR + wave + T::NW * j) * 256, bs_vo[j]);
     };
 
-    uint4 fa[RTW], fb[CTW];
-    uint32_t qa[RTW], qb[CTW];
+    struct Frag {
+        uint4 a[RTW];
+        uint4 b[CTW];
+    };
+    struct Scales {
+        uint32_t a[RTW];
+        uint32_t b[CTW];
+    };
+    Frag F0, F1;
+    Scales Q0, Q1;
     floatx4 acc[RTW][CTW];
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
         for (int ct = 0; ct < CTW; ++ct) acc[rt][ct] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    auto read_stage = [&](int b, Frag& F) {
+        const uint8_t* src = stage_buf(b);
+#pragma unroll
+        for (int rt = 0; rt < RTW; ++rt)
+            F.a[rt] = *reinterpret_cast<const uint4*>(src + (wr * RTW + rt) * 1024 + 16 * lane);
+#pragma unroll
+        for (int ct = 0; ct < CTW; ++ct)
+            F.b[ct] = *reinterpret_cast<const uint4*>(src + T::B_OFF + (wc * CTW + ct) * 1024 + 16 * lane);
+    };
+    auto read_scales = [&](int slot, Scales& Q) {
+        const uint8_t* sq = slot ? sq1 : sq0;
+#pragma unroll
+        for (int rt = 0; rt < RTW; ++rt)
+            Q.a[rt] = *reinterpret_cast<const uint32_t*>(sq + (wr * RTW + rt) * 256 + 4 * lane);
+#pragma unroll
+        for (int ct = 0; ct < CTW; ++ct)
+            Q.b[ct] = *reinterpret_cast<const uint32_t*>(sq + (T::AFR + wc * CTW + ct) * 256 + 4 * lane);
+    };
+    auto mfmas = [&](const Frag& F, const Scales& Q, auto u_tag, int rt0, int rt1) {
+        constexpr int U = decltype(u_tag)::value;
+#pragma unroll
+        for (int rt = rt0; rt < rt1; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < CTW; ++ct)
+                acc[rt][ct] = mfma_fp4_u<U>(F.a[rt], F.b[ct], acc[rt][ct], Q.a[rt], Q.b[ct]);
+    };
 
-    // Requests in program order: prologue [scales q0, stages 0, 1, 2]; step s,
-    // after its barrier: [scales of quad q+1 if s % 4 == 1], stage s+3.  The
-    // wait at the start of step s leaves in flight what steps s-2 and s-1
-    // requested (stage s was requested in step s-3, or in the prologue).
-    // Requests in program order: prologue [scales q0, stages 0, 1, 2]; step s,
-    // after its barrier: [scales of quad q+1 if s % 4 == 1], stage s+3.  The
-    // wait at the start of step s leaves in flight what steps s-2 and s-1
-    // requested (stage s was requested in step s-3, or in the prologue).
+    // Step s runs the first half of its MFMAs on fragments read during step
+    // s-1, waits for stage s+1 and passes the barrier (all waves' reads of
+    // stage s are then done), requests stage s+4 into stage s's buffer, reads
+    // stage s+1's fragments into the other register set and runs its second
+    // half: the reads overlap MFMAs instead of following the barrier.
+    // Requests in program order: prologue [scales q0, stages 0..3]; step s,
+    // after its barrier: [scales of quad q+1 if s % 4 == 1], stage s+4.  The
+    // wait for stage s+1 (requested in step s-3, or the prologue) leaves in
+    // flight stages s+2 and s+3, and at s % 4 == 2 the next quad's scales
+    // (requested in step s-1); at s % 4 == 3 those scales are read after the
+    // barrier, so the wait covers them too.
     dma_scales(0, 0);
     dma_stage(0, 0);
     dma_stage(1, 1);
     dma_stage(2, 2);
+    dma_stage(3, 3);
+    wait_vm<3 * T::D>();
+    lds_barrier();
+    read_stage(0, F0);
+    read_scales(0, Q0);
     for (int q = 0; q < nq2; q += 2) {
         auto step = [&](auto v_tag) {
             constexpr int v = decltype(v_tag)::value;       // step of the two-quad body
             constexpr int u = v & 3, qp = v >> 2;
             const int s = 4 * q + v;
-            if (u == 2 || u == 3) wait_vm<2 * T::D + T::DS>();
+            Frag& Fc = (v & 1) ? F1 : F0;
+            Frag& Fn = (v & 1) ? F0 : F1;
+            Scales& Qc = qp ? Q1 : Q0;
+            const std::integral_constant<int, u> ut;
+            const bool live = s < S;                       // padding steps of the last quad: no MFMAs
+            __builtin_amdgcn_sched_barrier(0);
+            if (live) mfmas(Fc, Qc, ut, 0, RTW / 2);
+            if (u == 2) wait_vm<2 * T::D + T::DS>();
             else wait_vm<2 * T::D>();
             lds_barrier();
             if (u == 1) dma_scales(q + qp + 1, qp ^ 1);
-            dma_stage(s + 3, (v + 3) & 3);
-            const uint8_t* src = stage_buf(v & 3);
-            if (u == 0) {
-                const uint8_t* sq = qp ? sq1 : sq0;
-#pragma unroll
-                for (int rt = 0; rt < RTW; ++rt)
-                    qa[rt] = *reinterpret_cast<const uint32_t*>(sq + (wr * RTW + rt) * 256 + 4 * lane);
-#pragma unroll
-                for (int ct = 0; ct < CTW; ++ct)
-                    qb[ct] = *reinterpret_cast<const uint32_t*>(sq + (T::AFR + wc * CTW + ct) * 256 + 4 * lane);
-            }
-#pragma unroll
-            for (int rt = 0; rt < RTW; ++rt)
-                fa[rt] = *reinterpret_cast<const uint4*>(src + (wr * RTW + rt) * 1024 + 16 * lane);
-#pragma unroll
-            for (int ct = 0; ct < CTW; ++ct)
-                fb[ct] = *reinterpret_cast<const uint4*>(src + T::B_OFF + (wc * CTW + ct) * 1024 + 16 * lane);
-            if (s < S) {                                   // padding steps of the last quad: no MFMAs
-#pragma unroll
-                for (int rt = 0; rt < RTW; ++rt)
-#pragma unroll
-                    for (int ct = 0; ct < CTW; ++ct)
-                        acc[rt][ct] = mfma_fp4_u<u>(fa[rt], fb[ct], acc[rt][ct], qa[rt], qb[ct]);
-            }
+            dma_stage(s + 4, v & 3);
+            read_stage((v + 1) & 3, Fn);
+            if (u == 3) read_scales(qp ^ 1, qp ? Q0 : Q1);
+            if (live) mfmas(Fc, Qc, ut, RTW / 2, RTW);
         };
         step(std::integral_constant<int, 0>());
         step(std::integral_constant<int, 1>());
