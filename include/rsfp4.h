@@ -128,15 +128,20 @@ size_t rsfp4_packed_weight_bytes(int fmt, int64_t N, int64_t K);
  * order (calls that may run concurrently need workspaces of their own).  The slices' partials are
  * summed in slice order, so the result does not depend on timing.  A linear
  * call given a NULL or smaller workspace runs the plan without the split
- * (same result up to the summation order of the slices).  MXFP4 with more than
- * 32 operand rows (2M compensated, M plain) uses the workspace differently:
- * after the same 16384-byte counter area (left untouched) the call rewrites the
- * activation records into the packed-weight layout (groups of 16 operand rows,
- * base and residue rows interleaved, 4352 bytes per group and quad of 4 steps;
- * 16384 + ceil(B/16) * ceil(K/512) * 4352 bytes in all), so that both operands
- * of the tiled product stream into LDS as contiguous 1 KB requests; given a
- * NULL or smaller workspace the call multiplies the records directly, with the
- * same bits.  ws must be 256-byte aligned. */
+ * (same result up to the summation order of the slices).  Wide operands, more
+ * than 32 operand rows B (2M compensated, M plain), use the workspace
+ * differently (except compensated NVFP4 with 33..64 rows, N <= 16384 and
+ * K <= 16384, which runs the narrow kernel): after the same 16384-byte counter
+ * area (left untouched) the call rewrites the activation records in tiles of
+ * 16 operand rows, base and residue rows interleaved -- MXFP4 in the
+ * packed-weight layout (4352 bytes per tile and quad of 4 steps: 16384 +
+ * ceil(B/16) * ceil(K/512) * 4352 bytes in all), NVFP4 as the exact f16
+ * products e * S_b in MFMA fragment order (4096 bytes per tile and step of 128:
+ * 16384 + ceil(B/16) * ceil(K/128) * 4096 bytes) -- so that the activations
+ * stream into LDS as contiguous 1 KB requests.  Given a NULL or smaller
+ * workspace the call multiplies the records directly, with the same bits.
+ * Wide shapes whose rewritten operand would exceed 1 GiB size to 0 (no
+ * rewrite).  ws must be 256-byte aligned. */
 size_t rsfp4_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, int compensated);
 
 /* ------------------------------------------------------------- prepack ----
@@ -186,8 +191,8 @@ rsfp4_status rsfp4_mxfp4_quantize_act_with_residue(const void* x, int xt, int64_
  * the size queries.  ws, ws_bytes: the optional workspace of
  * rsfp4_workspace_bytes (NULL, 0 for none; 256-byte aligned, counters zero on
  * first use, left zero); with it, compensated NVFP4 shapes that gain from it
- * split K across workgroups, and wide MXFP4 operands take the tiled product
- * over rewritten activations (same bits as without). */
+ * split K across workgroups, and wide operands take the tiled product over
+ * rewritten activations (same bits as without). */
 rsfp4_status rsfp4_nvfp4_linear(const void* act, size_t act_bytes, const void* w_packed,
                                 size_t w_packed_bytes, int64_t M, int64_t N, int64_t K,
                                 float* y, void* ws, size_t ws_bytes, void* stream);
