@@ -555,11 +555,17 @@ rsfp4_status rsfp4_stream_read(const void* src, size_t bytes, void* sink, void* 
 rsfp4_status rsfp4_nvfp4_linear_compensated_noalloc(const void* act, size_t act_bytes, const void* w_packed,
                                                     size_t w_packed_bytes, int64_t M, int64_t N, int64_t K,
                                                     float* y, void* stream) {
-    const size_t need = rsfp4_workspace_bytes(RSFP4_NVFP4, M, N, K, 1);
-    if (need > (size_t)scratch_bytes())
-        return fail(RSFP4_ERR_UNSUPPORTED, "this shape's split needs %zu bytes of workspace; the library's scratch "
-                    "holds %lld (use rsfp4_nvfp4_linear_compensated with a workspace)", need,
-                    (long long)scratch_bytes());
+    size_t need = rsfp4_workspace_bytes(RSFP4_NVFP4, M, N, K, 1);
+    if (need > (size_t)scratch_bytes()) {
+        // a wide operand's workspace holds its rewritten activations, which
+        // are optional (the records path gives the same bits): run without
+        if (M >= 1 && 2 * M > kNarrowRows && need == (size_t)tile_ws_bytes(RSFP4_NVFP4, 2 * M, K))
+            need = 0;
+        else
+            return fail(RSFP4_ERR_UNSUPPORTED, "this shape's split needs %zu bytes of workspace; the library's "
+                        "scratch holds %lld (use rsfp4_nvfp4_linear_compensated with a workspace)", need,
+                        (long long)scratch_bytes());
+    }
     void* ws = nullptr;
     if (need > 0) {
         const rsfp4_status st = hip_status(scratch_ptr((hipStream_t)stream, &ws), "library scratch");

@@ -213,9 +213,13 @@ rsfp4_status rsfp4_mxfp4_linear_compensated(const void* act, size_t act_bytes, c
  * Where the plan splits K it uses the library's own scratch, a device array of
  * 16384 + 16777216 bytes on each GPU (held until the process ends; its address
  * is taken, and its counter area cleared on `stream`, by the first call on a
- * device).  It calls no allocator.  Shapes whose split would need more than
- * the scratch holds are rejected with RSFP4_ERR_UNSUPPORTED (none of the
- * plans this library makes on a 256-CU device does).  Every call on a GPU
+ * device).  Wide operands (more than 64 operand rows, or N or K above 16384)
+ * use the scratch for their rewritten activations when those fit in it (at
+ * most 16777216 bytes: ceil(2M/16) * ceil(K/128) * 4096), and otherwise run
+ * without them, with the same bits.  It calls no allocator.  Shapes whose
+ * split would need more than the scratch holds are rejected with
+ * RSFP4_ERR_UNSUPPORTED (none of the plans this library makes on a 256-CU
+ * device does).  Every call on a GPU
  * shares that GPU's scratch: calls that may overlap on one GPU (other streams,
  * other threads) race; calls in stream order do not. */
 rsfp4_status rsfp4_nvfp4_linear_compensated_noalloc(const void* act, size_t act_bytes, const void* w_packed,
