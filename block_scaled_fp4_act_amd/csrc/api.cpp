@@ -100,11 +100,40 @@ rsfp4_status quantize(int fmt, const void* x, int xt, int64_t M, int64_t K, int 
 
 // Workspace of the tiled products over rewritten activations: the counter
 // area, then the tiled operand; 0 when that would exceed kMaxTileWs (the
-// records path then runs without it).
+// records path then runs without it).  An NVFP4 product with few tiles splits
+// K into ks slices (nv_tile_split), whose partial sums follow the tiled
+// operand at the next 256-byte boundary (tile_split_ws_bytes; 0 past
+// kMaxTileWs: the product then runs unsplit).
 constexpr int64_t kMaxTileWs = (int64_t)1 << 30;
 int64_t tile_ws_bytes(int fmt, int64_t B, int64_t K) {
     const int64_t t = act_tile_bytes(fmt, B, K);
     return t > kMaxTileWs ? 0 : kSplitCounterBytes + t;
+}
+int64_t tile_part_offset(int fmt, int64_t B, int64_t K) {
+    return kSplitCounterBytes + (act_tile_bytes(fmt, B, K) + 255) / 256 * 256;
+}
+int tile_split(int fmt, int64_t B, int64_t N, int64_t K, int cus) {
+    return fmt == RSFP4_NVFP4 ? nv_tile_split(B, N, K, cus) : 1;
+}
+int64_t tile_split_ws_bytes(int fmt, bool comp, int64_t B, int64_t N, int64_t K, int ks) {
+    if (ks <= 1) return tile_ws_bytes(fmt, B, K);
+    const int64_t t = tile_part_offset(fmt, B, K) + nv_split_bytes(B, N, ks, comp);
+    return t > kMaxTileWs ? 0 : t;
+}
+
+// Whether the linear takes the tiled kernel: above 32 operand rows B, except
+// compensated NVFP4 with 33..64 rows, K <= 4096 and N <= 4096, which runs the
+// narrow kernel with four row tiles in one launch, reading each weight step
+// once (measured at M = 17 and 32, K = N = 4096: 12.9 and 15.1 us against
+// 16.1 and 17.2 us tiled; but at K = 14336, N = 4096 the tiled product, split
+// in K, takes 24.2 and 25.6 us against 50.7 and 61.8, and at K = 4096,
+// N = 14336 19.9 and 21.2 us against 25.4 and 26.1); and bf16 output with K
+// above one narrow launch, which cannot take the narrow kernel's second,
+// accumulating launch (the tiled kernel makes one pass over K).
+bool tiled_shape(int fmt, bool comp, int64_t B, int64_t N, int64_t K, bool out_bf16) {
+    const bool narrow4 = fmt == RSFP4_NVFP4 && comp && B > kNarrowRows && B <= 2 * kNarrowRows && K <= 4096 &&
+                         N <= 4096;
+    return (B > kNarrowRows && !narrow4) || (out_bf16 && K > kMaxNarrowK);
 }
 
 // The narrow linear's plan for one launch over `steps` (split across
@@ -144,17 +173,7 @@ rsfp4_status linear(int fmt, bool comp, const void* act, size_t act_bytes, const
     if (w_bytes < need_w) return fail(RSFP4_ERR_BUFFER_TOO_SMALL, "w_packed holds %zu bytes, needs %zu", w_bytes, need_w);
     // The tiled kernel addresses the activation operand with 32-bit offsets
     // below its out-of-range marker 2^31.
-    // bf16 output cannot take the narrow kernel's second, accumulating launch:
-    // K above one narrow launch goes to the tiled kernel (one pass over K)
-    // Compensated NVFP4 with 33..64 operand rows and at most 16384 channels:
-    // the narrow kernel with four row tiles (launches of at most 32 steps),
-    // which reads each weight step once; the tiled kernel's 128-row tiles are
-    // half empty there and, with few channel tiles, leave compute units idle
-    // (measured: 14.6 against 37.6 us at M = 32, K = N = 4096; at N = 28672
-    // and for MXFP4 the tiled kernel is faster).
-    const bool narrow4 = fmt == RSFP4_NVFP4 && comp && B > kNarrowRows && B <= 2 * kNarrowRows &&
-                         K <= kMaxNarrowK && N <= 16384 && (!out_bf16 || num_steps(K) <= 32);
-    if ((B > kNarrowRows && !narrow4) || (out_bf16 && K > kMaxNarrowK)) {
+    if (tiled_shape(fmt, comp, B, N, K, out_bf16)) {
         if ((int64_t)rb * B >= ((int64_t)1 << 31))
             return fail(RSFP4_ERR_UNSUPPORTED, "activation operand of %lld bytes: the linear needs < 2^31",
                         (long long)((int64_t)rb * B));
@@ -166,18 +185,28 @@ rsfp4_status linear(int fmt, bool comp, const void* act, size_t act_bytes, const
         // layout, both operands then streamed into LDS; NVFP4: exact f16 MFMA
         // fragments, streamed into LDS) the activations arrive as contiguous
         // 1 KB requests; same bits as the records path
+        // (and, with room for them, the K slices' partial sums of a split)
         const int64_t tws = tile_ws_bytes(fmt, B, K);
         if (tws > 0 && (int64_t)ws_bytes >= tws) {
             int cus = 0;
             st = num_cus(&cus);
             if (st != RSFP4_OK) return st;
-            void* at = static_cast<uint8_t*>(ws) + kSplitCounterBytes;
+            int ks = tile_split(fmt, B, N, K, cus);
+            if (ks > 1) {
+                const int64_t sws = tile_split_ws_bytes(fmt, comp, B, N, K, ks);
+                if (sws == 0 || (int64_t)ws_bytes < sws) ks = 1;
+            }
+            uint8_t* wsb = static_cast<uint8_t*>(ws);
+            void* at = wsb + kSplitCounterBytes;
             st = hip_status(launch_act_tile(fmt, comp, act, rb, (int)M, K, at, (hipStream_t)stream), "linear launch");
             if (st != RSFP4_OK) return st;
             if (fmt == RSFP4_NVFP4)
-                return hip_status(launch_gemm_tile_dma_nv(comp, at, act, rb, w_packed, (int)M, N, K, y, out_bf16,
-                                                          (hipStream_t)stream),
-                                  "linear launch");
+                return hip_status(
+                    launch_gemm_tile_dma_nv(comp, at, act, rb, w_packed, (int)M, N, K, y, out_bf16, ks,
+                                            reinterpret_cast<int*>(wsb),
+                                            reinterpret_cast<float*>(wsb + tile_part_offset(fmt, B, K)),
+                                            (hipStream_t)stream),
+                    "linear launch");
             return hip_status(launch_gemm_tile_dma(comp, at, w_packed, (int)M, N, K, y, out_bf16, cus,
                                                    (hipStream_t)stream),
                               "linear launch");
@@ -445,15 +474,20 @@ size_t rsfp4_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, int compe
         return 0;
     const int64_t B = compensated ? 2 * M : M;
     const int64_t S = num_steps(K);
-    // wide operands on the tiled kernels (not the four-row-tile narrow plan of
-    // compensated NVFP4): the rewritten activation operand after the counter area
-    const bool narrow4 = fmt == RSFP4_NVFP4 && compensated && B <= 64 && K <= kMaxNarrowK && N <= 16384;
-    if (B > 32 && !narrow4) return (size_t)tile_ws_bytes(fmt, B, K);
+    // wide operands on the tiled kernels: the rewritten activation operand
+    // after the counter area
+    int cus = 0;
+    const bool have_cus = num_cus(&cus) == RSFP4_OK;
+    if (tiled_shape(fmt, compensated != 0, B, N, K, false)) {
+        // (without a device to count compute units on: the unsplit size)
+        const int64_t sws =
+            have_cus ? tile_split_ws_bytes(fmt, compensated != 0, B, N, K, tile_split(fmt, B, N, K, cus)) : 0;
+        g_err[0] = 0;
+        return (size_t)(sws > 0 ? sws : tile_ws_bytes(fmt, B, K));
+    }
     // the split applies to one-pass plans of the narrow kernel with one or two
     // row tiles
-    if (B > 32 || K > kMaxNarrowK) return 0;
-    int cus = 0;
-    if (num_cus(&cus) != RSFP4_OK) return 0;
+    if (B > 32 || K > kMaxNarrowK || !have_cus) return 0;
     int64_t need = 0;
     (void)narrow_plan(fmt, compensated != 0, M, N, S, cus, true, (size_t)1 << 62, &need);
     return (size_t)need;
@@ -557,10 +591,12 @@ rsfp4_status rsfp4_nvfp4_linear_compensated_noalloc(const void* act, size_t act_
                                                     float* y, void* stream) {
     size_t need = rsfp4_workspace_bytes(RSFP4_NVFP4, M, N, K, 1);
     if (need > (size_t)scratch_bytes()) {
-        // a wide operand's workspace holds its rewritten activations, which
-        // are optional (the records path gives the same bits): run without
-        if (M >= 1 && 2 * M > kNarrowRows && need == (size_t)tile_ws_bytes(RSFP4_NVFP4, 2 * M, K))
-            need = 0;
+        // a wide operand's workspace holds its rewritten activations and a
+        // split's partial sums, both optional (without the split: the same
+        // result up to the summation order of the K slices; without the
+        // rewrite: the records path, the same bits): run with what fits
+        if (M >= 1 && tiled_shape(RSFP4_NVFP4, true, 2 * M, N, K, false))
+            need = (size_t)scratch_bytes();
         else
             return fail(RSFP4_ERR_UNSUPPORTED, "this shape's split needs %zu bytes of workspace; the library's "
                         "scratch holds %lld (use rsfp4_nvfp4_linear_compensated with a workspace)", need,

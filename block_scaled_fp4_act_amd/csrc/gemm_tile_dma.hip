@@ -456,38 +456,54 @@ struct NvArgs {
     int64_t K;
     void* y;
     int out_bf16;
-    TileGrid grid;
+    TileGrid grid;      // over tiles x ks workgroups
+    int ks;             // K slices (1: no split)
+    int sl;             // steps per slice (a multiple of 8; the last slice may be shorter)
+    int* cnt;           // ks > 1: one zeroed counter per tile and wave
+    float* part;        // ks > 1: partial sums, per tile, wave and slice
 };
 
-template <bool COMP>
+// RTW 16-row tiles (the workgroup's rows, every wave) x CTW 16-channel groups
+// per wave
+template <bool COMP, int RTW, int CTW>
 __global__ __launch_bounds__(256, 2) void gemm_tile_nv_dma(NvArgs p) {
-    constexpr int RTW = 8, CTW = 2, RD = 4;           // 16-row tiles, 16-channel groups per wave; ring depth
+    constexpr int RD = 4;                             // weight ring depth (steps)
     constexpr int TM = 16 * RTW, GPT = 4 * CTW;       // workgroup rows, channel groups
     constexpr int STAGE = RTW * 4096;                 // one step of TM rows as f16: [u4][rt] blocks of 1 KB
     constexpr int DA = 4 * RTW / 4;                   // per-wave requests of one stage
     __shared__ __attribute__((aligned(16))) uint8_t st0[STAGE];
     __shared__ __attribute__((aligned(16))) uint8_t st1[STAGE];
 
-    int rtile;
-    int64_t ctile;
-    if (!tile_of(p.grid, &rtile, &ctile)) return;
+    // workgroup -> (tile, K slice): per XCD a contiguous range, slices of a
+    // tile fastest, then row tiles (which share a weight tile)
+    const int64_t L_id = blockIdx.x;
+    const int64_t t_id = (L_id % kXcds) * p.grid.per_xcd + L_id / kXcds;
+    if (t_id >= p.grid.tiles) return;
+    const int split = (int)(t_id % p.ks);
+    const int64_t tile = t_id / p.ks;
+    const int rtile = (int)(tile % p.grid.row_tiles);
+    const int64_t ctile = tile / p.grid.row_tiles;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4, i = lane & 15;
-    const int S = (int)num_steps(p.K);
+    // this workgroup's steps [s_lo, s_lo + S)
+    const int S_all = (int)num_steps(p.K);
+    const int s_lo = split * p.sl;
+    const int S = S_all - s_lo < p.sl ? S_all - s_lo : p.sl;
     const int nq2 = (((S + kQuadSteps - 1) / kQuadSteps) + 1) & ~1;
     const int64_t GB = group_bytes(kNV, p.K), QB = quad_bytes(kNV);
-    const int64_t GA = (int64_t)S * 4096;             // f16 fragments of one 16-row group
+    const int64_t GA = (int64_t)S_all * 4096;         // f16 fragments of one 16-row group
     const int B = COMP ? 2 * p.M : p.M;
     const int64_t NGA = (B + 15) / 16, G = num_groups(p.N);
     const int64_t a0 = (int64_t)rtile * RTW;
-    const uint8_t* abase = p.at + a0 * GA;
-    const int64_t abytes = (NGA - a0 < RTW ? NGA - a0 : RTW) * GA;
+    const uint8_t* abase = p.at + a0 * GA + (int64_t)s_lo * 4096;
+    const int64_t abytes = (NGA - a0 < RTW ? NGA - a0 : RTW) * GA - (int64_t)s_lo * 4096;
     const int64_t cw = ctile * GPT + wave * CTW;      // this wave's weight groups
     const int64_t live = G - cw < 0 ? 0 : (G - cw < CTW ? G - cw : CTW);
-    const uint8_t* wbase = p.blob + kWHeader + (live > 0 ? cw : 0) * GB;
-    const int64_t wbytes = live * GB;
+    const int64_t wq0 = (int64_t)(s_lo / kQuadSteps) * QB;   // the slice's first quad
+    const uint8_t* wbase = p.blob + kWHeader + (live > 0 ? cw : 0) * GB + wq0;
+    const int64_t wbytes = live * GB - wq0;
 
     // activation request j of this wave: block wave + 4j = (16-row tile rt, sub-step u4)
     uint32_t a_vo[DA];
@@ -585,7 +601,90 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_nv_dma(NvArgs p) {
     }
     wait_vm<0>();
 
-    // ---- Fold + store: lane holds rows 16rt + 4g + r of channel 16(cw+ct) + i ----
+    // ---- Fold: lane holds rows 16rt + 4g + r of channel 16(cw+ct) + i ----
+    // f = sx v0 + sr v1 per token (compensated: rows 2m, 2m + 1 are x and r of
+    // token m), sx v per row (plain); y = s_gw f
+    constexpr int FV = COMP ? 2 : 4;
+    float f[RTW][CTW][FV];
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+            const int R0 = TM * rtile + 16 * rt + 4 * g + 2 * pr;
+            if (COMP) {
+                const int m = R0 >> 1;
+                float sx = 0.0f, sr = 0.0f;
+                if (m < p.M) {
+                    sx = *reinterpret_cast<const float*>(p.act + (int64_t)m * p.row_bytes);
+                    sr = *reinterpret_cast<const float*>(p.act + (int64_t)(p.M + m) * p.row_bytes);
+                }
+#pragma unroll
+                for (int ct = 0; ct < CTW; ++ct) f[rt][ct][pr] = sx * acc[rt][ct][2 * pr] + sr * acc[rt][ct][2 * pr + 1];
+            } else {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int m = R0 + h;
+                    const float sx = m < p.M ? *reinterpret_cast<const float*>(p.act + (int64_t)m * p.row_bytes) : 0.0f;
+#pragma unroll
+                    for (int ct = 0; ct < CTW; ++ct) f[rt][ct][2 * pr + h] = sx * acc[rt][ct][2 * pr + h];
+                }
+            }
+        }
+    }
+
+    if (p.ks > 1) {
+        // Split K: publish this slice's folded partial sums, count the slice
+        // in, and let the wave that completes the count add all slices'
+        // partials in slice order (the result does not depend on arrival
+        // order), clear the counter for the next call, then store.  The
+        // workspace is accessed with device-scope atomics only (through to the
+        // memory side that all XCDs share), and the partial's stores complete
+        // before the count.
+        constexpr int NVAL = RTW * CTW * FV;
+        const int64_t wt = tile * 4 + wave;
+        float* rec = p.part + (wt * p.ks + split) * (NVAL * 64) + lane;
+#pragma unroll
+        for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < CTW; ++ct)
+#pragma unroll
+                for (int j = 0; j < FV; ++j)
+                    __hip_atomic_store(rec + ((rt * CTW + ct) * FV + j) * 64, f[rt][ct][j], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        int old = 0;
+        if (lane == 0) old = __hip_atomic_fetch_add(p.cnt + wt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        old = __builtin_amdgcn_readfirstlane(old);
+        if (old != p.ks - 1) return;
+        float tot[RTW][CTW][FV];
+#pragma unroll
+        for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < CTW; ++ct)
+#pragma unroll
+                for (int j = 0; j < FV; ++j) tot[rt][ct][j] = 0.0f;
+        for (int q = 0; q < p.ks; ++q) {
+            const float* rq = p.part + (wt * p.ks + q) * (NVAL * 64) + lane;
+#pragma unroll
+            for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < CTW; ++ct)
+#pragma unroll
+                    for (int j = 0; j < FV; ++j)
+                        tot[rt][ct][j] += q == split ? f[rt][ct][j]
+                                                     : __hip_atomic_load(rq + ((rt * CTW + ct) * FV + j) * 64,
+                                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+        for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < CTW; ++ct)
+#pragma unroll
+                for (int j = 0; j < FV; ++j) f[rt][ct][j] = tot[rt][ct][j];
+        if (lane == 0) __hip_atomic_store(p.cnt + wt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+
+    // ---- store ----
     const float s_gw = reinterpret_cast<const WHeader*>(p.blob)->s_g;
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt) {
@@ -596,22 +695,14 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_nv_dma(NvArgs p) {
 #pragma unroll
             for (int pr = 0; pr < 2; ++pr) {
                 const int R0 = TM * rtile + 16 * rt + 4 * g + 2 * pr;
-                const float v0 = acc[rt][ct][2 * pr], v1 = acc[rt][ct][2 * pr + 1];
                 if (COMP) {
                     const int m = R0 >> 1;
-                    if (m < p.M) {
-                        const float sx = *reinterpret_cast<const float*>(p.act + (int64_t)m * p.row_bytes);
-                        const float sr = *reinterpret_cast<const float*>(p.act + (int64_t)(p.M + m) * p.row_bytes);
-                        store_y(p.y, (int64_t)m * p.N + n, s_gw * (sx * v0 + sr * v1), p.out_bf16);
-                    }
+                    if (m < p.M) store_y(p.y, (int64_t)m * p.N + n, s_gw * f[rt][ct][pr], p.out_bf16);
                 } else {
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
                         const int m = R0 + h;
-                        if (m < p.M) {
-                            const float sx = *reinterpret_cast<const float*>(p.act + (int64_t)m * p.row_bytes);
-                            store_y(p.y, (int64_t)m * p.N + n, s_gw * (sx * (h ? v1 : v0)), p.out_bf16);
-                        }
+                        if (m < p.M) store_y(p.y, (int64_t)m * p.N + n, s_gw * f[rt][ct][2 * pr + h], p.out_bf16);
                     }
                 }
             }
@@ -644,15 +735,65 @@ hipError_t launch_act_tile(int fmt, bool comp, const void* act, int64_t row_byte
     return hipGetLastError();
 }
 
+namespace {
+
+// Rows of the NVFP4 product's tiles: 64 up to 128 operand rows (a 128-row tile
+// would be half empty at 33..64 rows, and at 65..128 rows twice the channel
+// tiles fill more compute units; measured at K = 8192, N = 28672: 46 against
+// 66 us at 64 rows, 65-68 against 70-77 us at 128, equal at 256), else 128.
+int nv_tile_rows(int64_t B) { return B <= 128 ? 64 : 128; }
+int64_t nv_tiles(int64_t B, int64_t N) {
+    const int tm = nv_tile_rows(B);
+    return (B + tm - 1) / tm * ((num_groups(N) + 7) / 8);
+}
+
+// Steps per slice of a split into ks slices: a multiple of 8 (the product's
+// loop body), so that ceil(S / slice) slices cover S.
+int slice_steps(int64_t S, int ks) { return (int)(((S + ks - 1) / ks + 7) & ~(int64_t)7); }
+
+}  // namespace
+
+// Split K while the tiles x slices stay within one workgroup per compute unit
+// and the slices hold at least 8 steps (measured at M = 64, K = 14336,
+// N = 4096, 64 tiles: 67 us unsplit, 40 us in 2 slices, 28 us in 4).
+int nv_tile_split(int64_t B, int64_t N, int64_t K, int num_cus) {
+    const int64_t tiles = nv_tiles(B, N), S = num_steps(K);
+    int ks = 1;
+    while (ks < kMaxTileSplit && tiles * 2 * ks <= num_cus && S >= 16 * ks && tiles * 4 <= kSplitGroups) ks *= 2;
+    return ks <= 1 ? 1 : (int)((S + slice_steps(S, ks) - 1) / slice_steps(S, ks));
+}
+
+// Folded partial sums per tile, wave and slice: the tile's 16-row tiles x 2
+// channel groups x 64 lanes x 2 values per lane (compensated: one per token of
+// each pair of rows) or 4 (plain).
+int64_t nv_split_bytes(int64_t B, int64_t N, int ks, bool comp) {
+    return ks <= 1 ? 0 : nv_tiles(B, N) * 4 * ks * (nv_tile_rows(B) / 16) * 2 * (comp ? 2 : 4) * 64 * 4;
+}
+
 hipError_t launch_gemm_tile_dma_nv(bool comp, const void* act_tiled, const void* act, int64_t row_bytes,
                                    const void* blob, int M, int64_t N, int64_t K, void* y, bool out_bf16,
-                                   hipStream_t s) {
+                                   int ks, int* cnt, float* part, hipStream_t s) {
     NvArgs a{static_cast<const uint8_t*>(act_tiled), static_cast<const uint8_t*>(act), row_bytes,
-             static_cast<const uint8_t*>(blob), M, N, K, y, out_bf16 ? 1 : 0, TileGrid{}};
-    a.grid = tile_grid(comp ? 2 * (int64_t)M : M, N, 128, 128);
+             static_cast<const uint8_t*>(blob), M, N, K, y, out_bf16 ? 1 : 0, TileGrid{}, 1, 0, cnt, part};
+    const int64_t S = num_steps(K);
+    a.sl = (int)S;
+    if (ks > 1) {
+        a.sl = slice_steps(S, ks);
+        a.ks = (int)((S + a.sl - 1) / a.sl);
+    }
+    const int64_t B = comp ? 2 * (int64_t)M : M;
+    const int tm = nv_tile_rows(B);
+    a.grid = tile_grid(B, N, tm, 128);
+    a.grid.tiles *= a.ks;
+    a.grid.per_xcd = (a.grid.tiles + kXcds - 1) / kXcds;
     const dim3 grid((unsigned)(a.grid.per_xcd * kXcds));
-    if (comp) hipLaunchKernelGGL((gemm_tile_nv_dma<true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((gemm_tile_nv_dma<false>), grid, dim3(256), 0, s, a);
+    if (tm == 64) {
+        if (comp) hipLaunchKernelGGL((gemm_tile_nv_dma<true, 4, 2>), grid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((gemm_tile_nv_dma<false, 4, 2>), grid, dim3(256), 0, s, a);
+    } else {
+        if (comp) hipLaunchKernelGGL((gemm_tile_nv_dma<true, 8, 2>), grid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((gemm_tile_nv_dma<false, 8, 2>), grid, dim3(256), 0, s, a);
+    }
     return hipGetLastError();
 }
 

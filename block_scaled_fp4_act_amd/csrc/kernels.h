@@ -116,9 +116,16 @@ hipError_t launch_gemm_tile_dma(bool comp, const void* act_tiled, const void* bl
                                 void* y, bool out_bf16, int num_cus, hipStream_t s);
 // NVFP4: the activations rewritten as exact f16 MFMA fragments (4 KB per 16
 // rows and step), streamed into LDS by DMA; weights from a register ring.
+// With few tiles K is split into ks slices (nv_tile_split; at most
+// kMaxTileSplit) whose folded partial sums (nv_split_bytes at part) are added in
+// slice order by the last slice to arrive at its counter (cnt: the zeroed
+// counter area of kSplitGroups ints, left zero).
+constexpr int kMaxTileSplit = 8;
+int nv_tile_split(int64_t B, int64_t N, int64_t K, int num_cus);
+int64_t nv_split_bytes(int64_t B, int64_t N, int ks, bool comp);
 hipError_t launch_gemm_tile_dma_nv(bool comp, const void* act_tiled, const void* act, int64_t row_bytes,
                                    const void* blob, int M, int64_t N, int64_t K, void* y, bool out_bf16,
-                                   hipStream_t s);
+                                   int ks, int* cnt, float* part, hipStream_t s);
 
 // Paper-numerics NVFP4 quantizer (tensor scale alpha from device memory, shared
 // by x and r; multiplier-scale codes and residue) and the alpha of a tensor.

@@ -130,9 +130,9 @@ size_t rsfp4_packed_weight_bytes(int fmt, int64_t N, int64_t K);
  * call given a NULL or smaller workspace runs the plan without the split
  * (same result up to the summation order of the slices).  Wide operands, more
  * than 32 operand rows B (2M compensated, M plain), use the workspace
- * differently (except compensated NVFP4 with 33..64 rows, N <= 16384 and
- * K <= 16384, which runs the narrow kernel): after the same 16384-byte counter
- * area (left untouched) the call rewrites the activation records in tiles of
+ * differently (except compensated NVFP4 with 33..64 rows, N <= 4096 and
+ * K <= 4096, which runs the narrow kernel): after the same 16384-byte counter
+ * area (left zero) the call rewrites the activation records in tiles of
  * 16 operand rows, base and residue rows interleaved -- MXFP4 in the
  * packed-weight layout (4352 bytes per tile and quad of 4 steps: 16384 +
  * ceil(B/16) * ceil(K/512) * 4352 bytes in all), NVFP4 as the exact f16
@@ -140,8 +140,20 @@ size_t rsfp4_packed_weight_bytes(int fmt, int64_t N, int64_t K);
  * 16384 + ceil(B/16) * ceil(K/128) * 4096 bytes) -- so that the activations
  * stream into LDS as contiguous 1 KB requests.  Given a NULL or smaller
  * workspace the call multiplies the records directly, with the same bits.
- * Wide shapes whose rewritten operand would exceed 1 GiB size to 0 (no
- * rewrite).  ws must be 256-byte aligned. */
+ * An NVFP4 product with few tiles (64 x 128 up to 128 operand rows, else
+ * 128 x 128; while twice the tiles stay within the compute units, K holds at
+ * least 16 steps per slice pair and the tiles number at most 1024) splits K
+ * into ks = 2..8 slices of a multiple of 8 steps: its workspace adds, at the
+ * next 256-byte boundary after the rewritten operand, one record of folded
+ * partial sums per tile, wave (4) and slice (the tile's rows / 16 x 2 x 64 x
+ * 2 floats compensated, one per token of each row pair, x 4 plain),
+ * and the 4 counters of each tile in the counter area count the slices in and
+ * are left zero; the slices are summed in slice order.  With a workspace that
+ * holds the rewritten operand but not the partials the product runs unsplit
+ * (the same result up to the summation order of the slices).  Without a
+ * device to count compute units on the size is the unsplit one.  Wide shapes
+ * whose rewritten operand would exceed 1 GiB size to 0 (no rewrite).  ws
+ * must be 256-byte aligned. */
 size_t rsfp4_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, int compensated);
 
 /* ------------------------------------------------------------- prepack ----
@@ -178,11 +190,11 @@ rsfp4_status rsfp4_mxfp4_quantize_act_with_residue(const void* x, int xt, int64_
  *   *_linear_compensated:  y = deq(q(x)) W^T + deq(q(r)) W^T (B = 2M rows; the
  *                          buffer must have been quantized with_residue)
  * B = M (plain) or 2M (compensated) activation rows enter the product.  Up to
- * 32 rows (compensated NVFP4 with N <= 16384 and K <= 16384: up to 64), each
+ * 32 rows (compensated NVFP4 with N <= 4096 and K <= 4096: up to 64), each
  * packed weight step is loaded from HBM once and multiplied with all B rows
  * (the narrow-M, memory-bound regime); above that a 2-D tiled kernel covers
- * 128 rows x 128 channels per workgroup (each weight tile is then read once
- * per 128 rows).  Either way base and residue products of one token
+ * 128 rows x 128 channels per workgroup (NVFP4 up to 128 rows: 64 x 128; each
+ * weight tile is then read once per 64 or 128 rows).  Either way base and residue products of one token
  * land in the same lane's accumulators and are added there before the single
  * store (ResServe Section 4.3, Eq. 2 and Section 5.1, Eq. 4).  With up to 32
  * rows and K above 16384 the narrow kernel runs twice, over the two halves of
@@ -192,7 +204,8 @@ rsfp4_status rsfp4_mxfp4_quantize_act_with_residue(const void* x, int xt, int64_
  * rsfp4_workspace_bytes (NULL, 0 for none; 256-byte aligned, counters zero on
  * first use, left zero); with it, compensated NVFP4 shapes that gain from it
  * split K across workgroups, and wide operands take the tiled product over
- * rewritten activations (same bits as without). */
+ * rewritten activations (same bits as without), NVFP4 with few tiles split
+ * across workgroups in K as well. */
 rsfp4_status rsfp4_nvfp4_linear(const void* act, size_t act_bytes, const void* w_packed,
                                 size_t w_packed_bytes, int64_t M, int64_t N, int64_t K,
                                 float* y, void* ws, size_t ws_bytes, void* stream);
@@ -209,14 +222,17 @@ rsfp4_status rsfp4_mxfp4_linear_compensated(const void* act, size_t act_bytes, c
 /* For callers that cannot allocate device memory (code under stream capture,
  * tight serving loops, harnesses that forbid allocation): the compensated
  * NVFP4 linear of rsfp4_nvfp4_linear_compensated, same arguments but no
- * workspace, same plan and the same bits as that call given a workspace.
+ * workspace: the same plan and the same bits as that call given a workspace of
+ * min(rsfp4_workspace_bytes, 16384 + 16777216) bytes.
  * Where the plan splits K it uses the library's own scratch, a device array of
  * 16384 + 16777216 bytes on each GPU (held until the process ends; its address
  * is taken, and its counter area cleared on `stream`, by the first call on a
  * device).  Wide operands (more than 64 operand rows, or N or K above 16384)
- * use the scratch for their rewritten activations when those fit in it (at
- * most 16777216 bytes: ceil(2M/16) * ceil(K/128) * 4096), and otherwise run
- * without them, with the same bits.  It calls no allocator.  Shapes whose
+ * use the scratch for their rewritten activations and a split's partial sums
+ * as far as they fit in it: a split that does not fit runs unsplit, and
+ * rewritten activations that do not fit (more than 16777216 bytes:
+ * ceil(2M/16) * ceil(K/128) * 4096) are not made (the records path, the same
+ * bits as the unsplit tiled product).  It calls no allocator.  Shapes whose
  * split would need more than the scratch holds are rejected with
  * RSFP4_ERR_UNSUPPORTED (none of the plans this library makes on a 256-CU
  * device does).  Every call on a GPU

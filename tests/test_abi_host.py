@@ -55,10 +55,13 @@ def test_size_queries():
     assert rs.workspace_bytes(1, 40, 64, 1056, False) == 16384 + 3 * 3 * (4096 + 256)
     assert rs.workspace_bytes(1, 17, 64, 1056, True) == 16384 + 3 * 3 * (4096 + 256)
     # NVFP4: 4 KB of f16 fragments per 16 rows and step (33..64 compensated
-    # rows with N, K <= 16384 take the narrow kernel and no such workspace)
+    # rows with N, K <= 4096 take the narrow kernel and no such workspace;
+    # without a device the size leaves out a split's partial sums)
     assert rs.workspace_bytes(0, 128, 28672, 8192, True) == 16384 + 16 * 64 * 4096
     assert rs.workspace_bytes(0, 40, 64, 1056, False) == 16384 + 3 * 9 * 4096
     assert rs.workspace_bytes(0, 20, 28672, 8192, True) == 16384 + 3 * 64 * 4096
+    assert rs.workspace_bytes(0, 20, 4096, 8192, True) == 16384 + 3 * 64 * 4096
+    assert rs.workspace_bytes(0, 20, 4096, 4096, True) == 0
     # invalid requests size to 0
     assert rs.packed_weight_bytes(0, 16, 48) == 0
     assert rs.packed_weight_bytes(2, 16, 64) == 0

@@ -212,9 +212,10 @@ SMALL_CASES = [  # (M, N, K): several tiles, ragged N and K tails, both row-tile
     # two row tiles, compensated NVFP4: launches of 32 steps adding into y
     # (two full ones; one full and a ragged one; four)
     (12, 80, 8192), (16, 48, 5120), (9, 40, 16384),
-    # four row tiles (compensated NVFP4, 33..64 operand rows): one launch, two,
-    # one full and a ragged one, and the tiled kernel past N = 16384
-    (20, 72, 4096), (32, 48, 8192), (25, 40, 5120), (30, 16400, 256),
+    # four row tiles (compensated NVFP4, 33..64 operand rows, K and N at most
+    # 4096): one launch of 32 steps and a ragged one of 17; the tiled kernel
+    # past K = 4096 and past N = 4096
+    (20, 72, 4096), (24, 40, 2112), (32, 48, 8192), (25, 40, 5120), (30, 16400, 256),
 ]
 
 

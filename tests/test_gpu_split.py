@@ -172,4 +172,5 @@ def test_workspace_query():
     assert rs.workspace_bytes(0, 8, 4096, 14336, False) == 0      # plain
     assert rs.workspace_bytes(0, 16, 4096, 14336, True) > 0       # two row tiles, 4 slices of 28 steps
     assert rs.workspace_bytes(0, 16, 4096, 4096, True) == 0       # two row tiles, 32 steps: one pass
-    assert rs.workspace_bytes(0, 17, 4096, 8192, True) == 0       # four row tiles
+    assert rs.workspace_bytes(0, 17, 4096, 4096, True) == 0       # four row tiles
+    assert rs.workspace_bytes(0, 17, 4096, 8192, True) > 0        # tiled, rewritten operand
