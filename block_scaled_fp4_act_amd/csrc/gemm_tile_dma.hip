@@ -464,15 +464,19 @@ struct NvArgs {
 };
 
 // RTW 16-row tiles (the workgroup's rows, every wave) x CTW 16-channel groups
-// per wave
-template <bool COMP, int RTW, int CTW>
+// per wave; NS activation stages in LDS (2 or 4: the activations of step s
+// are requested NS - 1 steps ahead)
+template <bool COMP, int RTW, int CTW, int NS>
 __global__ __launch_bounds__(256, 2) void gemm_tile_nv_dma(NvArgs p) {
+    static_assert(NS == 2 || NS == 4, "two or four activation stages");
     constexpr int RD = 4;                             // weight ring depth (steps)
     constexpr int TM = 16 * RTW, GPT = 4 * CTW;       // workgroup rows, channel groups
     constexpr int STAGE = RTW * 4096;                 // one step of TM rows as f16: [u4][rt] blocks of 1 KB
     constexpr int DA = 4 * RTW / 4;                   // per-wave requests of one stage
     __shared__ __attribute__((aligned(16))) uint8_t st0[STAGE];
     __shared__ __attribute__((aligned(16))) uint8_t st1[STAGE];
+    __shared__ __attribute__((aligned(16))) uint8_t st2[NS == 4 ? STAGE : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t st3[NS == 4 ? STAGE : 16];
 
     // workgroup -> (tile, K slice): per XCD a contiguous range, slices of a
     // tile fastest, then row tiles (which share a weight tile)
@@ -545,28 +549,59 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_nv_dma(NvArgs p) {
 #pragma unroll
         for (int ct = 0; ct < CTW; ++ct) acc[rt][ct] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // Requests in program order: prologue [scales q0, weights of steps
-    // 0..RD-3, activations of step 0, weights of step RD-2]; step s, after its
-    // barrier: activations of step s+1, [scales of quad q+1 if s % 4 == 0],
-    // weights of step s+RD-1.  The wait at the start of step s leaves in
-    // flight the weight and scale loads requested after step s's activations.
-    load_sw(0, 0);
+    // the stage of step s (s % NS, a compile-time index: the LDS-DMA writes
+    // then go to distinct arrays, which keeps the compiler's waits exact)
+    auto stage = [&](auto k_tag) -> uint8_t* {
+        constexpr int k = decltype(k_tag)::value % NS;
+        if constexpr (k == 0) return st0;
+        else if constexpr (k == 1) return st1;
+        else if constexpr (k == 2) return st2;
+        else return st3;
+    };
+    if constexpr (NS == 2) {
+        load_sw(0, 0);
 #pragma unroll
-    for (int r = 0; r < RD - 2; ++r) load_b(r, r);
-    dma_a(0, st0);
-    load_b(RD - 2, RD - 2);
+        for (int r = 0; r < RD - 2; ++r) load_b(r, r);
+        dma_a(0, st0);
+        load_b(RD - 2, RD - 2);
+    } else {
+        // steps 0..2 requested as steps -3..-1 would (activations, then
+        // weights), the first quad's scales before them
+        load_sw(0, 0);
+        dma_a(0, st0);
+        load_b(0, 0);
+        dma_a(1, st1);
+        load_b(1, 1);
+        dma_a(2, st2);
+        load_b(2, 2);
+    }
     for (int q = 0; q < nq2; q += 2) {
         auto step = [&](auto v_tag) {
             constexpr int v = decltype(v_tag)::value;   // step of the two-quad body
             constexpr int u = v & 3, qs = v >> 2;
             const int s = 4 * q + v;
-            if (u == 1) wait_vm<2 * CTW>();
-            else wait_vm<CTW>();
+            if constexpr (NS == 2) {
+                // Requests in program order: prologue [scales q0, weights of
+                // steps 0..RD-3, activations of step 0, weights of step RD-2];
+                // step s, after its barrier: activations of step s+1, [scales
+                // of quad q+1 if s % 4 == 0], weights of step s+RD-1.  The wait
+                // at the start of step s leaves in flight the weight and scale
+                // loads requested after step s's activations.
+                if (u == 1) wait_vm<2 * CTW>();
+                else wait_vm<CTW>();
+            } else {
+                // Step t requests the activations and weights of step t+3
+                // (and at t % 4 == 0 the next quad's scales): at the start of
+                // step s everything through step s-3's requests is complete,
+                // the requests of steps s-2 and s-1 stay in flight.
+                if (u == 1 || u == 2) wait_vm<2 * (DA + CTW) + CTW>();
+                else wait_vm<2 * (DA + CTW)>();
+            }
             lds_barrier();
-            dma_a(s + 1, (v & 1) ? st0 : st1);
+            dma_a(s + NS - 1, stage(std::integral_constant<int, v + NS - 1>()));
             if (u == 0) load_sw(q + qs + 1, qs ^ 1);
             load_b(s + RD - 1, (v + RD - 1) % RD);
-            const uint8_t* cur = (v & 1) ? st1 : st0;
+            const uint8_t* cur = stage(std::integral_constant<int, v>());
             constexpr int slot = v % RD;
             if (s < S) {
 #pragma unroll
@@ -787,12 +822,14 @@ hipError_t launch_gemm_tile_dma_nv(bool comp, const void* act_tiled, const void*
     a.grid.tiles *= a.ks;
     a.grid.per_xcd = (a.grid.tiles + kXcds - 1) / kXcds;
     const dim3 grid((unsigned)(a.grid.per_xcd * kXcds));
+    // 64-row tiles: four activation stages (64 KB of LDS, two workgroups per
+    // CU); 128-row tiles: two (64 KB)
     if (tm == 64) {
-        if (comp) hipLaunchKernelGGL((gemm_tile_nv_dma<true, 4, 2>), grid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((gemm_tile_nv_dma<false, 4, 2>), grid, dim3(256), 0, s, a);
+        if (comp) hipLaunchKernelGGL((gemm_tile_nv_dma<true, 4, 2, 4>), grid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((gemm_tile_nv_dma<false, 4, 2, 4>), grid, dim3(256), 0, s, a);
     } else {
-        if (comp) hipLaunchKernelGGL((gemm_tile_nv_dma<true, 8, 2>), grid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((gemm_tile_nv_dma<false, 8, 2>), grid, dim3(256), 0, s, a);
+        if (comp) hipLaunchKernelGGL((gemm_tile_nv_dma<true, 8, 2, 2>), grid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((gemm_tile_nv_dma<false, 8, 2, 2>), grid, dim3(256), 0, s, a);
     }
     return hipGetLastError();
 }
