@@ -93,7 +93,10 @@ rsfp4_status quantize(int fmt, const void* x, int xt, int64_t M, int64_t K, int 
     if (!aligned(x, 16) || !aligned(act, 16)) return fail(RSFP4_ERR_ALIGN, "x and act must be 16-byte aligned");
     const size_t need = (size_t)act_row_bytes(fmt, K) * (size_t)(with_res ? 2 * M : M);
     if (bytes < need) return fail(RSFP4_ERR_BUFFER_TOO_SMALL, "act holds %zu bytes, needs %zu", bytes, need);
-    return hip_status(launch_quantize_act(fmt, xt == RSFP4_BF16, x, (int)M, K, with_res ? 1 : 0, act,
+    int cus = 0;
+    st = num_cus(&cus);
+    if (st != RSFP4_OK) return st;
+    return hip_status(launch_quantize_act(fmt, xt == RSFP4_BF16, x, (int)M, K, with_res ? 1 : 0, act, cus,
                                           (hipStream_t)stream),
                       "quantize launch");
 }

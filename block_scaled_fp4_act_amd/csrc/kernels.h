@@ -5,8 +5,10 @@
 
 namespace rsfp4 {
 
+// The per-row quantizer; with few rows (M x parts within num_cus) a row is
+// shared by up to 8 workgroups (num_cus = 0: one workgroup per row).
 hipError_t launch_quantize_act(int fmt, int xt_bf16, const void* x, int M, int64_t K, int with_res,
-                               void* act, hipStream_t s);
+                               void* act, int num_cus, hipStream_t s);
 
 hipError_t launch_prepack(int fmt, int wt_bf16, const void* W, int64_t N, int64_t K, void* blob,
                           hipStream_t s);

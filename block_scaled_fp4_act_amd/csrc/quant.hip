@@ -1,6 +1,7 @@
 // quant.hip -- activation quantize + residue kernels (NVFP4 and MXFP4): the
-// per-row dynamic-scale quantizer (one workgroup per row, T = 64..1024
-// threads; the row routine and its steps are in quant_row.h), the selective
+// per-row dynamic-scale quantizer (one workgroup per row or, NVFP4 with few
+// rows, per part of a row; T = 64..1024 threads; the row routine and its
+// steps are in quant_row.h), the selective
 // (K-Ext) quantizer and the given-tensor-scale quantizer of the page's
 // Algorithm 1.
 #include <hip/hip_runtime.h>
@@ -16,25 +17,49 @@ namespace rsfp4 {
 
 namespace {
 
+// Row m is shared by `parts` workgroups (m = block / parts), the p-th writing
+// chunks [p cw, (p + 1) cw) of both records.
 template <int FMT, int NC, int EPT, typename TIn>
 __global__ __launch_bounds__(kQMaxThreads) void quant_act_kernel(const TIn* __restrict__ x, int M,
                                                                  int64_t K, int with_res,
                                                                  uint8_t* __restrict__ act,
-                                                                 int64_t row_bytes) {
+                                                                 int64_t row_bytes, int parts, int cw) {
     __shared__ float red[2][kQMaxThreads / 64];
-    const int m = blockIdx.x;
+    const int m = blockIdx.x / parts, p = blockIdx.x - m * parts;
     float v[NC][EPT];
     row_load<NC, EPT, TIn>(x + (int64_t)m * K, K, threadIdx.x, blockDim.x, true, v);
     row_quantize<FMT, NC, EPT>(v, K, threadIdx.x, blockDim.x, true, with_res, act + (int64_t)m * row_bytes,
-                               act + (int64_t)(M + m) * row_bytes, red);
+                               act + (int64_t)(M + m) * row_bytes, red, p * cw, cw);
+}
+
+// Parts per row (NVFP4): with few rows a row's quantization is bound by one
+// compute unit's VALU issue (the exact quotients), so rows of at least 512
+// chunks (4096 elements) are shared by up to 8 workgroups, parts of a
+// multiple of 64 chunks (whole waves) and at least 256 (four waves, one per
+// SIMD), while rows x parts stay within the compute units.  Each part
+// recomputes the row statistics; the residue's codes, half the work, split
+// across the parts (the plain quantizer's codes entirely).  Measured in the
+// compensated step at M = 8: K = 14336 18.0 against 18.7 us, K = 8192 30.8
+// against 30.9-31.0 us, K = 4096 unchanged; MXFP4 (no divisions) is 0.2 us
+// slower shared and keeps one workgroup per row.
+void quant_parts(int M, int64_t nchunks, int num_cus, int* parts, int* cw) {
+    int W = (int)(nchunks / 256);
+    if (W > 8) W = 8;
+    while (W > 1 && (int64_t)M * W > num_cus) --W;
+    if (W < 1) W = 1;
+    const int64_t per = ((nchunks + W - 1) / W + 63) / 64 * 64;
+    *cw = (int)per;
+    *parts = (int)((nchunks + per - 1) / per);
 }
 
 template <int FMT, int NC, int EPT, typename TIn>
-hipError_t launch_quant_t(const void* x, int M, int64_t K, int with_res, void* act, int threads,
+hipError_t launch_quant_t(const void* x, int M, int64_t K, int with_res, void* act, int threads, int num_cus,
                           hipStream_t s) {
     const int64_t rb = act_row_bytes(FMT, K);
-    hipLaunchKernelGGL((quant_act_kernel<FMT, NC, EPT, TIn>), dim3(M), dim3(threads), 0, s,
-                       static_cast<const TIn*>(x), M, K, with_res, static_cast<uint8_t*>(act), rb);
+    int parts = 1, cw = 0x7fffffff;
+    if (FMT == kNV && num_cus > 0) quant_parts(M, K / EPT, num_cus, &parts, &cw);
+    hipLaunchKernelGGL((quant_act_kernel<FMT, NC, EPT, TIn>), dim3((unsigned)M * (unsigned)parts), dim3(threads), 0,
+                       s, static_cast<const TIn*>(x), M, K, with_res, static_cast<uint8_t*>(act), rb, parts, cw);
     return hipGetLastError();
 }
 
@@ -44,14 +69,15 @@ hipError_t launch_quant_t(const void* x, int M, int64_t K, int with_res, void* a
 // computation; with one row per compute unit the quantizer is bound by that
 // unit's VALU issue, and at K = 4096 this measured 3.7 us against 4.4 us.
 template <int FMT, typename TIn>
-hipError_t launch_quant_f(const void* x, int M, int64_t K, int with_res, void* act, hipStream_t s) {
+hipError_t launch_quant_f(const void* x, int M, int64_t K, int with_res, void* act, int num_cus, hipStream_t s) {
     const int64_t nch = K / 8;
     if (nch <= kQMaxThreads) {
         const int threads = (int)((nch + 63) / 64 * 64);
-        return launch_quant_t<FMT, 1, 8, TIn>(x, M, K, with_res, act, threads, s);
+        return launch_quant_t<FMT, 1, 8, TIn>(x, M, K, with_res, act, threads, num_cus, s);
     }
-    if (nch <= 2 * kQMaxThreads) return launch_quant_t<FMT, 2, 8, TIn>(x, M, K, with_res, act, kQMaxThreads, s);
-    return launch_quant_t<FMT, 4, 8, TIn>(x, M, K, with_res, act, kQMaxThreads, s);
+    if (nch <= 2 * kQMaxThreads)
+        return launch_quant_t<FMT, 2, 8, TIn>(x, M, K, with_res, act, kQMaxThreads, num_cus, s);
+    return launch_quant_t<FMT, 4, 8, TIn>(x, M, K, with_res, act, kQMaxThreads, num_cus, s);
 }
 
 // ---------------------------------------------------------------- K-Ext --
@@ -309,13 +335,13 @@ __global__ void alpha_finish_kernel(float* alpha) {
 }  // namespace
 
 hipError_t launch_quantize_act(int fmt, int xt_bf16, const void* x, int M, int64_t K, int with_res,
-                               void* act, hipStream_t s) {
+                               void* act, int num_cus, hipStream_t s) {
     if (fmt == kNV) {
-        return xt_bf16 ? launch_quant_f<kNV, __hip_bfloat16>(x, M, K, with_res, act, s)
-                       : launch_quant_f<kNV, float>(x, M, K, with_res, act, s);
+        return xt_bf16 ? launch_quant_f<kNV, __hip_bfloat16>(x, M, K, with_res, act, num_cus, s)
+                       : launch_quant_f<kNV, float>(x, M, K, with_res, act, num_cus, s);
     }
-    return xt_bf16 ? launch_quant_f<kMX, __hip_bfloat16>(x, M, K, with_res, act, s)
-                   : launch_quant_f<kMX, float>(x, M, K, with_res, act, s);
+    return xt_bf16 ? launch_quant_f<kMX, __hip_bfloat16>(x, M, K, with_res, act, num_cus, s)
+                   : launch_quant_f<kMX, float>(x, M, K, with_res, act, num_cus, s);
 }
 
 hipError_t launch_quantize_act_kext(int fmt, int xt_bf16, const void* x, int M, int64_t K,

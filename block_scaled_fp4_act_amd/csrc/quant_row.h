@@ -272,15 +272,22 @@ __device__ __forceinline__ void store_head(uint8_t* rec, float s_g, int lt) {
 // residue): chunk j's codes go to codes[j * EPT / 2 ..], its block scale byte
 // to scales[j / lanes-per-block].  s_g is the row's tensor scale (NVFP4);
 // nchunks = K / EPT; the row's nt threads (a multiple of 64) hold chunks
-// lt, lt + nt, ...
+// lt, lt + nt, ...  Only chunks of the part [j0, j0 + cw) are written (j0 and
+// cw multiples of 64, so a wave's 64 chunks of one c are all in or all out);
+// the others are quantized (for their residue) when all is set and skipped
+// otherwise.
 template <int FMT, int NC, int EPT, bool FAST>
 __device__ __forceinline__ void quantize_chunks_q(float (&v)[NC][EPT], int nchunks, float s_g,
-                                                  uint8_t* codes, uint8_t* scales, int lt, int nt) {
+                                                  uint8_t* codes, uint8_t* scales, int lt, int nt, int j0, int cw,
+                                                  bool all) {
     constexpr int LPB = (FMT == kNV ? 16 : 32) / EPT;   // lanes sharing one block
     const BlockDiv bd = make_block_div<FAST>(s_g);
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
         const int j = lt + nt * c;                   // chunk index
+        const int jw = (lt & ~63) + nt * c;          // the wave's first chunk of this c
+        const bool in = jw >= j0 && jw - j0 < cw;    // wave-uniform
+        if (!in && !all) continue;
         float bm = 0.0f;
 #pragma unroll
         for (int e = 0; e < EPT; ++e) bm = fmaxf(bm, fabsf(v[c][e]));
@@ -292,7 +299,7 @@ __device__ __forceinline__ void quantize_chunks_q(float (&v)[NC][EPT], int nchun
         const float st = block_scale<FMT, FAST>(bm, s_g, bd, sbyte);   // effective element scale
         // codes, and v becomes the residue x - fl(s~ e) (exact: Sterbenz)
         const uint32_t packed = encode_residue<FMT, EPT, FAST>(v[c], st);
-        if (j < nchunks) {
+        if (in && j < nchunks) {
             if (EPT == 8)
                 *reinterpret_cast<uint32_t*>(codes + 4 * (int64_t)j) = packed;
             else
@@ -306,11 +313,12 @@ __device__ __forceinline__ void quantize_chunks_q(float (&v)[NC][EPT], int nchun
 // in every thread of the workgroup, so the branch does not diverge).
 template <int FMT, int NC, int EPT>
 __device__ __forceinline__ void quantize_chunks(float (&v)[NC][EPT], int nchunks, float s_g,
-                                                uint8_t* codes, uint8_t* scales, int lt, int nt) {
+                                                uint8_t* codes, uint8_t* scales, int lt, int nt, int j0 = 0,
+                                                int cw = 0x7fffffff, bool all = true) {
     if (FMT == kNV && !fast_quot_row(s_g))
-        quantize_chunks_q<FMT, NC, EPT, false>(v, nchunks, s_g, codes, scales, lt, nt);
+        quantize_chunks_q<FMT, NC, EPT, false>(v, nchunks, s_g, codes, scales, lt, nt, j0, cw, all);
     else
-        quantize_chunks_q<FMT, NC, EPT, true>(v, nchunks, s_g, codes, scales, lt, nt);
+        quantize_chunks_q<FMT, NC, EPT, true>(v, nchunks, s_g, codes, scales, lt, nt, j0, cw, all);
 }
 
 // One row, in two phases so a caller can issue other loads in between:
@@ -319,6 +327,10 @@ __device__ __forceinline__ void quantize_chunks(float (&v)[NC][EPT], int nchunks
 // residue's record).  The row's nt threads are lt = 0 .. nt - 1, waves w0 ..
 // w0 + nt / 64 - 1 of the workgroup; every thread of the workgroup calls
 // row_quantize (it holds two barriers), threads of no row with active = false.
+// A row may be shared by several workgroups, each writing the part of chunks
+// [j0, j0 + cw) (the heads with the part at j0 = 0): each forms both row
+// maxima over the whole row (the residue's needs every base code), but only
+// its part's residue codes.
 template <int NC, int EPT, typename TIn>
 __device__ __forceinline__ void row_load(const TIn* __restrict__ xr, int64_t K, int lt, int nt, bool active,
                                          float (&v)[NC][EPT]) {
@@ -337,7 +349,8 @@ __device__ __forceinline__ void row_load(const TIn* __restrict__ xr, int64_t K, 
 
 template <int FMT, int NC, int EPT>
 __device__ __forceinline__ void row_quantize(float (&v)[NC][EPT], int64_t K, int lt, int nt, bool active, int with_res,
-                                             uint8_t* rec, uint8_t* rrec, float (*red)[kQMaxThreads / 64]) {
+                                             uint8_t* rec, uint8_t* rrec, float (*red)[kQMaxThreads / 64],
+                                             int j0 = 0, int cw = 0x7fffffff) {
     const int nchunks = (int)(K / EPT);
     const int w0 = (threadIdx.x - lt) >> 6, nw = nt >> 6;
     float tmax = 0.0f;
@@ -348,8 +361,9 @@ __device__ __forceinline__ void row_quantize(float (&v)[NC][EPT], int64_t K, int
     const float amax = group_max(tmax, red[0], w0, nw);
     const float s_g = FMT == kNV ? amax / 2688.0f : 0.0f;
     if (active) {
-        store_head(rec, s_g, lt);
-        quantize_chunks<FMT, NC, EPT>(v, nchunks, s_g, rec + kActHead, rec + kActHead + K / 2, lt, nt);
+        if (j0 == 0) store_head(rec, s_g, lt);
+        quantize_chunks<FMT, NC, EPT>(v, nchunks, s_g, rec + kActHead, rec + kActHead + K / 2, lt, nt, j0, cw,
+                                      with_res != 0);
     }
     if (!with_res) return;
     // v now holds the residue (zero in chunks past K): second row statistic.
@@ -361,8 +375,9 @@ __device__ __forceinline__ void row_quantize(float (&v)[NC][EPT], int64_t K, int
     const float ramax = group_max(rmax, red[1], w0, nw);
     const float r_g = FMT == kNV ? ramax / 2688.0f : 0.0f;
     if (active) {
-        store_head(rrec, r_g, lt);
-        quantize_chunks<FMT, NC, EPT>(v, nchunks, r_g, rrec + kActHead, rrec + kActHead + K / 2, lt, nt);
+        if (j0 == 0) store_head(rrec, r_g, lt);
+        quantize_chunks<FMT, NC, EPT>(v, nchunks, r_g, rrec + kActHead, rrec + kActHead + K / 2, lt, nt, j0, cw,
+                                      false);
     }
 }
 

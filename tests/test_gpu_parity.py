@@ -119,6 +119,23 @@ def test_quantize_quotient_near_ties(K):
     assert_quant_equal(x, 0, False, True)
 
 
+# NVFP4 rows shared by several workgroups (at most 256 rows x parts on a
+# 256-CU device): two to eight parts of whole waves, a ragged last part
+# (K = 8224: 1028 chunks of 8 in parts of 320), the part count cut by M
+# (M = 100: two parts) and none left (M = 300), with and without residue
+@pytest.mark.parametrize("MK", [(1, 8224), (3, 16384), (5, 14336), (40, 4096), (100, 8192), (300, 4160)],
+                         ids=lambda t: "M%dK%d" % t)
+def test_quantize_row_parts_bitexact(MK):
+    M, K = MK
+    rng = np.random.default_rng(M + K)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    x[:, rng.choice(K, max(1, K // 100), replace=False)] *= 20
+    x[0, :16] = 0.0
+    assert_quant_equal(x, 0, True, True)
+    assert_quant_equal(x, 0, False, True)
+    assert_quant_equal(x, 0, True, False)
+
+
 @pytest.mark.parametrize("fmt", [0, 1])
 def test_quantize_exact_residue_identity(fmt):
     """The buffer's base and residue rows dequantize to d and d_r with
