@@ -463,16 +463,17 @@ struct NvArgs {
     float* part;        // ks > 1: partial sums, per tile, wave and slice
 };
 
-// RTW 16-row tiles (the workgroup's rows, every wave) x CTW 16-channel groups
-// per wave; NS activation stages in LDS (2 or 4: the activations of step s
-// are requested NS - 1 steps ahead)
-template <bool COMP, int RTW, int CTW, int NS>
-__global__ __launch_bounds__(256, 2) void gemm_tile_nv_dma(NvArgs p) {
+// NW waves, each with RTW 16-row tiles (the workgroup's rows, every wave) x
+// CTW 16-channel groups; NS activation stages in LDS (2 or 4: the activations
+// of step s are requested NS - 1 steps ahead)
+template <bool COMP, int RTW, int CTW, int NS, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void gemm_tile_nv_dma(NvArgs p) {
     static_assert(NS == 2 || NS == 4, "two or four activation stages");
+    static_assert((4 * RTW) % NW == 0, "a stage's 1 KB blocks divide among the waves");
     constexpr int RD = 4;                             // weight ring depth (steps)
-    constexpr int TM = 16 * RTW, GPT = 4 * CTW;       // workgroup rows, channel groups
+    constexpr int TM = 16 * RTW, GPT = NW * CTW;      // workgroup rows, channel groups
     constexpr int STAGE = RTW * 4096;                 // one step of TM rows as f16: [u4][rt] blocks of 1 KB
-    constexpr int DA = 4 * RTW / 4;                   // per-wave requests of one stage
+    constexpr int DA = 4 * RTW / NW;                  // per-wave requests of one stage
     __shared__ __attribute__((aligned(16))) uint8_t st0[STAGE];
     __shared__ __attribute__((aligned(16))) uint8_t st1[STAGE];
     __shared__ __attribute__((aligned(16))) uint8_t st2[NS == 4 ? STAGE : 16];
@@ -514,7 +515,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_nv_dma(NvArgs p) {
     int a_dst[DA];
 #pragma unroll
     for (int j = 0; j < DA; ++j) {
-        const int blk = wave + 4 * j, rt = blk >> 2, u4 = blk & 3;
+        const int blk = wave + NW * j, rt = blk >> 2, u4 = blk & 3;
         a_vo[j] = (uint32_t)(rt * GA) + (uint32_t)(u4 * 1024) + 16u * lane;
         a_dst[j] = (u4 * RTW + rt) * 1024;
     }
@@ -676,7 +677,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_nv_dma(NvArgs p) {
         // memory side that all XCDs share), and the partial's stores complete
         // before the count.
         constexpr int NVAL = RTW * CTW * FV;
-        const int64_t wt = tile * 4 + wave;
+        const int64_t wt = tile * NW + wave;
         float* rec = p.part + (wt * p.ks + split) * (NVAL * 64) + lane;
 #pragma unroll
         for (int rt = 0; rt < RTW; ++rt)
@@ -772,14 +773,21 @@ hipError_t launch_act_tile(int fmt, bool comp, const void* act, int64_t row_byte
 
 namespace {
 
+// Waves of an NVFP4 product workgroup, 32 channels each: 8 (256 channels, one
+// activation stage shared by twice the channels) from 16384 channels, else 4
+// (more tiles where channels are few; measured at M = 128, K = 8192,
+// N = 28672: 103 against 111 us, and at M = 128, K = N = 4096: 30.3
+// against 27.0 us).
+int nv_waves(int64_t N) { return num_groups(N) >= 1024 ? 8 : 4; }
+
 // Rows of the NVFP4 product's tiles: 64 up to 128 operand rows (a 128-row tile
 // would be half empty at 33..64 rows, and at 65..128 rows twice the channel
 // tiles fill more compute units; measured at K = 8192, N = 28672: 46 against
 // 66 us at 64 rows, 65-68 against 70-77 us at 128, equal at 256), else 128.
 int nv_tile_rows(int64_t B) { return B <= 128 ? 64 : 128; }
 int64_t nv_tiles(int64_t B, int64_t N) {
-    const int tm = nv_tile_rows(B);
-    return (B + tm - 1) / tm * ((num_groups(N) + 7) / 8);
+    const int tm = nv_tile_rows(B), nw = nv_waves(N);
+    return (B + tm - 1) / tm * ((num_groups(N) + nw * 2 - 1) / (nw * 2));
 }
 
 // Steps per slice of a split into ks slices: a multiple of 8 (the product's
@@ -794,7 +802,8 @@ int slice_steps(int64_t S, int ks) { return (int)(((S + ks - 1) / ks + 7) & ~(in
 int nv_tile_split(int64_t B, int64_t N, int64_t K, int num_cus) {
     const int64_t tiles = nv_tiles(B, N), S = num_steps(K);
     int ks = 1;
-    while (ks < kMaxTileSplit && tiles * 2 * ks <= num_cus && S >= 16 * ks && tiles * 4 <= kSplitGroups) ks *= 2;
+    while (ks < kMaxTileSplit && tiles * 2 * ks <= num_cus && S >= 16 * ks && tiles * nv_waves(N) <= kSplitGroups)
+        ks *= 2;
     return ks <= 1 ? 1 : (int)((S + slice_steps(S, ks) - 1) / slice_steps(S, ks));
 }
 
@@ -802,7 +811,7 @@ int nv_tile_split(int64_t B, int64_t N, int64_t K, int num_cus) {
 // channel groups x 64 lanes x 2 values per lane (compensated: one per token of
 // each pair of rows) or 4 (plain).
 int64_t nv_split_bytes(int64_t B, int64_t N, int ks, bool comp) {
-    return ks <= 1 ? 0 : nv_tiles(B, N) * 4 * ks * (nv_tile_rows(B) / 16) * 2 * (comp ? 2 : 4) * 64 * 4;
+    return ks <= 1 ? 0 : nv_tiles(B, N) * nv_waves(N) * ks * (nv_tile_rows(B) / 16) * 2 * (comp ? 2 : 4) * 64 * 4;
 }
 
 hipError_t launch_gemm_tile_dma_nv(bool comp, const void* act_tiled, const void* act, int64_t row_bytes,
@@ -818,18 +827,26 @@ hipError_t launch_gemm_tile_dma_nv(bool comp, const void* act_tiled, const void*
     }
     const int64_t B = comp ? 2 * (int64_t)M : M;
     const int tm = nv_tile_rows(B);
-    a.grid = tile_grid(B, N, tm, 128);
+    const int nw = nv_waves(N);
+    a.grid = tile_grid(B, N, tm, 16 * 2 * nw);
     a.grid.tiles *= a.ks;
     a.grid.per_xcd = (a.grid.tiles + kXcds - 1) / kXcds;
     const dim3 grid((unsigned)(a.grid.per_xcd * kXcds));
     // 64-row tiles: four activation stages (64 KB of LDS, two workgroups per
     // CU); 128-row tiles: two (64 KB)
-    if (tm == 64) {
-        if (comp) hipLaunchKernelGGL((gemm_tile_nv_dma<true, 4, 2, 4>), grid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((gemm_tile_nv_dma<false, 4, 2, 4>), grid, dim3(256), 0, s, a);
+    auto run = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(64 * nw), 0, s, a); };
+    if (tm == 64 && nw == 4) {
+        if (comp) run(gemm_tile_nv_dma<true, 4, 2, 4, 4>);
+        else run(gemm_tile_nv_dma<false, 4, 2, 4, 4>);
+    } else if (tm == 64) {
+        if (comp) run(gemm_tile_nv_dma<true, 4, 2, 4, 8>);
+        else run(gemm_tile_nv_dma<false, 4, 2, 4, 8>);
+    } else if (nw == 4) {
+        if (comp) run(gemm_tile_nv_dma<true, 8, 2, 2, 4>);
+        else run(gemm_tile_nv_dma<false, 8, 2, 2, 4>);
     } else {
-        if (comp) hipLaunchKernelGGL((gemm_tile_nv_dma<true, 8, 2, 2>), grid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((gemm_tile_nv_dma<false, 8, 2, 2>), grid, dim3(256), 0, s, a);
+        if (comp) run(gemm_tile_nv_dma<true, 8, 2, 2, 8>);
+        else run(gemm_tile_nv_dma<false, 8, 2, 2, 8>);
     }
     return hipGetLastError();
 }

@@ -140,15 +140,16 @@ size_t rsfp4_packed_weight_bytes(int fmt, int64_t N, int64_t K);
  * 16384 + ceil(B/16) * ceil(K/128) * 4096 bytes) -- so that the activations
  * stream into LDS as contiguous 1 KB requests.  Given a NULL or smaller
  * workspace the call multiplies the records directly, with the same bits.
- * An NVFP4 product with few tiles (64 x 128 up to 128 operand rows, else
- * 128 x 128; while twice the tiles stay within the compute units, K holds at
- * least 16 steps per slice pair and the tiles number at most 1024) splits K
+ * An NVFP4 product's tiles are 64 rows up to 128 operand rows, else 128, by
+ * 32 channels per wave, W = 4 waves (W = 8 from N = 16384 on).  With few
+ * tiles (while twice the tiles stay within the compute units, K holds at
+ * least 16 steps per slice pair and tiles x W is at most 4096) it splits K
  * into ks = 2..8 slices of a multiple of 8 steps: its workspace adds, at the
  * next 256-byte boundary after the rewritten operand, one record of folded
- * partial sums per tile, wave (4) and slice (the tile's rows / 16 x 2 x 64 x
+ * partial sums per tile, wave and slice (the tile's rows / 16 x 2 x 64 x
  * 2 floats compensated, one per token of each row pair, x 4 plain),
- * and the 4 counters of each tile in the counter area count the slices in and
- * are left zero; the slices are summed in slice order.  With a workspace that
+ * and W counters per tile in the counter area count the slices in and are
+ * left zero; the slices are summed in slice order.  With a workspace that
  * holds the rewritten operand but not the partials the product runs unsplit
  * (the same result up to the summation order of the slices).  Without a
  * device to count compute units on the size is the unsplit one.  Wide shapes
@@ -193,8 +194,9 @@ rsfp4_status rsfp4_mxfp4_quantize_act_with_residue(const void* x, int xt, int64_
  * 32 rows (compensated NVFP4 with N <= 4096 and K <= 4096: up to 64), each
  * packed weight step is loaded from HBM once and multiplied with all B rows
  * (the narrow-M, memory-bound regime); above that a 2-D tiled kernel covers
- * 128 rows x 128 channels per workgroup (NVFP4 up to 128 rows: 64 x 128; each
- * weight tile is then read once per 64 or 128 rows).  Either way base and residue products of one token
+ * 128 rows x 128 channels per workgroup (NVFP4: 64 rows up to 128 operand
+ * rows, and 256 channels from N = 16384 on; each weight tile is then read
+ * once per 64 or 128 rows).  Either way base and residue products of one token
  * land in the same lane's accumulators and are added there before the single
  * store (ResServe Section 4.3, Eq. 2 and Section 5.1, Eq. 4).  With up to 32
  * rows and K above 16384 the narrow kernel runs twice, over the two halves of

@@ -151,8 +151,11 @@ def test_split_deterministic(case, bf16):
         assert torch.equal(y.view(it), ys[0].view(it))
     assert int(ws[:16384].count_nonzero()) == 0, "the split's counters must be left zero"
     y1 = _call(fmt, act, blob, M, N, K, comp, _ws(fmt, M, N, K, comp, split=False), bf16).float()
-    d = (ys[0].float() - y1).abs().max().item()
-    assert d <= 1e-4 * max(1.0, y1.abs().max().item()), d
+    # fp32 sums that differ in the last bits may round to neighbouring bf16
+    # values: one bf16 ulp, at most 2^-7 of the value
+    tol = 1e-4 * max(1.0, y1.abs().max().item()) + (2.0 ** -7 if bf16 else 0.0) * y1.abs()
+    d = (ys[0].float() - y1).abs()
+    assert bool((d <= tol).all()), float(d.max())
 
 
 @pytest.mark.parametrize("wl", [inputs.MX.with_m(m) for m in (17, 32, 64, 128, 256)]
