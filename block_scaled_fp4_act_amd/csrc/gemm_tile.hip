@@ -450,20 +450,10 @@ hipError_t launch_tile_t(TileArgs a, hipStream_t s) {
 // two workgroups per CU.  An MXFP4 step is a single FP4 MFMA per tile, so its
 // activation fragments are read from LDS four times as often per MFMA; a
 // 128 x 256 tile halves that, at one workgroup per CU.
-#ifndef RSFP4_TILE_MX_CTW
-#define RSFP4_TILE_MX_CTW 4
-#endif
-#ifndef RSFP4_TILE_MX_RD
-#define RSFP4_TILE_MX_RD 4
-#endif
-#ifndef RSFP4_TILE_MX_OCC
-#define RSFP4_TILE_MX_OCC 1
-#endif
-
 template <int FMT, bool COMP>
 hipError_t launch_fmt(const TileArgs& a, hipStream_t s) {
     if (FMT == kNV) return launch_tile_t<FMT, COMP, 8, 2, 4, 2>(a, s);
-    return launch_tile_t<FMT, COMP, 8, RSFP4_TILE_MX_CTW, RSFP4_TILE_MX_RD, RSFP4_TILE_MX_OCC>(a, s);
+    return launch_tile_t<FMT, COMP, 8, 4, 4, 1>(a, s);
 }
 
 }  // namespace
