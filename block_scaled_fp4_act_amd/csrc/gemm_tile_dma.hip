@@ -438,14 +438,16 @@ hipError_t launch_mx_tiles(const DmaArgs& a, int num_cus, hipStream_t s) {
 
 
 // ---- NVFP4: f16 activation fragments (DMA) x weights from a register ring ----
-// The register-staged kernel's structure (4 waves, two workgroups per compute
-// unit; a workgroup owns 128 rows x 128 channels, each wave all 128 rows and
-// its own 2 groups of 16 channels, whose weight fragments it streams into a
-// register ring 3 steps ahead and dequantizes to f16 at use, the scale words a
-// quad ahead), with the activation staging replaced: the f16 fragments of each
-// step (32 KB) stream into one of two LDS stages by DMA instead of passing
-// through registers, a dequantization and LDS stores in every workgroup.  Same
-// f16 operands and MFMA order as that kernel: bit-identical results.
+// The register-staged kernel's structure (each wave all the workgroup's rows
+// and its own 2 groups of 16 channels, whose weight fragments it streams into
+// a register ring 3 steps ahead and dequantizes to f16 at use, the scale words
+// a quad ahead), with the activation staging replaced: the f16 fragments of
+// each step stream into LDS stages by DMA instead of passing through
+// registers, a dequantization and LDS stores in every workgroup.  Tiles of 64
+// or 128 rows, 4 or 8 waves (128 or 256 channels) sharing each stage, and K
+// optionally split across workgroups (see nv_tile_rows, nv_waves and
+// nv_tile_split below).  Same f16 operands and MFMA order as that kernel:
+// bit-identical results (unsplit).
 struct NvArgs {
     const uint8_t* at;     // f16 activation fragments (act_tile_f16_kernel)
     const uint8_t* act;    // the activation records (per-row tensor scales)
