@@ -229,17 +229,17 @@ rsfp4_status rsfp4_mxfp4_linear_compensated(const void* act, size_t act_bytes, c
  * Where the plan splits K it uses the library's own scratch, a device array of
  * 16384 + 16777216 bytes on each GPU (held until the process ends; its address
  * is taken, and its counter area cleared on `stream`, by the first call on a
- * device).  Wide operands (more than 64 operand rows, or N or K above 16384)
- * use the scratch for their rewritten activations and a split's partial sums
- * as far as they fit in it: a split that does not fit runs unsplit, and
- * rewritten activations that do not fit (more than 16777216 bytes:
- * ceil(2M/16) * ceil(K/128) * 4096) are not made (the records path, the same
- * bits as the unsplit tiled product).  It calls no allocator.  Shapes whose
- * split would need more than the scratch holds are rejected with
- * RSFP4_ERR_UNSUPPORTED (none of the plans this library makes on a 256-CU
- * device does).  Every call on a GPU
- * shares that GPU's scratch: calls that may overlap on one GPU (other streams,
- * other threads) race; calls in stream order do not. */
+ * device).  Wide operands (more than 32 operand rows, except 33..64 with N
+ * and K at most 4096) use the scratch for their rewritten activations and a
+ * split's partial sums as far as they fit in it: a split that does not fit
+ * runs unsplit, and rewritten activations that do not fit (more than 16777216
+ * bytes: ceil(2M/16) * ceil(K/128) * 4096) are not made (the records path,
+ * the same bits as the unsplit tiled product).  It calls no allocator.
+ * Narrow shapes whose split would need more than the scratch holds are
+ * rejected with RSFP4_ERR_UNSUPPORTED (none of the plans this library makes on
+ * a 256-CU device does).  Every call on a GPU shares that GPU's scratch:
+ * calls that may overlap on one GPU (other streams, other threads) race;
+ * calls in stream order do not. */
 rsfp4_status rsfp4_nvfp4_linear_compensated_noalloc(const void* act, size_t act_bytes, const void* w_packed,
                                                     size_t w_packed_bytes, int64_t M, int64_t N, int64_t K,
                                                     float* y, void* stream);
