@@ -235,9 +235,11 @@ def _weights(wl):
     return _W_CACHE[key]
 
 
-KEXT_CASES = [  # (M, N, K, k): narrow and tiled kernels, ragged N, K tails of a quad
+KEXT_CASES = [  # (M, N, K, k): narrow and tiled kernels, ragged N, K tails of a quad,
+    # and (NVFP4) a tiled product split in K (K_eff = 5120: 40 steps in slices of 16, 16, 8)
     (1, 512, 512, 1), (4, 264, 512, 2), (8, 100, 1024, 4), (16, 72, 256, 8),
     (33, 130, 768, 2), (64, 128, 256, 4), (129, 300, 512, 1), (200, 64, 1024, 2),
+    (64, 200, 4096, 2),
 ]
 
 
