@@ -34,11 +34,12 @@ def test_noalloc_matches_workspace_entry():
     oracle.build()
     # the MLP down projection (K split in four on a 256-CU device), then a
     # smaller split call, a shape whose plan does not split, two row tiles
-    # split in two, a wide operand whose rewritten activations and split
-    # partials fit in the scratch (1 + 2 MB) and one whose do not (32 MB: it
-    # runs without them, with the records path's bits)
+    # split in two, wide operands whose rewritten activations and split
+    # partials fit in the scratch (1 + 2 MB; 8-wave tiles over N = 16400,
+    # 0.4 + 8.3 MB) and one whose do not (32 MB: it runs without them, with
+    # the records path's bits)
     for i, (M, N, K) in enumerate([(8, 4096, 14336), (3, 512, 8192), (4, 1024, 4096), (16, 2048, 8192),
-                                   (64, 1024, 4096), (1024, 256, 8192)]):
+                                   (64, 1024, 4096), (20, 16400, 4096), (1024, 256, 8192)]):
         x, W, blob, act = _case(M, N, K, 40 + i)
         # the workspace entry given what the scratch holds of the workspace
         nb = min(rs.workspace_bytes(0, M, N, K, True), 16384 + 16777216)
