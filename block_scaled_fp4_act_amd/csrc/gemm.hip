@@ -702,17 +702,16 @@ GemmPlan plan_gemm_small(int64_t M, int64_t N, int64_t S, bool comp, int num_cus
     if (!split_ok || pl.rt > 2 || !comp) return pl;
 
     // Split K across workgroups (one workgroup per CU, each owning one K slice
-    // of several channel groups), where one of two shapes makes it pay
-    // (measured on the compensated NVFP4 MLP pair, M = 8):
-    //   * few groups, long K (G <= CUs, S >= 64): four slices, so a workgroup
-    //     streams four groups' slices instead of one group's whole K and holds
-    //     a quarter of the activation operand (K = 14336, N = 4096: 12.5
-    //     against 14.8 us);
-    //   * a half round of groups (G a multiple of CUs / 2 but not of CUs): two
-    //     slices make the (group, slice) units a multiple of the CUs (K = 4096,
-    //     N = 14336: 10.7 against 12.6 us).
-    // The MXFP4 shapes and K = N = 4096 are slower split (one handoff costs
-    // about as much as a whole K = 4096 group).
+    // of several channel groups) where the shape makes it pay: few groups with
+    // long K (G <= CUs, S >= 64): four slices, so a workgroup streams four
+    // groups' slices instead of one group's whole K and holds a quarter of
+    // the activation operand (K = 14336, N = 4096, M = 8: 11.8 against
+    // 14.2 us).  A half round of groups (G a multiple of CUs / 2 but not of
+    // CUs) split in two, which once paid, is now slower than the unsplit
+    // four-steps-per-wave plan (K = 4096, N = 14336: 10.3 against 9.8 us at
+    // M = 8, 10.3 against 8.7 us at M = 2).  The MXFP4 shapes and
+    // K = N = 4096 are slower split (one handoff costs about as much as a
+    // whole K = 4096 group).
     int ks = 0;
     if (G > kSplitGroups) return pl;
     if (pl.rt == 2) {
@@ -725,8 +724,6 @@ GemmPlan plan_gemm_small(int64_t M, int64_t N, int64_t S, bool comp, int num_cus
             if (S % k == 0 && ((S / k) % 2 == 0 || S / k <= kMaxWaves)) ks = k;
     } else if (G <= num_cus && S >= 64 && S % 4 == 0) {
         ks = 4;
-    } else if (G > num_cus && G % num_cus != 0 && (2 * G) % num_cus == 0 && S % 4 == 0 && S <= 64) {
-        ks = 2;
     }
     if (ks == 0) return pl;
     const int64_t ss = S / ks;

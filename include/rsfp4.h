@@ -113,13 +113,13 @@ size_t rsfp4_packed_weight_bytes(int fmt, int64_t N, int64_t K);
 /* Device workspace (bytes) with which a linear call of this shape may split K
  * across workgroups; 0 when its plan does not split.  The value depends on the
  * current device's compute-unit count.  Shapes that split (compensated NVFP4,
- * K <= 16384 on the narrow kernel: with at most 16 operand rows where one of
- * two patterns makes the split faster -- few 16-channel groups with K of 64
- * and more steps of 128, or a number of groups that leaves the last round of
- * workgroups half empty; the ResServe page's tile-count model, Section 5.1
- * Eq. 5, names the second -- and with 17..32 operand rows when K of more
- * than 32 steps of 128 divides into 2..4 equal slices of at most 32 steps,
- * one pass over K instead of launches of 32 steps) sum their K slices' partial outputs
+ * K <= 16384 on the narrow kernel: with at most 16 operand rows when there are
+ * few 16-channel groups (at most one per compute unit) and K of 64 and more
+ * steps of 128 -- the ResServe page's tile-count model, Section 5.1 Eq. 5:
+ * too few units of work leave compute units idle -- and with 17..32 operand
+ * rows when K of more than 32 steps of 128 divides into 2..4 equal slices of
+ * at most 32 steps, one pass over K instead of launches of 32 steps) sum
+ * their K slices' partial outputs
  * through the workspace: 4096 int counters, one per 16-channel group (the first 16384
  * bytes; only N of at most 4096 groups splits), then one partial-sum record
  * per group and slice.  The counters must be zero before the workspace's
