@@ -53,7 +53,7 @@ METRIC = "compensated FP4 linear µs/call + HBM GB/s (% of peak) at M=1–8, K,N
 # calibration factors (FETCH_SIZE x2.0, WRITE_SIZE x1.0).  Valid only for the
 # kernel sources whose hash is recorded; reported as null otherwise.
 TRAFFIC = {
-    "sources_sha256": "1babbbbe91c6aaa8d09e42ba12ab84543bc1dec103bcd23b72243b30ad39c956",
+    "sources_sha256": "838d053b533f7e0f2da85baadf0b1b003ce9d3c3c016b989f5fc9cbf38729c36",
     "fetch_bytes": 132851712,     # 2.0 x 64,869 KiB
     "write_bytes": 917504,        # 1.0 x 896 KiB
 }

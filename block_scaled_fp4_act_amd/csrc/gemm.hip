@@ -682,12 +682,12 @@ GemmPlan plan_gemm_small(int64_t M, int64_t N, int64_t S, bool comp, int num_cus
     pl.rt = B <= 16 ? 1 : (B <= 32 ? 2 : 4);
     const int64_t G = num_groups(N);
     // the fewest steps per wave (a power of two) that covers K with <= 16 waves;
-    // compensated with one row tile and more groups than compute units, K of
-    // 17..32 steps takes four steps per wave over eight waves, one workgroup
-    // per CU (K = 4096, N = 14336, M = 8: 9.8 against 11.1 us for two steps
-    // over 16 waves)
+    // compensated with one row tile and at least as many groups as compute
+    // units, K of 17..32 steps takes four steps per wave over eight waves, one
+    // workgroup per CU (K = 4096, N = 14336, M = 8: 9.8 against 10.4 us for
+    // two steps over 16 waves; K = N = 4096, M = 4: 5.8 against 6.05 us)
     pl.maxs = S <= 16 ? 1 : (S <= 32 ? 2 : (S <= 64 ? 4 : 8));
-    const bool wide4 = comp && pl.rt == 1 && S > 16 && S <= 32 && G > num_cus;
+    const bool wide4 = comp && pl.rt == 1 && S > 16 && S <= 32 && G >= num_cus;
     if (wide4) pl.maxs = 4;
     pl.kw = (int)((S + pl.maxs - 1) / pl.maxs);
     const int per_cu = wide4 ? 1 : (kMaxWaves / pl.kw > 0 ? kMaxWaves / pl.kw : 1);
