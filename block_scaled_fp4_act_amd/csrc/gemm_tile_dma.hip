@@ -783,12 +783,15 @@ namespace {
 int nv_waves(int64_t N) { return num_groups(N) >= 1024 ? 8 : 4; }
 
 // Rows of the NVFP4 product's tiles: 64 up to 128 operand rows (a 128-row tile
-// would be half empty at 33..64 rows, and at 65..128 rows twice the channel
+// would be half empty at 33..64 rows, and at 65..128 rows twice the row
 // tiles fill more compute units; measured at K = 8192, N = 28672: 46 against
-// 66 us at 64 rows, 65-68 against 70-77 us at 128, equal at 256), else 128.
-int nv_tile_rows(int64_t B) { return B <= 128 ? 64 : 128; }
+// 66 us at 64 rows, 65-68 against 70-77 us at 128), and up to 256 rows where
+// N is below 16384 (few channel tiles: K = N = 4096 at 256 rows 22.3 against
+// 26.9 us, K = 14336, N = 4096 42.9 against 47.1 us; at N = 28672 128-row
+// tiles stay 2-3 % faster, and at 512 rows the two are mixed); else 128.
+int nv_tile_rows(int64_t B, int64_t N) { return B <= 128 || (B <= 256 && num_groups(N) < 1024) ? 64 : 128; }
 int64_t nv_tiles(int64_t B, int64_t N) {
-    const int tm = nv_tile_rows(B), nw = nv_waves(N);
+    const int tm = nv_tile_rows(B, N), nw = nv_waves(N);
     return (B + tm - 1) / tm * ((num_groups(N) + nw * 2 - 1) / (nw * 2));
 }
 
@@ -813,7 +816,7 @@ int nv_tile_split(int64_t B, int64_t N, int64_t K, int num_cus) {
 // channel groups x 64 lanes x 2 values per lane (compensated: one per token of
 // each pair of rows) or 4 (plain).
 int64_t nv_split_bytes(int64_t B, int64_t N, int ks, bool comp) {
-    return ks <= 1 ? 0 : nv_tiles(B, N) * nv_waves(N) * ks * (nv_tile_rows(B) / 16) * 2 * (comp ? 2 : 4) * 64 * 4;
+    return ks <= 1 ? 0 : nv_tiles(B, N) * nv_waves(N) * ks * (nv_tile_rows(B, N) / 16) * 2 * (comp ? 2 : 4) * 64 * 4;
 }
 
 hipError_t launch_gemm_tile_dma_nv(bool comp, const void* act_tiled, const void* act, int64_t row_bytes,
@@ -828,7 +831,7 @@ hipError_t launch_gemm_tile_dma_nv(bool comp, const void* act_tiled, const void*
         a.ks = (int)((S + a.sl - 1) / a.sl);
     }
     const int64_t B = comp ? 2 * (int64_t)M : M;
-    const int tm = nv_tile_rows(B);
+    const int tm = nv_tile_rows(B, N);
     const int nw = nv_waves(N);
     a.grid = tile_grid(B, N, tm, 16 * 2 * nw);
     a.grid.tiles *= a.ks;
