@@ -389,27 +389,30 @@ __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmArgs p) {
     // per lane: compensated, token row (16 rt + 4 g + 2 pr) / 2 of channel i
     // per (row tile, pair); plain, tile rows ti0 and ti0 + 1.
     constexpr int PV = COMP ? 2 * RT : 4 * RT;
+    // The LDS reads of the partials go out in batches of RB waves (at most 16
+    // values per lane), one wait per batch: read one at a time, each waiting
+    // for the last, the 16 waves' partials took about 1.5 us at the end of
+    // every workgroup.
+    constexpr int RB = PV >= 16 ? 1 : 16 / PV;
     auto reduce_slot = [&](int64_t c, int slot) {
+        // value k of wave w's partial at base[(w * PV + k) * 64]
+        const float* base = red + slot * KW * PV * 64 + lane;
         float pv[PV];
 #pragma unroll
-        for (int item = 0; item < 2 * RT; ++item) {   // (row tile, pair) per lane
-            const int rt = item >> 1, pr = item & 1;
-            if (COMP) {
-                // the waves' folded partials of token row ti0 / 2, in wave order
-                const float* src = red + (slot * KW * RT + rt) * (PW * 64) + pr * 64 + lane;
-                float v = 0.0f;
-                for (int w = 0; w < KW; ++w) v += src[w * RT * (PW * 64)];
-                pv[item] = v;
-            } else {
-                const float* src = red + (slot * KW * RT + rt) * (PW * 64) + (2 * pr) * 64 + lane;
-                float v0 = 0.0f, v1 = 0.0f;
-                for (int w = 0; w < KW; ++w) {
-                    v0 += src[w * RT * (PW * 64)];
-                    v1 += src[w * RT * (PW * 64) + 64];
-                }
-                pv[2 * item] = v0;
-                pv[2 * item + 1] = v1;
+        for (int k = 0; k < PV; ++k) pv[k] = 0.0f;
+        for (int w0 = 0; w0 < KW; w0 += RB) {
+            float t[RB][PV];
+#pragma unroll
+            for (int u = 0; u < RB; ++u) {
+                const int w = w0 + u < KW ? w0 + u : KW - 1;   // in range; only w0 + u < KW is added
+#pragma unroll
+                for (int k = 0; k < PV; ++k) t[u][k] = base[(w * PV + k) * 64];
             }
+#pragma unroll
+            for (int u = 0; u < RB; ++u)
+                if (w0 + u < KW)
+#pragma unroll
+                    for (int k = 0; k < PV; ++k) pv[k] += t[u][k];
         }
         if constexpr (XS) {
             // Split K: publish this slice's partial, count it in, and let the
@@ -432,14 +435,27 @@ __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmArgs p) {
             if (lane == 0) old = __hip_atomic_fetch_add(p.cnt + c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             old = __builtin_amdgcn_readfirstlane(old);
             if (old != p.ks - 1) return;
+            // the loads of up to QB slices' partials are in flight together (at
+            // most 8 values per lane)
+            constexpr int QB = PV >= 8 ? 1 : 8 / PV;
             float tot[PV];
 #pragma unroll
             for (int k = 0; k < PV; ++k) tot[k] = 0.0f;
-            for (int q = 0; q < p.ks; ++q) {
-                const float* rq = p.ws + ((c * p.ks + q) * PV) * 64 + lane;
+            for (int q0 = 0; q0 < p.ks; q0 += QB) {
+                float t[QB][PV];
 #pragma unroll
-                for (int k = 0; k < PV; ++k)
-                    tot[k] += q == ks ? pv[k] : __hip_atomic_load(rq + k * 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                for (int u = 0; u < QB; ++u) {
+                    const int q = q0 + u < p.ks ? q0 + u : p.ks - 1;   // only q0 + u < ks is added
+                    const float* rq = p.ws + ((c * p.ks + q) * PV) * 64 + lane;
+#pragma unroll
+                    for (int k = 0; k < PV; ++k)
+                        t[u][k] = q == ks ? pv[k] : __hip_atomic_load(rq + k * 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+#pragma unroll
+                for (int u = 0; u < QB; ++u)
+                    if (q0 + u < p.ks)
+#pragma unroll
+                        for (int k = 0; k < PV; ++k) tot[k] += t[u][k];
             }
 #pragma unroll
             for (int k = 0; k < PV; ++k) pv[k] = tot[k];

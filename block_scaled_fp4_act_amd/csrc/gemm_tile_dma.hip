@@ -701,17 +701,35 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void gemm_tile_nv_dma(NvArgs p) {
             for (int ct = 0; ct < CTW; ++ct)
 #pragma unroll
                 for (int j = 0; j < FV; ++j) tot[rt][ct][j] = 0.0f;
-        for (int q = 0; q < p.ks; ++q) {
-            const float* rq = p.part + (wt * p.ks + q) * (NVAL * 64) + lane;
+        // the loads of QB slices' partials are in flight together (at most 64
+        // values per lane; one slice at a time, each waiting for the last,
+        // cost a memory round trip per slice)
+        constexpr int QB = NVAL >= 64 ? 1 : 64 / NVAL;
+        for (int q0 = 0; q0 < p.ks; q0 += QB) {
+            float t[QB][RTW][CTW][FV];
 #pragma unroll
-            for (int rt = 0; rt < RTW; ++rt)
+            for (int u = 0; u < QB; ++u) {
+                const int q = q0 + u < p.ks ? q0 + u : p.ks - 1;   // only q0 + u < ks is added
+                const float* rq = p.part + (wt * p.ks + q) * (NVAL * 64) + lane;
 #pragma unroll
-                for (int ct = 0; ct < CTW; ++ct)
+                for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
-                    for (int j = 0; j < FV; ++j)
-                        tot[rt][ct][j] += q == split ? f[rt][ct][j]
-                                                     : __hip_atomic_load(rq + ((rt * CTW + ct) * FV + j) * 64,
-                                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    for (int ct = 0; ct < CTW; ++ct)
+#pragma unroll
+                        for (int j = 0; j < FV; ++j)
+                            t[u][rt][ct][j] = q == split ? f[rt][ct][j]
+                                                         : __hip_atomic_load(rq + ((rt * CTW + ct) * FV + j) * 64,
+                                                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+#pragma unroll
+            for (int u = 0; u < QB; ++u)
+                if (q0 + u < p.ks)
+#pragma unroll
+                    for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+                        for (int ct = 0; ct < CTW; ++ct)
+#pragma unroll
+                            for (int j = 0; j < FV; ++j) tot[rt][ct][j] += t[u][rt][ct][j];
         }
 #pragma unroll
         for (int rt = 0; rt < RTW; ++rt)
