@@ -53,8 +53,8 @@ METRIC = "compensated FP4 linear µs/call + HBM GB/s (% of peak) at M=1–8, K,N
 # calibration factors (FETCH_SIZE x2.0, WRITE_SIZE x1.0).  Valid only for the
 # kernel sources whose hash is recorded; reported as null otherwise.
 TRAFFIC = {
-    "sources_sha256": "838d053b533f7e0f2da85baadf0b1b003ce9d3c3c016b989f5fc9cbf38729c36",
-    "fetch_bytes": 132851712,     # 2.0 x 64,869 KiB
+    "sources_sha256": "20ed006d2149b95685a6aaa186144db8cc527bab9a3235262384b05224e6e23e",
+    "fetch_bytes": 132855467,     # 2.0 x 64,870.83 KiB (mean of three launches)
     "write_bytes": 917504,        # 1.0 x 896 KiB
 }
 KERNEL_SOURCES = ["gemm.hip", "layout.h", "codec.h", "fp4_frag.h", "quant_row.h", "kernels.h"]
