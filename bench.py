@@ -53,7 +53,7 @@ METRIC = "compensated FP4 linear µs/call + HBM GB/s (% of peak) at M=1–8, K,N
 # calibration factors (FETCH_SIZE x2.0, WRITE_SIZE x1.0).  Valid only for the
 # kernel sources whose hash is recorded; reported as null otherwise.
 TRAFFIC = {
-    "sources_sha256": "20ed006d2149b95685a6aaa186144db8cc527bab9a3235262384b05224e6e23e",
+    "sources_sha256": "e54e314917d3683aae23ffaa095f514c7c41689daaa49c5cd8c7edcaf5ad3e73",
     "fetch_bytes": 132855467,     # 2.0 x 64,870.83 KiB (mean of three launches)
     "write_bytes": 917504,        # 1.0 x 896 KiB
 }
