@@ -800,14 +800,19 @@ namespace {
 // against 27.0 us).
 int nv_waves(int64_t N) { return num_groups(N) >= 1024 ? 8 : 4; }
 
-// Rows of the NVFP4 product's tiles: 64 up to 128 operand rows (a 128-row tile
-// would be half empty at 33..64 rows, and at 65..128 rows twice the row
-// tiles fill more compute units; measured at K = 8192, N = 28672: 46 against
-// 66 us at 64 rows, 65-68 against 70-77 us at 128), and up to 256 rows where
-// N is below 16384 (few channel tiles: K = N = 4096 at 256 rows 22.3 against
-// 26.9 us, K = 14336, N = 4096 42.9 against 47.1 us; at N = 28672 128-row
-// tiles stay 2-3 % faster, and at 512 rows the two are mixed); else 128.
-int nv_tile_rows(int64_t B, int64_t N) { return B <= 128 || (B <= 256 && num_groups(N) < 1024) ? 64 : 128; }
+// Rows of the NVFP4 product's tiles: 64 up to 64 operand rows and at 128
+// (at 128 rows both forms measured within 3 %, the 64-row one ahead in the
+// plain product), and up to 256 rows where N is below 16384 (few channel
+// tiles: K = N = 4096 at 256 rows 22.3 against 26.9 us, K = 14336, N = 4096
+// 42.9 against 47.1 us); else 128.  At 65..127 rows and wide N one 128-row
+// tile reads the weights once and splits K where its tiles are few, against
+// two 64-row tiles reading them twice (K = 8192, N = 28672: 57.4-57.7
+// against 60.0-60.2 us at 68 rows, 60.6 against 61.6-62.7 us at 96); at
+// N = 28672 and 256 rows the 128-row tiles are 2-3 % faster, and at 512
+// rows the two are mixed.
+int nv_tile_rows(int64_t B, int64_t N) {
+    return B <= 64 || B == 128 || (B <= 256 && num_groups(N) < 1024) ? 64 : 128;
+}
 int64_t nv_tiles(int64_t B, int64_t N) {
     const int tm = nv_tile_rows(B, N), nw = nv_waves(N);
     return (B + tm - 1) / tm * ((num_groups(N) + nw * 2 - 1) / (nw * 2));
