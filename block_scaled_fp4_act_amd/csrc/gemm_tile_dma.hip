@@ -800,18 +800,20 @@ namespace {
 // against 27.0 us).
 int nv_waves(int64_t N) { return num_groups(N) >= 1024 ? 8 : 4; }
 
-// Rows of the NVFP4 product's tiles: 64 up to 64 operand rows and at 128
-// (at 128 rows both forms measured within 3 %, the 64-row one ahead in the
-// plain product), and up to 256 rows where N is below 16384 (few channel
-// tiles: K = N = 4096 at 256 rows 22.3 against 26.9 us, K = 14336, N = 4096
-// 42.9 against 47.1 us); else 128.  At 65..127 rows and wide N one 128-row
-// tile reads the weights once and splits K where its tiles are few, against
-// two 64-row tiles reading them twice (K = 8192, N = 28672: 57.4-57.7
-// against 60.0-60.2 us at 68 rows, 60.6 against 61.6-62.7 us at 96); at
-// N = 28672 and 256 rows the 128-row tiles are 2-3 % faster, and at 512
+// Rows of the NVFP4 product's tiles: 64 up to 64 operand rows and from 97
+// to 128, and up to 256 rows where N is below 16384 (few channel tiles:
+// K = N = 4096 at 256 rows 22.3 against 26.9 us, K = 14336, N = 4096 42.9
+// against 47.1 us); else 128.  At 65..96 rows and wide N one 128-row tile
+// reads the weights once and splits K where its tiles are few, against two
+// 64-row tiles reading them twice (K = 8192, N = 28672, compensated: 60.3-61.0
+// against 64.3-64.7 us at 68 rows, 58.3-58.6 against 62.9-66.0 at 80,
+// 60.7-62.3 against 64.6-65.7 at 96; plain at 80 rows 63.8 against 64.2-64.7);
+// from 100 rows the plain product is 4-5 % slower on one tile (67.9-72.1
+// against 64.5-69.2 us at 100 and 120), and at 128 the two are within 3 %.
+// At N = 28672 and 256 rows the 128-row tiles are 2-3 % faster, and at 512
 // rows the two are mixed.
 int nv_tile_rows(int64_t B, int64_t N) {
-    return B <= 64 || B == 128 || (B <= 256 && num_groups(N) < 1024) ? 64 : 128;
+    return B <= 64 || (B > 96 && B <= 128) || (B <= 256 && num_groups(N) < 1024) ? 64 : 128;
 }
 int64_t nv_tiles(int64_t B, int64_t N) {
     const int tm = nv_tile_rows(B, N), nw = nv_waves(N);

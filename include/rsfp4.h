@@ -140,8 +140,8 @@ size_t rsfp4_packed_weight_bytes(int fmt, int64_t N, int64_t K);
  * 16384 + ceil(B/16) * ceil(K/128) * 4096 bytes) -- so that the activations
  * stream into LDS as contiguous 1 KB requests.  Given a NULL or smaller
  * workspace the call multiplies the records directly, with the same bits.
- * An NVFP4 product's tiles are 64 rows up to 64 operand rows and at 128
- * (and up to 256 below N = 16384), else 128, by 32 channels per wave, W = 4 waves (W = 8
+ * An NVFP4 product's tiles are 64 rows up to 64 operand rows and from 97
+ * to 128 (and up to 256 below N = 16384), else 128, by 32 channels per wave, W = 4 waves (W = 8
  * from N = 16384 on).  With few
  * tiles (while twice the tiles stay within the compute units, K holds at
  * least 16 steps per slice pair and tiles x W is at most 4096) it splits K
@@ -196,7 +196,7 @@ rsfp4_status rsfp4_mxfp4_quantize_act_with_residue(const void* x, int xt, int64_
  * packed weight step is loaded from HBM once and multiplied with all B rows
  * (the narrow-M, memory-bound regime); above that a 2-D tiled kernel covers
  * 128 rows x 128 channels per workgroup (NVFP4: 64 rows up to 64 operand
- * rows and at 128, up to 256 below N = 16384, and 256 channels from N = 16384 on; each
+ * rows and from 97 to 128, up to 256 below N = 16384, and 256 channels from N = 16384 on; each
  * weight tile is then read once per 64 or 128 rows).  Either way base and residue products of one token
  * land in the same lane's accumulators and are added there before the single
  * store (ResServe Section 4.3, Eq. 2 and Section 5.1, Eq. 4).  With up to 32

@@ -31,7 +31,7 @@ def _rs():
 
 
 # (M, N, K, compensated): more than 32 stacked rows (NVFP4 64-row tiles up to
-# 64 rows and at 128, and up to 256 below N = 16384: 180 rows in three); ragged row tiles (rows
+# 64 rows and from 97 to 128, and up to 256 below N = 16384: 180 rows in three); ragged row tiles (rows
 # past the operand), ragged channel tiles (N not a multiple of 16 or 256),
 # K tails (K not a multiple of 128, or of 512: a partial last quad), a long K,
 # and N past one channel tile many times over
@@ -39,8 +39,8 @@ CASES = [(17, 264, 384, True), (33, 130, 160, False), (40, 512, 1056, True), (64
          (100, 72, 2048, False), (129, 300, 512, True), (40, 64, 24576, True), (30, 16400, 256, True),
          (200, 1000, 1184, True), (48, 520, 5152, False), (300, 40, 96, True), (37, 2056, 4096, True),
          (20, 16400, 4096, True), (90, 520, 1184, True),
-         # 65..127 stacked rows at wide N: one 128-row tile (split in K when few)
-         (40, 16400, 4096, True), (100, 16400, 1184, False)]
+         # 65..96 stacked rows at wide N: one 128-row tile (split in K when few)
+         (40, 16400, 4096, True), (90, 16400, 1184, False)]
 # NVFP4 compensated with 33..64 stacked rows, N <= 4096 and K <= 4096 runs
 # the narrow kernel with four row tiles instead: those shapes are left out
 NV_NARROW4 = lambda M, N, K, comp: comp and 2 * M <= 64 and N <= 4096 and K <= 4096
